@@ -1,0 +1,278 @@
+"""CPU oracle for the MoE FFN layer forward -- TEST INFRASTRUCTURE ONLY.
+
+A plain fp64 statement of what the layer computes (``moe_oracle.c``), loaded
+through ctypes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product
+path (the HIP library and its binding) never does.  It shares no code with
+the HIP path; the only thing both sides take from a common place is the
+seeded input generator, which holds none of the method's arithmetic.
+
+Arrays are numpy arrays (torch CPU tensors are accepted and viewed as numpy):
+  float32  -> exact fp32 values
+  bfloat16 -> passed as the raw 16-bit patterns (exact)
+  int8     -> symmetric int8 codes; their fp16 scales are passed as float32
+Every function cites, in ``moe_oracle.c``, the passage of the pages it
+follows.
+
+MOE_ORACLE_LIB, when set, names another build of ``moe_oracle.c`` to load;
+the mutant test uses it to run the pins against deliberately broken copies.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+and ``tests/test_oracle_bruteforce.py``; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16, I8 = 0, 1, 2
+DROP_TOKEN_ORDER, DROP_GATE_PRIORITY = 0, 1
+
+
+def build(out: str = _LIB, src: str = _SRC, extra: tuple = ()) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, IEEE semantics kept)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-Wall", "-Wextra", *extra, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _load(path: str | None = None):
+    global _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        p = path or os.environ.get("MOE_ORACLE_LIB") or _LIB
+        if path is None and p == _LIB and (not os.path.exists(p) or
+                             os.path.getmtime(p) < os.path.getmtime(_SRC)):
+            build(p)
+        lib = ctypes.CDLL(p)
+        i64, dbl, vp, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+        lib.oracle_capacity.restype = i64
+        lib.oracle_capacity.argtypes = [i64, i64, i64, dbl, i64]
+        lib.oracle_route.restype = i32
+        lib.oracle_route.argtypes = [i64, i64, i64, i64, i32, vp, i32, vp, i32, vp,
+                                     vp, vp, vp, vp]
+        lib.oracle_aux_loss.restype = dbl
+        lib.oracle_aux_loss.argtypes = [i64, i64, i64, vp, vp, dbl, vp, vp]
+        lib.oracle_dispatch.restype = i32
+        lib.oracle_dispatch.argtypes = [i64, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp]
+        lib.oracle_ffn_rows.restype = i32
+        lib.oracle_ffn_rows.argtypes = [i64, i64, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp]
+        lib.oracle_combine.restype = i32
+        lib.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        lib.oracle_layer_forward.restype = i32
+        lib.oracle_layer_forward.argtypes = (
+            [i64] * 6 + [dbl, i64] + [i32] * 4 + [dbl, vp, i32, vp, vp, vp, vp, i32, vp, vp,
+                                                  vp, vp] + [vp] * 13)
+        lib.oracle_z_loss.restype = dbl
+        lib.oracle_z_loss.argtypes = [i64, i64, vp]
+        lib.oracle_quantize_sym_int8.restype = i32
+        lib.oracle_quantize_sym_int8.argtypes = [i64, i64, vp, vp, vp, vp]
+        if path is None:
+            _lib = lib
+        return lib
+
+
+# ---------------------------------------------------------------- helpers
+def _np(a):
+    """numpy view of an array / CPU torch tensor, with its oracle format."""
+    try:
+        import torch  # noqa: F401
+        if isinstance(a, torch.Tensor):
+            t = a.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), BF16
+            if t.dtype == torch.float16:
+                return t.float().numpy(), F32
+            a = t.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    if a.dtype == np.int8:
+        return a, I8
+    if a.dtype == np.float64:
+        raise TypeError("the oracle takes the device formats (f32, bf16, int8), "
+                        "not float64 inputs")
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _scales(s):
+    if s is None:
+        return None
+    s_np, fmt = _np(s)
+    if fmt == BF16:
+        raise TypeError("scales are fp16 or fp32")
+    return np.ascontiguousarray(s_np, dtype=np.float32)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+# ---------------------------------------------------------------- stages
+def capacity(T: int, E: int, k: int, cf: float, override: int = 0) -> int:
+    return int(_load().oracle_capacity(T, E, k, float(cf), int(override)))
+
+
+def route(x, w_router, k: int, bias=None, normalize: bool = True):
+    """logits, probs (T x E fp64), ids (T x k int32), gates (T x k fp64)."""
+    xa, xf = _np(x)
+    wa, wf = _np(w_router)
+    T, d = xa.shape
+    E = wa.shape[0]
+    assert wa.shape[1] == d
+    b = None if bias is None else np.ascontiguousarray(_np(bias)[0], dtype=np.float32)
+    logits = np.zeros((T, E)); probs = np.zeros((T, E))
+    ids = np.zeros((T, k), np.int32); gates = np.zeros((T, k))
+    rc = _load().oracle_route(T, d, E, k, int(normalize), xa.ctypes.data, xf,
+                              wa.ctypes.data, wf, _p(b), logits.ctypes.data,
+                              probs.ctypes.data, ids.ctypes.data, gates.ctypes.data)
+    if rc:
+        raise ValueError("oracle_route rejected its arguments")
+    return dict(logits=logits, probs=probs, ids=ids, gates=gates)
+
+
+def aux_loss(ids, probs, alpha: float = 1.0):
+    """(loss, f, Q) of the Switch load-balance loss."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    probs = np.ascontiguousarray(probs, np.float64)
+    T, k = ids.shape
+    E = probs.shape[1]
+    f = np.zeros(E); q = np.zeros(E)
+    loss = _load().oracle_aux_loss(T, E, k, ids.ctypes.data, probs.ctypes.data,
+                                   float(alpha), f.ctypes.data, q.ctypes.data)
+    return loss, f, q
+
+
+def dispatch(ids, E: int, C: int, gates=None, policy: int = DROP_TOKEN_ORDER):
+    """slots (T x k, -1 = dropped), drop (T x k u8), load (E), kept (E)."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = ids.shape
+    g = None if gates is None else np.ascontiguousarray(gates, np.float64)
+    slots = np.zeros((T, k), np.int32); drop = np.zeros((T, k), np.uint8)
+    load = np.zeros(E, np.int32); kept = np.zeros(E, np.int32)
+    rc = _load().oracle_dispatch(T, E, k, C, ids.ctypes.data, _p(g), policy,
+                                 slots.ctypes.data, drop.ctypes.data,
+                                 load.ctypes.data, kept.ctypes.data)
+    if rc:
+        raise ValueError("oracle_dispatch rejected its arguments")
+    return dict(slots=slots, drop=drop, load=load, kept=kept)
+
+
+def ffn_rows(rows, w1, w2, s1=None, s2=None, want_h: bool = False):
+    """Two-layer GELU FFN on rows (n x D) with W1 [F, D], W2 [D, F]."""
+    ra, rf = _np(rows)
+    if ra.ndim == 1:
+        ra = ra[None]
+    w1a, w1f = _np(w1)
+    w2a, w2f = _np(w2)
+    assert w1f == w2f
+    n, D = ra.shape
+    F = w1a.shape[0]
+    assert w1a.shape == (F, D) and w2a.shape == (D, F), (w1a.shape, w2a.shape)
+    s1a, s2a = _scales(s1), _scales(s2)
+    out = np.zeros((n, D))
+    h = np.zeros((n, F)) if want_h else None
+    rc = _load().oracle_ffn_rows(n, D, F, ra.ctypes.data, rf, w1a.ctypes.data,
+                                 w2a.ctypes.data, w1f, _p(s1a), _p(s2a),
+                                 out.ctypes.data, _p(h))
+    if rc:
+        raise ValueError("oracle_ffn_rows rejected its arguments")
+    return (out, h) if want_h else out
+
+
+def combine(slots, gates, expert_out, base=None):
+    """y = base + sum over kept assignments of gate * expert output; also M."""
+    slots = np.ascontiguousarray(slots, np.int32)
+    gates = np.ascontiguousarray(gates, np.float64)
+    T, k = slots.shape
+    eo = np.ascontiguousarray(expert_out, np.float64)
+    D = eo.shape[-1]
+    assert eo.shape == (T, k, D)
+    b = None if base is None else np.ascontiguousarray(base, np.float64)
+    y = np.zeros((T, D)); m = np.zeros((T, D))
+    _load().oracle_combine(T, D, k, slots.ctypes.data, gates.ctypes.data,
+                           eo.ctypes.data, _p(b), y.ctypes.data, m.ctypes.data)
+    return y, m
+
+
+def z_loss(logits) -> float:
+    lg = np.ascontiguousarray(logits, np.float64)
+    T, E = lg.shape
+    return float(_load().oracle_z_loss(T, E, lg.ctypes.data))
+
+
+def quantize_sym_int8(w, scale=None):
+    """(codes int8 [N, K], scales fp64 [N, K/128]) of an fp64 matrix."""
+    w = np.ascontiguousarray(w, np.float64)
+    N, K = w.shape
+    q = np.zeros((N, K), np.int8)
+    s_out = np.zeros((N, K // 128))
+    s_in = None if scale is None else np.ascontiguousarray(scale, np.float64)
+    rc = _load().oracle_quantize_sym_int8(N, K, w.ctypes.data, _p(s_in),
+                                          q.ctypes.data, s_out.ctypes.data)
+    if rc:
+        raise ValueError("K must be a multiple of 128")
+    return q, s_out
+
+
+def layer_forward(x, w_router, w1, w2, *, k: int, capacity_factor: float,
+                  capacity_override: int = 0, bias=None, s1=None, s2=None,
+                  wm1=None, wm2=None, normalize: bool = True, pr_moe: bool = False,
+                  add_skip: bool = True, policy: int = DROP_TOKEN_ORDER,
+                  alpha: float = 1.0):
+    """Whole layer; returns a dict of every intermediate the layer defines."""
+    xa, xf = _np(x)
+    wra, wrf = _np(w_router)
+    assert wrf == xf, "router weights share the activation format"
+    w1a, wf = _np(w1)
+    w2a, wf2 = _np(w2)
+    assert wf == wf2
+    T, D = xa.shape
+    E, F = w1a.shape[0], w1a.shape[1]
+    assert w1a.shape == (E, F, D) and w2a.shape == (E, D, F)
+    Fd = 0
+    wm1a = wm2a = None
+    if pr_moe:
+        wm1a, f1 = _np(wm1)
+        wm2a, f2 = _np(wm2)
+        assert f1 == xf and f2 == xf
+        Fd = wm1a.shape[0]
+        assert wm1a.shape == (Fd, D) and wm2a.shape == (D, Fd)
+    b = None if bias is None else np.ascontiguousarray(_np(bias)[0], dtype=np.float32)
+    s1a, s2a = _scales(s1), _scales(s2)
+    out = dict(
+        logits=np.zeros((T, E)), probs=np.zeros((T, E)),
+        ids=np.zeros((T, k), np.int32), gates=np.zeros((T, k)),
+        slots=np.zeros((T, k), np.int32), drop=np.zeros((T, k), np.uint8),
+        load=np.zeros(E, np.int32), kept=np.zeros(E, np.int32),
+        expert_out=np.zeros((T, k, D)), m=np.zeros((T, D)), dense=np.zeros((T, D)),
+        y=np.zeros((T, D)), aux=np.zeros(1))
+    rc = _load().oracle_layer_forward(
+        T, D, E, k, F, Fd, float(capacity_factor), int(capacity_override),
+        int(normalize), int(pr_moe), int(add_skip), int(policy), float(alpha),
+        xa.ctypes.data, xf, wra.ctypes.data, _p(b), w1a.ctypes.data,
+        w2a.ctypes.data, wf, _p(s1a), _p(s2a), _p(wm1a), _p(wm2a),
+        *(out[n].ctypes.data for n in ("logits", "probs", "ids", "gates", "slots",
+                                       "drop", "load", "kept", "expert_out", "m",
+                                       "dense", "y", "aux")))
+    if rc:
+        raise ValueError("oracle_layer_forward rejected its arguments")
+    out["aux"] = float(out["aux"][0])
+    out["capacity"] = capacity(T, E, k, capacity_factor, capacity_override)
+    return out

@@ -1,0 +1,436 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * A plain, slow, obviously-correct CPU statement of the forward pass of one
+ * Mixture-of-Experts FFN layer, in double precision, written from the pages'
+ * description of the method. Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it. It shares no code, header,
+ * table or helper with the HIP library and includes nothing from it.
+ *
+ * Sources (cited by page title and section):
+ *  [DSC]  "DeepSpeed MoE and Model Compression" (shaojiemike.top),
+ *         section "DeepSpeed-MoE" (the equation p(x)=softmax(W_r x),
+ *         y = sum over TopK(p,k) of p_e(x) E_e(x), and the pipeline block:
+ *         router -> topk -> pack_by_expert(capacity) -> experts -> combine
+ *         with gates, plus a load-balance loss).
+ *  [DvS]  "DeepSpeed-MoE vs Switch Transformer" (hncyxsy.com), sections
+ *         "router computation" (logits = x W_r, p = softmax(logits)),
+ *         "Top-1 routing decision", "expert capacity overflow" (capacity =
+ *         tokens / experts x capacity_factor; an overflowing token skips the
+ *         expert FFN and reaches the next layer through the residual),
+ *         "PR-MoE residual example".
+ *  [SRV]  "MoE survey, pruning and quantization notes" (ken1301225.github.io),
+ *         sec. 1.1.1.1 (TopK after softmax needs renormalisation),
+ *         sec. 1.1.2.1 (an expert is a two-layer FFN; MoE(x)=sum w_i M_i(x)),
+ *         sec. 1.1.4.1 (Switch load-balance loss alpha*N*sum f_i Q_i),
+ *         sec. 1.2.1 (bf16 is the top half of an fp32),
+ *         sec. 1.2.2 (symmetric quantization: r_hat = s*q).
+ *  [DSN]  "DeepSpeed-MoE: Advancing Mixture-of-Experts Inference and Training
+ *         to Power Next-Generation AI Scale" (unpurerationalist.github.io
+ *         notes), sec. 3.1 (Residual-MoE: fixed dense MLP plus one top-1
+ *         expert as a residual correction), sec. 4.4 (cumsum mapping table).
+ *
+ * Readings where the pages are silent are listed in the design doc; the ones
+ * that shape this file are restated next to the code they affect.
+ *
+ * Element formats accepted for x and weights (exactly converted to double):
+ *   OR_F32  : IEEE binary32
+ *   OR_BF16 : bfloat16 bit patterns (uint16), the upper half of a binary32
+ *   OR_I8   : signed 8-bit codes, with one float32 scale per 128 consecutive
+ *             input-dimension elements of each output row (symmetric int8)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_DROP_TOKEN_ORDER = 0, OR_DROP_GATE_PRIORITY = 1 };
+
+#define OR_GROUP 128
+
+/* value of element i of an array in one of the formats above */
+static double elem(const void *p, int fmt, int64_t i) {
+  if (fmt == OR_F32) return (double)((const float *)p)[i];
+  if (fmt == OR_BF16) {
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16; /* [SRV] 1.2.1 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return (double)((const int8_t *)p)[i];
+}
+
+/* weight element (n, i) of an [N, K] row-major matrix; int8 codes are
+ * dequantised as scale * code with the scale of group i / 128 of row n
+ * ([SRV] 1.2.2, symmetric form). */
+static double weight(const void *w, int fmt, const float *scale, int64_t N,
+                     int64_t K, int64_t n, int64_t i) {
+  (void)N;
+  double v = elem(w, fmt, n * K + i);
+  if (fmt == OR_I8) v *= (double)scale[n * (K / OR_GROUP) + i / OR_GROUP];
+  return v;
+}
+
+/* exact (erf) GELU; the configurations name GELU as the FFN activation */
+static double gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
+
+/* ------------------------------------------------------------------------
+ * Capacity.  [DvS] "expert capacity overflow": capacity = tokens per batch /
+ * number of experts x capacity_factor.  Reading: with top-k routing there
+ * are k*T assignments, so C = ceil(k*T*cf/E); a positive override replaces
+ * it; C is clamped to T (no expert can receive more than T assignments
+ * because a token's k experts are distinct, so the clamp changes nothing).
+ * ---------------------------------------------------------------------- */
+int64_t oracle_capacity(int64_t T, int64_t E, int64_t k, double cf,
+                        int64_t override_c) {
+  int64_t c;
+  if (override_c > 0)
+    c = override_c;
+  else
+    c = (int64_t)ceil((double)k * (double)T * cf / (double)E);
+  if (c > T) c = T;
+  if (c < 0) c = 0;
+  return c;
+}
+
+/* ------------------------------------------------------------------------
+ * Router.  [DSC] eq. p(x) = softmax(W_r x); [DvS] "router computation".
+ * logits[t,e] = sum_i x[t,i] W_r[e,i] (+ b[e]); p = softmax over e.
+ * Top-k: the k largest probabilities, in descending order, ties to the lower
+ * expert index.  Softmax is strictly increasing in the logit, so ranking by
+ * logits ranks by probability.
+ * Gates: k = 1 -> the chosen expert's full-softmax probability ([DSC] eq.);
+ * k >= 2 with normalize -> p_j / sum of the k chosen p ([SRV] 1.1.1.1),
+ * without normalize -> p_j.
+ * ---------------------------------------------------------------------- */
+int oracle_route(int64_t T, int64_t d, int64_t E, int64_t k, int normalize,
+                 const void *x, int x_fmt, const void *wr, int wr_fmt,
+                 const float *bias, double *logits, double *probs,
+                 int32_t *ids, double *gates) {
+  if (k < 1 || k > E) return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t t = 0; t < T; t++) {
+    double *l = logits + t * E, *p = probs + t * E;
+    for (int64_t e = 0; e < E; e++) {
+      double s = 0.0;
+      for (int64_t i = 0; i < d; i++)
+        s += elem(x, x_fmt, t * d + i) * elem(wr, wr_fmt, e * d + i);
+      if (bias) s += (double)bias[e];
+      l[e] = s;
+    }
+    double m = l[0];
+    for (int64_t e = 1; e < E; e++)
+      if (l[e] > m) m = l[e];
+    double z = 0.0;
+    for (int64_t e = 0; e < E; e++) {
+      p[e] = exp(l[e] - m);
+      z += p[e];
+    }
+    for (int64_t e = 0; e < E; e++) p[e] /= z;
+
+    /* selection: repeatedly take the best not-yet-chosen expert under the
+     * order (larger logit first, then smaller index) */
+    int32_t *sel = ids + t * k;
+    for (int64_t j = 0; j < k; j++) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < E; e++) {
+        int taken = 0;
+        for (int64_t q = 0; q < j; q++)
+          if (sel[q] == e) taken = 1;
+        if (taken) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict: keeps lower index on ties */
+      }
+      sel[j] = (int32_t)best;
+    }
+    double *g = gates + t * k;
+    double den = 0.0;
+    for (int64_t j = 0; j < k; j++) den += p[sel[j]];
+    for (int64_t j = 0; j < k; j++)
+      g[j] = (k >= 2 && normalize) ? p[sel[j]] / den : p[sel[j]];
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Switch load-balance loss.  [SRV] 1.1.4.1:
+ *   f_i = (1/T) #{tokens whose argmax expert is i}
+ *   Q_i = (1/T) sum over tokens of the router probability of i
+ *   loss = alpha * N * sum_i f_i Q_i,   N = number of experts.
+ * Readings: the argmax is the first-ranked choice ids[t,0] (also for k=2);
+ * f counts routing decisions before any capacity drop; Q uses the full
+ * softmax (bias included).  T = 0 gives loss 0 (both sums are empty).
+ * f and Q are written out when the pointers are non-NULL.
+ * ---------------------------------------------------------------------- */
+double oracle_aux_loss(int64_t T, int64_t E, int64_t k, const int32_t *ids,
+                       const double *probs, double alpha, double *f_out,
+                       double *q_out) {
+  double *f = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+  double *q = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+  for (int64_t t = 0; t < T; t++) {
+    f[ids[t * k]] += 1.0;
+    for (int64_t e = 0; e < E; e++) q[e] += probs[t * E + e];
+  }
+  double loss = 0.0;
+  if (T > 0) {
+    for (int64_t e = 0; e < E; e++) {
+      f[e] /= (double)T;
+      q[e] /= (double)T;
+      loss += f[e] * q[e];
+    }
+    loss *= alpha * (double)E;
+  }
+  if (f_out) memcpy(f_out, f, (size_t)E * sizeof(double));
+  if (q_out) memcpy(q_out, q, (size_t)E * sizeof(double));
+  free(f);
+  free(q);
+  return loss;
+}
+
+/* ------------------------------------------------------------------------
+ * Dispatch into the expert-major capacity buffer.  [DSC] pack_by_expert with
+ * a capacity; [DvS] overflow tokens skip the expert; [DSN] 4.4 builds the
+ * token-to-expert mapping from a cumulative sum over tokens.
+ *
+ * OR_DROP_TOKEN_ORDER (the contract): an expert takes its assignments in
+ * token order; the n-th one (counting from 0) gets slot n and is kept iff
+ * n < C.  A token's k experts are distinct, so token order is a total order
+ * within one expert.
+ * OR_DROP_GATE_PRIORITY ([DvS] capacity example): an expert keeps its C
+ * assignments with the largest gate (ties to the earlier token); the slot is
+ * the rank in that order.
+ * Outputs: slots[t,j] (-1 when dropped), drop[t,j] (1 when dropped),
+ * load[e] = assignments received, kept[e] = min(load[e], C).
+ * ---------------------------------------------------------------------- */
+int oracle_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
+                    const int32_t *ids, const double *gates, int policy,
+                    int32_t *slots, uint8_t *drop, int32_t *load,
+                    int32_t *kept) {
+  if (policy == OR_DROP_GATE_PRIORITY && !gates) return -1;
+  for (int64_t e = 0; e < E; e++) {
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; t++)
+      for (int64_t j = 0; j < k; j++) {
+        if (ids[t * k + j] != e) continue;
+        int64_t rank;
+        if (policy == OR_DROP_TOKEN_ORDER) {
+          rank = n;
+        } else {
+          /* number of this expert's assignments that come before (t,j) */
+          rank = 0;
+          double g = gates[t * k + j];
+          for (int64_t u = 0; u < T; u++)
+            for (int64_t i = 0; i < k; i++) {
+              if (ids[u * k + i] != e) continue;
+              double h = gates[u * k + i];
+              if (h > g || (h == g && u < t)) rank++;
+            }
+        }
+        n++;
+        if (rank < C) {
+          slots[t * k + j] = (int32_t)rank;
+          drop[t * k + j] = 0;
+        } else {
+          slots[t * k + j] = -1;
+          drop[t * k + j] = 1;
+        }
+      }
+    load[e] = (int32_t)n;
+    kept[e] = (int32_t)(n < C ? n : C);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Two-layer GELU FFN on a list of rows with one weight pair.
+ * [SRV] 1.1.2.1: an expert is a two-layer feed-forward network; the
+ * configurations name GELU and no biases.  Weights are [out, in] row-major:
+ * W1 [F, D], W2 [D, F].   h = GELU(W1 x) (F values);  out = W2 h (D values).
+ * The same function states PR-MoE's fixed dense MLP ([DSN] 3.1).
+ * rows: n x D in x_fmt; out: n x D doubles; h_out (optional): n x F.
+ * ---------------------------------------------------------------------- */
+/* one row: h = GELU(W1 x), out = W2 h; h is caller scratch of F doubles */
+static void ffn_one_row(int64_t D, int64_t F, const void *xr, int x_fmt,
+                        int64_t row, const void *w1, const void *w2, int w_fmt,
+                        const float *s1, const float *s2, double *h,
+                        double *out) {
+  for (int64_t f = 0; f < F; f++) {
+    double s = 0.0;
+    for (int64_t i = 0; i < D; i++)
+      s += weight(w1, w_fmt, s1, F, D, f, i) * elem(xr, x_fmt, row * D + i);
+    h[f] = gelu(s);
+  }
+  for (int64_t o = 0; o < D; o++) {
+    double s = 0.0;
+    for (int64_t f = 0; f < F; f++) s += weight(w2, w_fmt, s2, D, F, o, f) * h[f];
+    out[o] = s;
+  }
+}
+
+int oracle_ffn_rows(int64_t n, int64_t D, int64_t F, const void *xr, int x_fmt,
+                    const void *w1, const void *w2, int w_fmt,
+                    const float *s1, const float *s2, double *out,
+                    double *h_out) {
+  if (w_fmt == OR_I8 && (!s1 || !s2 || D % OR_GROUP || F % OR_GROUP)) return -1;
+#pragma omp parallel
+  {
+    double *h = (double *)malloc((size_t)(F > 0 ? F : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+      ffn_one_row(D, F, xr, x_fmt, r, w1, w2, w_fmt, s1, s2, h, out + r * D);
+      if (h_out) memcpy(h_out + r * F, h, (size_t)F * sizeof(double));
+    }
+    free(h);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Gate-weighted combine.  [DSC] combine(returned, gates) and the equation's
+ * sum of p_e E_e(x); [DvS] a dropped assignment contributes nothing and the
+ * token reaches the next layer through the residual; [DvS] PR-MoE example
+ * (fixed-MLP output plus gate times the expert's residual output).
+ *   M[t] = sum over kept j (in rank order) of gates[t,j] * expert_out[t,j]
+ *   y[t] = base[t] + M[t]          (base NULL -> 0)
+ * expert_out: T x k x D doubles (the expert's output for that assignment;
+ * ignored for dropped ones).  m_out (optional) receives M.
+ * ---------------------------------------------------------------------- */
+int oracle_combine(int64_t T, int64_t D, int64_t k, const int32_t *slots,
+                   const double *gates, const double *expert_out,
+                   const double *base, double *y, double *m_out) {
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t o = 0; o < D; o++) {
+      double m = 0.0;
+      for (int64_t j = 0; j < k; j++)
+        if (slots[t * k + j] >= 0)
+          m += gates[t * k + j] * expert_out[(t * k + j) * D + o];
+      if (m_out) m_out[t * D + o] = m;
+      y[t * D + o] = (base ? base[t * D + o] : 0.0) + m;
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Whole layer, composed from the stages above in the order of [DSC]'s
+ * pipeline (router, top-k, capacity dispatch, experts, combine, aux loss).
+ *   y = (add_skip ? x : 0) + (pr_moe ? D(x) : 0) + M(x)
+ * add_skip: the residual that carries a dropped token on ([DvS] overflow);
+ * pr_moe: the fixed dense MLP of Residual-MoE ([DSN] 3.1).
+ * Expert weights: w1 [E, F, D], w2 [E, D, F] (int8: scales [E, F, D/128]
+ * and [E, D, F/128]); dense MLP wm1 [Fd, D], wm2 [D, Fd] in x_fmt.
+ * Outputs (doubles unless noted): logits/probs T x E, ids/slots T x k
+ * (int32), gates T x k, drop T x k (uint8), load/kept E (int32),
+ * expert_out T x k x D (per assignment; zero when dropped),
+ * m T x D, dense T x D (zero when !pr_moe), y T x D, aux [1].
+ * ---------------------------------------------------------------------- */
+int oracle_layer_forward(int64_t T, int64_t D, int64_t E, int64_t k,
+                         int64_t F, int64_t Fd, double cf, int64_t cap_override,
+                         int normalize, int pr_moe, int add_skip, int policy,
+                         double alpha, const void *x, int x_fmt,
+                         const void *wr, const float *bias, const void *w1,
+                         const void *w2, int w_fmt, const float *s1,
+                         const float *s2, const void *wm1, const void *wm2,
+                         double *logits, double *probs, int32_t *ids,
+                         double *gates, int32_t *slots, uint8_t *drop,
+                         int32_t *load, int32_t *kept, double *expert_out,
+                         double *m, double *dense, double *y, double *aux) {
+  int rc = oracle_route(T, D, E, k, normalize, x, x_fmt, wr, x_fmt, bias,
+                        logits, probs, ids, gates);
+  if (rc) return rc;
+  *aux = oracle_aux_loss(T, E, k, ids, probs, alpha, NULL, NULL);
+  int64_t C = oracle_capacity(T, E, k, cf, cap_override);
+  rc = oracle_dispatch(T, E, k, C, ids, gates, policy, slots, drop, load, kept);
+  if (rc) return rc;
+
+  size_t ws = (w_fmt == OR_F32) ? 4 : (w_fmt == OR_BF16 ? 2 : 1);
+  if (w_fmt == OR_I8 && (!s1 || !s2 || D % OR_GROUP || F % OR_GROUP)) return -1;
+  memset(expert_out, 0, (size_t)(T * k * D) * sizeof(double));
+#pragma omp parallel
+  {
+    double *h = (double *)malloc((size_t)(F > 0 ? F : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < T * k; a++) {
+      if (slots[a] < 0) continue;
+      int64_t e = ids[a];
+      ffn_one_row(D, F, x, x_fmt, a / k,
+                  (const char *)w1 + (size_t)(e * F * D) * ws,
+                  (const char *)w2 + (size_t)(e * D * F) * ws, w_fmt,
+                  s1 ? s1 + e * F * (D / OR_GROUP) : NULL,
+                  s2 ? s2 + e * D * (F / OR_GROUP) : NULL, h,
+                  expert_out + a * D);
+    }
+    free(h);
+  }
+
+  if (pr_moe) {
+    rc = oracle_ffn_rows(T, D, Fd, x, x_fmt, wm1, wm2, x_fmt, NULL, NULL,
+                         dense, NULL);
+    if (rc) return rc;
+  } else {
+    memset(dense, 0, (size_t)(T * D) * sizeof(double));
+  }
+  double *base = (double *)malloc((size_t)(T * D > 0 ? T * D : 1) * sizeof(double));
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t o = 0; o < D; o++)
+      base[t * D + o] = (add_skip ? elem(x, x_fmt, t * D + o) : 0.0) + dense[t * D + o];
+  rc = oracle_combine(T, D, k, slots, gates, expert_out, base, y, m);
+  free(base);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Router z-loss, [DvS] section "Router Z-loss":
+ *   L_z = (1/B) sum over tokens of (log sum_j exp(logit_j))^2
+ * computed with the max shifted out of the exponentials.
+ * ---------------------------------------------------------------------- */
+double oracle_z_loss(int64_t T, int64_t E, const double *logits) {
+  if (T <= 0) return 0.0;
+  double acc = 0.0;
+  for (int64_t t = 0; t < T; t++) {
+    const double *l = logits + t * E;
+    double m = l[0];
+    for (int64_t e = 1; e < E; e++)
+      if (l[e] > m) m = l[e];
+    double s = 0.0;
+    for (int64_t e = 0; e < E; e++) s += exp(l[e] - m);
+    double lz = m + log(s);
+    acc += lz * lz;
+  }
+  return acc / (double)T;
+}
+
+/* ------------------------------------------------------------------------
+ * Symmetric int8 quantisation of one [N, K] matrix in groups of 128 along K,
+ * [SRV] 1.2.2: s = max|r| / q_max with q_max = 127; q = clamp(round(r / s),
+ * -127, 127) with round-half-to-even; a group whose values are all zero gets
+ * s = 0 and q = 0.  Scales come out as doubles; a caller that stores them in
+ * a narrower format rounds them first and passes that value in scale_in to
+ * quantise against it (scale_in NULL: use the exact scale).
+ * ---------------------------------------------------------------------- */
+int oracle_quantize_sym_int8(int64_t N, int64_t K, const double *w,
+                             const double *scale_in, int8_t *q,
+                             double *scale_out) {
+  if (K % OR_GROUP) return -1;
+  int64_t G = K / OR_GROUP;
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t g = 0; g < G; g++) {
+      const double *r = w + n * K + g * OR_GROUP;
+      double s;
+      if (scale_in) {
+        s = scale_in[n * G + g];
+      } else {
+        double amax = 0.0;
+        for (int64_t i = 0; i < OR_GROUP; i++)
+          if (fabs(r[i]) > amax) amax = fabs(r[i]);
+        s = amax / 127.0;
+      }
+      if (scale_out) scale_out[n * G + g] = s;
+      for (int64_t i = 0; i < OR_GROUP; i++) {
+        double v = (s > 0.0) ? nearbyint(r[i] / s) : 0.0; /* default mode: half to even */
+        if (v > 127.0) v = 127.0;
+        if (v < -127.0) v = -127.0;
+        q[n * K + g * OR_GROUP + i] = (int8_t)v;
+      }
+    }
+  return 0;
+}
