@@ -1,0 +1,198 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one
+ * Mixture-of-Experts FFN layer.
+ *
+ * The layer ("DeepSpeed MoE and Model Compression", section "DeepSpeed-MoE",
+ * its equation and its pipeline block):
+ *   p(x)  = softmax(W_r x (+ b_r))                      router
+ *   ids   = the k largest p, descending, ties -> lower expert index
+ *   gates = p of the chosen experts (k >= 2: renormalised over the k)
+ *   dispatch into an expert-major capacity buffer [E, C, d], in token order,
+ *   C = min(T, ceil(k*T*cf/E)); assignments past C are dropped
+ *   ("DeepSpeed-MoE vs Switch Transformer", section "expert capacity overflow")
+ *   expert FFN  y_e = W2_e GELU(W1_e x)   (survey notes sec. 1.1.2.1)
+ *   y = [x] + [dense MLP(x)] + sum over kept j of gates_j y_{e_j}
+ *   (PR-MoE, "DeepSpeed-MoE ... notes" sec. 3.1)
+ *   aux = alpha * E * sum_i f_i Q_i   (survey notes sec. 1.1.4.1)
+ *
+ * Conventions for every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, row-major,
+ *     16-byte aligned.  Weights are [out, in]: W_r [E, d], W1 [E, d_ff, d],
+ *     W2 [E, d, d_ff], Wm1 [d_ff_dense, d], Wm2 [d, d_ff_dense].
+ *   - "act" = the configuration's activation type (MOE_F32 or MOE_BF16); it is
+ *     the type of x, W_r, plain expert weights, the dense MLP weights, x_disp,
+ *     y_disp and y.  ids/slots/load/kept are int32, gates/logits/aux float32,
+ *     drop masks uint8, int8 scales IEEE fp16.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work: no host synchronisation, no allocation, no host<->device
+ *     copies.  Results are valid once the stream has been synchronised.
+ *   - Scratch memory comes from the caller's workspace `ws` of at least
+ *     moe_workspace_bytes(cfg, entry) bytes (256-byte aligned).
+ *   - Arguments are validated before anything is enqueued; on error nothing
+ *     is launched and no output is written.  Return 0 (MOE_OK) or a negative
+ *     MOE_ERR_* code; moe_status_string() names it.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - The library keeps no state between calls; calls on different streams
+ *     with disjoint buffers may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null required pointer, bad size, misaligned */
+#define MOE_ERR_UNSUPPORTED (-2) /* a valid configuration this build does not run */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define MOE_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+/* activation types */
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/* expert weight formats */
+#define MOE_W_PLAIN 0     /* act type */
+#define MOE_W_INT8_G128 1 /* symmetric int8 codes q, fp16 scale s per 128
+                             consecutive input-dim elements of an output row;
+                             weight = s * q (survey notes sec. 1.2.2) */
+
+/* capacity overflow policy */
+#define MOE_DROP_TOKEN_ORDER 0 /* first come, first served in token order */
+
+/* workspace query selectors */
+#define MOE_ENTRY_ROUTE 0
+#define MOE_ENTRY_DISPATCH 1
+#define MOE_ENTRY_EXPERT_FFN 2
+#define MOE_ENTRY_COMBINE 3
+#define MOE_ENTRY_LAYER 4
+
+typedef struct moe_config {
+  int64_t T;          /* tokens (>= 0) */
+  int64_t d;          /* model dim (>= 1) */
+  int64_t E;          /* experts, 1..256 */
+  int64_t k;          /* experts per token, 1..min(E, 8) */
+  int64_t d_ff;       /* expert hidden dim (>= 1) */
+  int64_t d_ff_dense; /* PR-MoE dense MLP hidden dim (used when pr_moe) */
+  double capacity_factor; /* > 0; C = min(T, ceil(k*T*cf/E)) */
+  int64_t capacity;       /* > 0 overrides the formula (still clamped to T) */
+  int32_t act_dtype;      /* MOE_F32 | MOE_BF16 */
+  int32_t expert_wfmt;    /* MOE_W_PLAIN | MOE_W_INT8_G128 (bf16 acts only) */
+  int32_t normalize_topk; /* k >= 2: 1 = gates renormalised over the k */
+  int32_t pr_moe;         /* 1 = add the fixed dense MLP D(x) */
+  int32_t add_skip;       /* 1 = add x (the residual a dropped token rides) */
+  int32_t drop_policy;    /* MOE_DROP_TOKEN_ORDER */
+  float aux_alpha;        /* alpha of the load-balance loss */
+} moe_config;
+
+typedef struct moe_weights {
+  const void *w_router;  /* [E, d] act */
+  const float *b_router; /* [E] or NULL (a logit bias, included in p) */
+  const void *w1;        /* [E, d_ff, d] act or int8 */
+  const void *w1_scale;  /* [E, d_ff, d/128] fp16 (int8 only, else NULL) */
+  const void *w2;        /* [E, d, d_ff] act or int8 */
+  const void *w2_scale;  /* [E, d, d_ff/128] fp16 (int8 only, else NULL) */
+  const void *wm1;       /* [d_ff_dense, d] act (pr_moe only) */
+  const void *wm2;       /* [d, d_ff_dense] act (pr_moe only) */
+} moe_weights;
+
+typedef struct moe_outputs {
+  void *y;             /* [T, d] act                           required */
+  int32_t *expert_ids; /* [T, k]                                required */
+  float *gates;        /* [T, k]                                required */
+  int32_t *slots;      /* [T, k] slot in the expert, -1 dropped required */
+  int32_t *load;       /* [E] assignments received              required */
+  int32_t *kept;       /* [E] min(load, C)                      required */
+  float *aux_loss;     /* [1]                                   required */
+  uint8_t *drop_mask;  /* [T, k] 1 = dropped                    optional */
+  float *logits;       /* [T, E] router logits (+ bias)         optional */
+  void *x_disp;        /* [E, C, d] act; NULL = in the workspace */
+  void *y_disp;        /* [E, C, d] act; NULL = in the workspace */
+  void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
+} moe_outputs;
+
+/* Capacity C of the configuration, or a negative MOE_ERR_* code. */
+int64_t moe_capacity(const moe_config *cfg);
+
+/* Workspace bytes an entry point needs (MOE_ENTRY_*); 0 for an invalid
+ * configuration. */
+size_t moe_workspace_bytes(const moe_config *cfg, int entry);
+
+/* Router, softmax, top-k gate and load-balance loss ("DeepSpeed-MoE vs Switch
+ * Transformer", section "router computation"; survey notes sec. 1.1.1.1 and
+ * 1.1.4.1).  x [T, d], w_router [E, d] act; b_router [E] or NULL.
+ * Out: expert_ids [T, k], gates [T, k], logits [T, E] (NULL = not written),
+ * aux_loss [1].  Logits accumulate in fp32. */
+int moe_route(const moe_config *cfg, const void *x, const void *w_router,
+              const float *b_router, int32_t *expert_ids, float *gates,
+              float *logits, float *aux_loss, void *ws, size_t ws_bytes,
+              void *stream);
+
+/* Capacity-limited dispatch in token order and the layout transform into
+ * the expert-major buffer ("DeepSpeed MoE and Model Compression",
+ * pack_by_expert; "DeepSpeed-MoE ... notes" sec. 4.4 cumsum mapping table
+ * and layout transformation).  x [T, d], expert_ids [T, k].
+ * Out: slots [T, k] (-1 = dropped), drop_mask [T, k] (NULL ok), load [E],
+ * kept [E], x_disp [E, C, d]: row (e, s) = x[t] for the assignment with slot
+ * s in expert e; rows s >= kept[e] are not written. */
+int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids,
+                 int32_t *slots, uint8_t *drop_mask, int32_t *load,
+                 int32_t *kept, void *x_disp, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Every expert's two-layer GELU FFN over its kept rows (survey notes sec.
+ * 1.1.2.1; weight-only int8 dequantisation, survey notes sec. 1.2.3.1).
+ * x_disp [E, C, d], kept [E] (device), w1/w2 (+ fp16 scales for int8).
+ * Out: y_disp [E, C, d]; rows s >= kept[e] are not written. */
+int moe_expert_ffn(const moe_config *cfg, const void *x_disp,
+                   const int32_t *kept, const void *w1, const void *w1_scale,
+                   const void *w2, const void *w2_scale, void *y_disp, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* PR-MoE's fixed dense MLP over all tokens ("DeepSpeed-MoE ... notes" sec.
+ * 3.1): dense_out[t] = Wm2 GELU(Wm1 x[t]).  x [T, d]; out [T, d] act.
+ * Workspace: moe_workspace_bytes(cfg, MOE_ENTRY_LAYER) covers it. */
+int moe_dense_mlp(const moe_config *cfg, const void *x, const void *wm1,
+                  const void *wm2, void *dense_out, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/* Gate-weighted combine with residual ("DeepSpeed MoE and Model Compression",
+ * combine(returned, gates); "DeepSpeed-MoE vs Switch Transformer", PR-MoE
+ * residual example and overflow-through-residual):
+ *   y[t] = base[t] + sum over j with slots[t,j] >= 0 of
+ *          gates[t,j] * y_disp[expert_ids[t,j], slots[t,j]]
+ * accumulated in fp32 in rank order j.  base [T, d] act or NULL (= 0);
+ * base2 [T, d] act or NULL, added to base (x and D(x) for PR-MoE). */
+int moe_combine(const moe_config *cfg, const void *y_disp,
+                const int32_t *expert_ids, const int32_t *slots,
+                const float *gates, const void *base, const void *base2,
+                void *y, void *stream);
+
+/* The whole layer: route, dispatch, [dense MLP], expert FFN, combine. */
+int moe_layer_forward(const moe_config *cfg, const void *x,
+                      const moe_weights *w, moe_outputs *out, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+/* Per-kernel timing (diagnostics).  When enabled, every kernel launch is
+ * bracketed by a pair of HIP events recorded on its stream; moe_profile_read
+ * synchronises those events and returns, per kernel name, the number of
+ * launches and the summed duration in milliseconds since the last reset.
+ * Not thread-safe; meant for one benchmarking thread. */
+int moe_profile_enable(int on);
+int moe_profile_reset(void);
+/* Fills up to `cap` entries; returns the number of kernel names recorded. */
+int moe_profile_read(char *names /* cap x 64 chars */, int64_t *launches,
+                     double *total_ms, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,439 @@
+// api.hip -- the C ABI declared in include/moe.h: argument validation (all of
+// it before anything is enqueued), capacity, workspace layout, the launch
+// sequence of each entry point, and the optional per-kernel event timing.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t act_size(const moe_config *c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
+
+int check_config(const moe_config *c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d < 1 || c->E < 1 || c->k < 1 || c->k > c->E || c->d_ff < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->expert_wfmt != MOE_W_PLAIN && c->expert_wfmt != MOE_W_INT8_G128)
+    return MOE_ERR_INVALID_ARG;
+  if ((c->normalize_topk | c->pr_moe | c->add_skip) & ~1) return MOE_ERR_INVALID_ARG;
+  if (c->capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (c->capacity == 0 && !(c->capacity_factor > 0.0 && isfinite(c->capacity_factor)))
+    return MOE_ERR_INVALID_ARG;
+  if (c->pr_moe && c->d_ff_dense < 1) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (c->drop_policy != MOE_DROP_TOKEN_ORDER) return MOE_ERR_UNSUPPORTED;
+  if (c->E > 256 || c->k > 8 || c->T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (c->d > (1 << 20) || c->d_ff > (1 << 20) || c->d_ff_dense > (1 << 20))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_BF16) {
+    if (c->d % 64 || c->d_ff % 64 || (c->pr_moe && c->d_ff_dense % 64))
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (c->expert_wfmt == MOE_W_INT8_G128) {
+    if (c->act_dtype != MOE_BF16 || c->d % 128 || c->d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_config *c) {
+  int64_t C;
+  if (c->capacity > 0)
+    C = c->capacity;
+  else
+    C = (int64_t)ceil((double)c->k * (double)c->T * c->capacity_factor / (double)c->E);
+  if (C > c->T) C = c->T;
+  if (C < 0) C = 0;
+  return C;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// a pointer that must be given when `n` elements are to be read or written
+bool need(const void *p, int64_t n, size_t align) {
+  if (n <= 0) return true;
+  return p != nullptr && aligned(p, align);
+}
+bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align); }
+
+// ---- workspace layout
+struct Layout {
+  size_t qsum, fcount, hist, offs, x_disp, y_disp, hidden, dense, total;
+};
+
+Layout layout(const moe_config *c, int entry) {
+  Layout L{};
+  const int64_t nblk = moe_host::router_blocks(c->T);
+  const size_t blkE = align256((size_t)nblk * (size_t)c->E * 4);
+  const int64_t C = capacity_of(c);
+  const size_t as = act_size(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  switch (entry) {
+    case MOE_ENTRY_ROUTE:
+      L.qsum = take(blkE);
+      L.fcount = take(blkE);
+      break;
+    case MOE_ENTRY_DISPATCH:
+      L.hist = take(blkE);
+      L.offs = take(blkE);
+      break;
+    case MOE_ENTRY_EXPERT_FFN:
+      L.hidden = take((size_t)c->E * C * c->d_ff * as);
+      break;
+    case MOE_ENTRY_COMBINE:
+      break;
+    case MOE_ENTRY_LAYER: {
+      L.qsum = take(blkE);
+      L.fcount = take(blkE);
+      L.hist = take(blkE);
+      L.offs = take(blkE);
+      L.x_disp = take((size_t)c->E * C * c->d * as);
+      L.y_disp = take((size_t)c->E * C * c->d * as);
+      size_t hid = (size_t)c->E * C * c->d_ff * as;
+      if (c->pr_moe) {
+        const size_t hd = (size_t)c->T * c->d_ff_dense * as;
+        if (hd > hid) hid = hd;
+        L.dense = take((size_t)c->T * c->d * as);
+      }
+      L.hidden = take(hid);
+      break;
+    }
+    default:
+      break;
+  }
+  L.total = o;
+  return L;
+}
+
+int check_ws(const moe_config *c, int entry, void *ws, size_t ws_bytes) {
+  const size_t need_b = layout(c, entry).total;
+  if (need_b == 0) return MOE_OK;
+  if (!ws || ws_bytes < need_b || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+char *at(void *ws, size_t off) { return (char *)ws + off; }
+
+// ---- launch sequences (arguments already validated)
+hipError_t do_route(const moe_config *c, const void *x, const void *wr, const float *br,
+                    int32_t *ids, float *gates, float *logits, float *aux, float *qsum,
+                    int32_t *fcount, int32_t *hist, hipStream_t s) {
+  RouterArgs a{};
+  a.x = x;
+  a.w = wr;
+  a.bias = br;
+  a.ids = ids;
+  a.gates = gates;
+  a.logits = logits;
+  a.qsum = qsum;
+  a.fcount = fcount;
+  a.hist = hist;
+  a.T = c->T;
+  a.d = (int)c->d;
+  a.E = (int)c->E;
+  a.k = (int)c->k;
+  a.normalize = c->normalize_topk;
+  hipError_t e = moe_host::launch_router(a, c->act_dtype == MOE_BF16, s);
+  if (e != hipSuccess) return e;
+  return moe_host::launch_aux_final(qsum, fcount, moe_host::router_blocks(c->T), (int)c->E, c->T,
+                                    c->aux_alpha, aux, s);
+}
+
+hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *ids,
+                           const int32_t *hist, int32_t *offs, int32_t *slots, uint8_t *drop,
+                           int32_t *load, int32_t *kept, void *x_disp, hipStream_t s) {
+  const int64_t C = capacity_of(c);
+  const int nblk = moe_host::router_blocks(c->T);
+  hipError_t e = moe_host::launch_dispatch_scan(hist, nblk, (int)c->E, C, offs, load, kept, s);
+  if (e != hipSuccess) return e;
+  e = moe_host::launch_dispatch_place(ids, offs, c->T, (int)c->E, (int)c->k, C, slots, drop, s);
+  if (e != hipSuccess) return e;
+  return moe_host::launch_gather(x, ids, slots, c->T, (int)c->k, C,
+                                 c->d * (int64_t)act_size(c), x_disp, s);
+}
+
+hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t *kept,
+                         const void *w1, const void *s1, const void *w2, const void *s2,
+                         void *y_disp, void *hidden, hipStream_t s) {
+  const int64_t C = capacity_of(c);
+  if (C == 0) return hipSuccess;
+  const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
+  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E};
+  hipError_t e = moe_host::launch_gemm(g1, bf, q8, 1, s);
+  if (e != hipSuccess) return e;
+  GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E};
+  return moe_host::launch_gemm(g2, bf, q8, 0, s);
+}
+
+hipError_t do_dense(const moe_config *c, const void *x, const void *wm1, const void *wm2,
+                    void *out, void *hidden, hipStream_t s) {
+  if (c->T == 0) return hipSuccess;
+  const int bf = c->act_dtype == MOE_BF16;
+  GemmArgs g1{x, wm1, nullptr, hidden, nullptr, c->T, (int)c->d_ff_dense, (int)c->d, 1};
+  hipError_t e = moe_host::launch_gemm(g1, bf, 0, 1, s);
+  if (e != hipSuccess) return e;
+  GemmArgs g2{hidden, wm2, nullptr, out, nullptr, c->T, (int)c->d, (int)c->d_ff_dense, 1};
+  return moe_host::launch_gemm(g2, bf, 0, 0, s);
+}
+
+// ---- profiling records
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace moe_host {
+void prof_begin(hipStream_t s, const char *name) {
+  if (!g_prof) return;
+  ProfRec r{name, pool_event(), pool_event()};
+  if (r.a) (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+}
+void prof_end(hipStream_t s) {
+  if (!g_prof || g_recs.empty()) return;
+  if (g_recs.back().b) (void)hipEventRecord(g_recs.back().b, s);
+}
+}  // namespace moe_host
+
+extern "C" {
+
+int64_t moe_capacity(const moe_config *cfg) {
+  const int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  return capacity_of(cfg);
+}
+
+size_t moe_workspace_bytes(const moe_config *cfg, int entry) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  if (entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_LAYER) return 0;
+  return layout(cfg, entry).total;
+}
+
+int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *b_router,
+              int32_t *expert_ids, float *gates, float *logits, float *aux_loss, void *ws,
+              size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  const int64_t T = cfg->T, Tk = T * cfg->k;
+  if (!need(x, T, 16) || !need(w_router, 1, 16) || !opt(b_router, 4) ||
+      !need(expert_ids, Tk, 4) || !need(gates, Tk, 4) || !opt(logits, 4) ||
+      !need(aux_loss, 1, 4))
+    return MOE_ERR_INVALID_ARG;
+  rc = check_ws(cfg, MOE_ENTRY_ROUTE, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_ROUTE);
+  return hip_status(do_route(cfg, x, w_router, b_router, expert_ids, gates, logits, aux_loss,
+                             (float *)at(ws, L.qsum), (int32_t *)at(ws, L.fcount), nullptr,
+                             (hipStream_t)stream));
+}
+
+int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids, int32_t *slots,
+                 uint8_t *drop_mask, int32_t *load, int32_t *kept, void *x_disp, void *ws,
+                 size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  const int64_t T = cfg->T, Tk = T * cfg->k, C = capacity_of(cfg);
+  if (!need(x, T, 16) || !need(expert_ids, Tk, 4) || !need(slots, Tk, 4) || !opt(drop_mask, 1) ||
+      !need(load, 1, 4) || !need(kept, 1, 4) || !need(x_disp, cfg->E * C, 16))
+    return MOE_ERR_INVALID_ARG;
+  rc = check_ws(cfg, MOE_ENTRY_DISPATCH, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_DISPATCH);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *hist = (int32_t *)at(ws, L.hist), *offs = (int32_t *)at(ws, L.offs);
+  hipError_t e = moe_host::launch_dispatch_count(expert_ids, T, (int)cfg->E, (int)cfg->k, hist, s);
+  if (e == hipSuccess)
+    e = do_place_gather(cfg, x, expert_ids, hist, offs, slots, drop_mask, load, kept, x_disp, s);
+  return hip_status(e);
+}
+
+int moe_expert_ffn(const moe_config *cfg, const void *x_disp, const int32_t *kept, const void *w1,
+                   const void *w1_scale, const void *w2, const void *w2_scale, void *y_disp,
+                   void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  const int64_t rowsE = cfg->E * capacity_of(cfg);
+  const bool q8 = cfg->expert_wfmt == MOE_W_INT8_G128;
+  if (!need(x_disp, rowsE, 16) || !need(kept, 1, 4) || !need(w1, 1, 16) || !need(w2, 1, 16) ||
+      !need(y_disp, rowsE, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (q8 ? (!need(w1_scale, 1, 2) || !need(w2_scale, 1, 2)) : (w1_scale || w2_scale))
+    return MOE_ERR_INVALID_ARG;
+  rc = check_ws(cfg, MOE_ENTRY_EXPERT_FFN, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_EXPERT_FFN);
+  return hip_status(do_expert_ffn(cfg, x_disp, kept, w1, w1_scale, w2, w2_scale, y_disp,
+                                  at(ws, L.hidden), (hipStream_t)stream));
+}
+
+int moe_dense_mlp(const moe_config *cfg, const void *x, const void *wm1, const void *wm2,
+                  void *dense_out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!cfg->pr_moe) return MOE_ERR_INVALID_ARG;
+  const int64_t T = cfg->T;
+  if (!need(x, T, 16) || !need(wm1, 1, 16) || !need(wm2, 1, 16) || !need(dense_out, T, 16))
+    return MOE_ERR_INVALID_ARG;
+  const size_t hid = (size_t)T * cfg->d_ff_dense * act_size(cfg);
+  if (hid > 0 && (!ws || ws_bytes < hid || !aligned(ws, 16))) return MOE_ERR_WORKSPACE;
+  return hip_status(do_dense(cfg, x, wm1, wm2, dense_out, ws, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_config *cfg, const void *y_disp, const int32_t *expert_ids,
+                const int32_t *slots, const float *gates, const void *base, const void *base2,
+                void *y, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  const int64_t T = cfg->T, Tk = T * cfg->k;
+  if (!need(expert_ids, Tk, 4) || !need(slots, Tk, 4) || !need(gates, Tk, 4) ||
+      !opt(base, 16) || !opt(base2, 16) || !need(y, T, 16) ||
+      !need(y_disp, cfg->E * capacity_of(cfg) > 0 ? Tk : 0, 16))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe_host::launch_combine(y_disp, expert_ids, slots, gates, base, base2, y, T,
+                                             (int)cfg->d, (int)cfg->k, capacity_of(cfg),
+                                             (int)cfg->E, cfg->act_dtype == MOE_BF16,
+                                             (hipStream_t)stream));
+}
+
+int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w,
+                      moe_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  const int64_t T = cfg->T, Tk = T * cfg->k, rowsE = cfg->E * capacity_of(cfg);
+  const bool q8 = cfg->expert_wfmt == MOE_W_INT8_G128;
+  if (!need(x, T, 16) || !need(w->w_router, 1, 16) || !opt(w->b_router, 4) ||
+      !need(w->w1, 1, 16) || !need(w->w2, 1, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (q8 ? (!need(w->w1_scale, 1, 2) || !need(w->w2_scale, 1, 2))
+         : (w->w1_scale || w->w2_scale))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->pr_moe && (!need(w->wm1, 1, 16) || !need(w->wm2, 1, 16))) return MOE_ERR_INVALID_ARG;
+  if (!need(out->y, T, 16) || !need(out->expert_ids, Tk, 4) || !need(out->gates, Tk, 4) ||
+      !need(out->slots, Tk, 4) || !need(out->load, 1, 4) || !need(out->kept, 1, 4) ||
+      !need(out->aux_loss, 1, 4) || !opt(out->drop_mask, 1) || !opt(out->logits, 4) ||
+      !opt(out->x_disp, 16) || !opt(out->y_disp, 16) || !opt(out->dense_out, 16))
+    return MOE_ERR_INVALID_ARG;
+  (void)rowsE;
+  rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_LAYER);
+  hipStream_t s = (hipStream_t)stream;
+  float *qsum = (float *)at(ws, L.qsum);
+  int32_t *fcount = (int32_t *)at(ws, L.fcount), *hist = (int32_t *)at(ws, L.hist);
+  int32_t *offs = (int32_t *)at(ws, L.offs);
+  void *x_disp = out->x_disp ? out->x_disp : at(ws, L.x_disp);
+  void *y_disp = out->y_disp ? out->y_disp : at(ws, L.y_disp);
+  void *hidden = at(ws, L.hidden);
+  void *dense = nullptr;
+  if (cfg->pr_moe) dense = out->dense_out ? out->dense_out : at(ws, L.dense);
+
+  hipError_t e = do_route(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates,
+                          out->logits, out->aux_loss, qsum, fcount, hist, s);
+  if (e == hipSuccess)
+    e = do_place_gather(cfg, x, out->expert_ids, hist, offs, out->slots, out->drop_mask,
+                        out->load, out->kept, x_disp, s);
+  if (e == hipSuccess && cfg->pr_moe) e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden, s);
+  if (e == hipSuccess)
+    e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
+                      hidden, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_combine(y_disp, out->expert_ids, out->slots, out->gates,
+                                 cfg->add_skip ? x : nullptr, dense, out->y, T, (int)cfg->d,
+                                 (int)cfg->k, capacity_of(cfg), (int)cfg->E,
+                                 cfg->act_dtype == MOE_BF16, s);
+  return hip_status(e);
+}
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_profile_enable(int on) {
+  g_prof = on != 0;
+  return MOE_OK;
+}
+
+int moe_profile_reset(void) {
+  for (auto &r : g_recs) {
+    if (r.b) (void)hipEventSynchronize(r.b);
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return MOE_OK;
+}
+
+int moe_profile_read(char *names, int64_t *launches, double *total_ms, int cap) {
+  std::vector<const char *> keys;
+  std::vector<int64_t> cnt;
+  std::vector<double> ms;
+  for (auto &r : g_recs) {
+    float t = 0.f;
+    if (r.a && r.b && hipEventSynchronize(r.b) == hipSuccess &&
+        hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+      size_t i = 0;
+      while (i < keys.size() && strcmp(keys[i], r.name) != 0) i++;
+      if (i == keys.size()) {
+        keys.push_back(r.name);
+        cnt.push_back(0);
+        ms.push_back(0.0);
+      }
+      cnt[i]++;
+      ms[i] += t;
+    }
+  }
+  moe_profile_reset();
+  for (size_t i = 0; i < keys.size() && (int)i < cap; i++) {
+    if (names) {
+      strncpy(names + 64 * i, keys[i], 63);
+      names[64 * i + 63] = 0;
+    }
+    if (launches) launches[i] = cnt[i];
+    if (total_ms) total_ms[i] = ms[i];
+  }
+  return (int)keys.size();
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// common.h -- shared device types and helpers of the gfx950 MoE-layer library.
+// Internal to the library (not part of the C ABI in include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16-byte staging register (a native vector: HIP's uint4 struct copies are
+// lowered through private memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // butterfly: every lane ends with the same value, summed in a fixed order
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// (value, index) arg-max over the wave: larger value wins, equal values go
+// to the smaller index.  Every lane returns the winner.
+__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float ov = __shfl_xor(v, m, kWave);
+    int oi = __shfl_xor(idx, m, kWave);
+    if (ov > v || (ov == v && oi < idx)) {
+      v = ov;
+      idx = oi;
+    }
+  }
+}
+
+// ------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(bf16 b) { return (float)b; }
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }  // RNE
+
+// exact (erf) GELU in fp32 using the device library's erff
+__device__ __forceinline__ float gelu_f(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+template <typename T>
+struct ActTraits;
+template <>
+struct ActTraits<float> {
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+template <>
+struct ActTraits<bf16> {
+  static __device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
+  static __device__ __forceinline__ bf16 from_f(float v) { return (bf16)v; }
+};
+
+// Blocks are spread over the 8 XCDs round-robin by hardware: block b runs on
+// XCD b % 8.  Remap so each XCD receives a contiguous range of logical tiles
+// (tiles of one expert then share that XCD's L2).  Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  constexpr int X = 8;
+  const int per = n / X, rem = n % X;
+  const int x = b % X, i = b / X;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+}  // namespace moe
+
+// ------------------------------------------------------------- host side
+namespace moe_host {
+// Launch bookkeeping: records per-kernel HIP events when profiling is on.
+void prof_begin(hipStream_t s, const char *name);
+void prof_end(hipStream_t s);
+
+template <typename... KArgs, typename... Args>
+inline void launch(const char *name, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                   hipStream_t s, Args... args) {
+  prof_begin(s, name);
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+  prof_end(s);
+}
+}  // namespace moe_host
+
+#define MOE_LAUNCH(name, kernel, grid, block, lds, stream, ...) \
+  moe_host::launch((name), kernel, (grid), (block), (lds), (stream), __VA_ARGS__)

@@ -1,0 +1,182 @@
+// dispatch.hip -- capacity-limited, token-order dispatch and the layout
+// transform into the expert-major buffer [E, C, d].
+//
+// Method: "DeepSpeed MoE and Model Compression", pipeline step
+// pack_by_expert(hidden, expert_ids, capacity); "DeepSpeed-MoE vs Switch
+// Transformer", section "expert capacity overflow" (per-expert cap; an
+// overflowing token skips the expert); "DeepSpeed-MoE ... notes" sec. 4.4
+// (a cumulative sum over tokens gives each assignment its place in a dense
+// token-to-expert mapping table, and rows are then moved with that table
+// instead of one-hot masks, so the cost does not grow with E).
+//
+// The slot of assignment (t, j) in expert e is the number of assignments to e
+// that come before it in token order; it is kept iff slot < C.  Computed
+// deterministically without order-dependent atomics:
+//   count : per 64-token block, an integer histogram over experts
+//   scan  : exclusive prefix over blocks, per expert -> block offsets,
+//           load[e] = total, kept[e] = min(load[e], C)
+//   place : one wave per block walks its 64*k assignments in order in chunks
+//           of 64; within a chunk, lanes with equal expert ids are grouped
+//           with ballots, ranked by lane order (popcount of the lower lanes),
+//           and the running per-expert count lives in registers spread over
+//           the lanes (expert e in lane e % 64, register e / 64)
+//   gather: one wave per assignment copies the token's row to its slot with
+//           16-byte vector loads/stores (each row is contiguous on both sides,
+//           so the copy is fully coalesced without staging)
+// Expert ids outside [0, E) are treated as dropped and not counted.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int DBT = 64;  // tokens per dispatch block (the router's block size)
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t *ids, int64_t T, int E,
+                                                             int k, int32_t *hist) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int64_t a0 = (int64_t)blk * DBT * k;
+  int64_t a1 = a0 + (int64_t)DBT * k;
+  if (a1 > T * k) a1 = T * k;
+  for (int64_t a = a0 + tid; a < a1; a += 256) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) hist[(int64_t)blk * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t *hist, int nblk, int E,
+                                                            int64_t C, int32_t *offs,
+                                                            int32_t *load, int32_t *kept) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  int run = 0;
+  for (int b = 0; b < nblk; b++) {
+    const int64_t o = (int64_t)b * E + e;
+    const int h = hist[o];
+    offs[o] = run;
+    run += h;
+  }
+  load[e] = run;
+  kept[e] = (int64_t)run < C ? run : (int32_t)C;
+}
+
+__device__ __forceinline__ int sel4(int v0, int v1, int v2, int v3, int i) {
+  return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
+
+__global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, const int32_t *offs,
+                                                            int64_t T, int E, int k, int64_t C,
+                                                            int32_t *slots, uint8_t *drop) {
+  const int lane = lane_id(), blk = blockIdx.x;
+  // running slot of expert e = lane + 64 i, starting at this block's offset
+  int run0 = 0, run1 = 0, run2 = 0, run3 = 0;
+  {
+    const int64_t o = (int64_t)blk * E;
+    if (lane < E) run0 = offs[o + lane];
+    if (lane + 64 < E) run1 = offs[o + lane + 64];
+    if (lane + 128 < E) run2 = offs[o + lane + 128];
+    if (lane + 192 < E) run3 = offs[o + lane + 192];
+  }
+  const int64_t a0 = (int64_t)blk * DBT * k;
+  int64_t a1 = a0 + (int64_t)DBT * k;
+  if (a1 > T * k) a1 = T * k;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = a0; base < a1; base += 64) {
+    const int64_t a = base + lane;
+    int e = (a < a1) ? ids[a] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = -1;
+    int slot = -1;
+    uint64_t rem = __ballot(valid);
+    while (rem) {
+      const int leader = __ffsll((long long)rem) - 1;
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t mask = __ballot(e == el);
+      const int ri = el >> 6, rl = el & 63;
+      const int start = __builtin_amdgcn_readlane(sel4(run0, run1, run2, run3, ri), rl);
+      if (e == el) slot = start + __popcll(mask & lower);
+      if (lane == rl) {
+        const int add = __popcll(mask);
+        if (ri == 0) run0 += add;
+        else if (ri == 1) run1 += add;
+        else if (ri == 2) run2 += add;
+        else run3 += add;
+      }
+      rem &= ~mask;
+    }
+    if (a < a1) {
+      const bool keep = valid && (int64_t)slot < C;
+      slots[a] = keep ? slot : -1;
+      if (drop) drop[a] = keep ? 0 : 1;
+    }
+  }
+}
+
+// one wave per assignment; VT = the vector type moved per lane
+template <typename VT>
+__global__ __launch_bounds__(256) void gather_kernel(const char *x, const int32_t *ids,
+                                                     const int32_t *slots, int64_t n_assign, int k,
+                                                     int64_t C, int64_t row_bytes, char *x_disp) {
+  const int lane = lane_id();
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t nvec = row_bytes / (int64_t)sizeof(VT);
+  for (int64_t a = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave; a < n_assign; a += nw) {
+    const int slot = __builtin_amdgcn_readfirstlane(slots[a]);
+    if (slot < 0) continue;
+    const int e = __builtin_amdgcn_readfirstlane(ids[a]);
+    const VT *src = (const VT *)(x + (a / k) * row_bytes);
+    VT *dst = (VT *)(x_disp + ((int64_t)e * C + slot) * row_bytes);
+    for (int64_t c = lane; c < nvec; c += kWave) dst[c] = src[c];
+  }
+}
+
+}  // namespace moe
+
+namespace moe_host {
+using namespace moe;
+
+hipError_t launch_dispatch_count(const int32_t *ids, int64_t T, int E, int k, int32_t *hist,
+                                 hipStream_t s) {
+  const int nblk = (int)((T + DBT - 1) / DBT);
+  if (nblk > 0)
+    MOE_LAUNCH("dispatch_count", dispatch_count_kernel, dim3(nblk), dim3(256), 0, s, ids, T, E, k,
+               hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(const int32_t *hist, int nblk, int E, int64_t C, int32_t *offs,
+                                int32_t *load, int32_t *kept, hipStream_t s) {
+  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(256), 0, s, hist, nblk, E, C,
+             offs, load, kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
+                                 int64_t C, int32_t *slots, uint8_t *drop, hipStream_t s) {
+  const int nblk = (int)((T + DBT - 1) / DBT);
+  if (nblk > 0)
+    MOE_LAUNCH("dispatch_place", dispatch_place_kernel, dim3(nblk), dim3(64), 0, s, ids, offs, T,
+               E, k, C, slots, drop);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots, int64_t T, int k,
+                         int64_t C, int64_t row_bytes, void *x_disp, hipStream_t s) {
+  const int64_t n = T * k;
+  if (n <= 0) return hipGetLastError();
+  int64_t blocks = (n + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (row_bytes % 16 == 0)
+    MOE_LAUNCH("gather_x16", gather_kernel<u32x4>, dim3((unsigned)blocks), dim3(256), 0, s,
+               (const char *)x, ids, slots, n, k, C, row_bytes, (char *)x_disp);
+  else
+    MOE_LAUNCH("gather_x4", gather_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+               (const char *)x, ids, slots, n, k, C, row_bytes, (char *)x_disp);
+  return hipGetLastError();
+}
+
+}  // namespace moe_host

@@ -1,0 +1,313 @@
+// gemm.hip -- grouped expert GEMMs (and the PR-MoE dense MLP) on gfx950.
+//
+// Method: survey notes sec. 1.1.2.1 (each expert is a two-layer FFN that
+// replaces the transformer FFN); "DeepSpeed-MoE ... notes" sec. 4.4 and its
+// closing outline ("sparse GEMM -> dense GEMM": after the layout transform
+// each expert runs a dense GEMM on its packed rows); survey notes sec.
+// 1.2.3.1 (weight-only quantisation: low-precision weights are dequantised
+// for the arithmetic) with the symmetric form of sec. 1.2.2 (w = s * q).
+//
+// C[g][m][n] = epi( sum_k A[g][m][k] * B[g][n][k] ),  m < rows[g]
+// A: activations [G][M_cap][K] (x_disp, H or x), K contiguous.
+// B: weights [G][N][K] ([out, in], K contiguous), bf16 or int8 + fp16 scale
+//    per 128 K-elements of a row.  epi = GELU (first layer) or identity.
+//
+// bf16 path: a BM x BN block tile, 64-wide K steps double-buffered through
+// LDS (rows padded to 144 B so the 16-byte MFMA operand reads are free of
+// bank conflicts), register prefetch of the next K step while the MFMAs run
+// on the current one.  Each wave owns a WTM x WTN sub-tile of 32x32x16 (or
+// 16x16x32) bf16 MFMAs accumulating in fp32.  int8 weights are converted to
+// bf16 (s * q rounded once) on their way into LDS, so the MFMA loop is the
+// same as for bf16 weights.  Rows past rows[g] are neither read (their loads
+// are clamped to the last valid row) nor written; blocks whose first row is
+// past rows[g] exit at once, so only kept rows cost MFMA time, and only
+// experts with at least one kept row stream their weights.
+// Blocks are mapped to tiles XCD by XCD (contiguous tile ranges per XCD), so
+// the N-tiles of one expert share that XCD's L2 for their A rows.
+#include "common.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace moe {
+
+template <int BM, int BN, int WM, int WN, int MF, bool BINT8, bool GELU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BK = 64;
+  constexpr int LDK = BK + 8;  // 144-byte LDS rows
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / MF, TN = WTN / MF;
+  constexpr int KSTEP = (MF == 32) ? 16 : 32;
+  constexpr int ACC = (MF == 32) ? 16 : 4;
+  constexpr int A_CH = BM * 8;                    // 16-byte chunks per A stage
+  constexpr int A_PT = (A_CH + NT - 1) / NT;
+  constexpr int B_CPR = BINT8 ? 4 : 8;            // 16-byte chunks per B row
+  constexpr int B_CH = BN * B_CPR;
+  constexpr int B_PT = (B_CH + NT - 1) / NT;
+  constexpr int STAGE = (BM + BN) * LDK;          // bf16 elements per LDS stage
+  static_assert(TM >= 1 && TN >= 1 && WTM % MF == 0 && WTN % MF == 0, "bad tile");
+  typedef typename std::conditional<MF == 32, f32x16, f32x4>::type acc_t;
+
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int tiles_n = a.N / BN;
+  const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
+  const int total = a.G * tiles_m * tiles_n;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int64_t rows = a.M_cap;
+  if (a.rows) {
+    const int64_t r = a.rows[g];
+    rows = r < rows ? r : rows;
+  }
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= rows) return;
+  const int n0 = tn * BN;
+  const int K = a.K, N = a.N;
+
+  const bf16 *Ag = (const bf16 *)a.A + (int64_t)g * a.M_cap * K;
+  const bf16 *Bg = (const bf16 *)a.B + (int64_t)g * N * K;
+  const int8_t *Bq = (const int8_t *)a.B + (int64_t)g * N * K;
+  const _Float16 *Sg = (const _Float16 *)a.Bscale + (int64_t)g * N * (K / 128);
+  bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+
+  u32x4 ra[A_PT], rb[B_PT];
+  float rs[BINT8 ? B_PT : 1];
+  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < A_PT; p++) {
+      const int c = tid + p * NT;
+      if (A_CH % NT == 0 || c < A_CH) {
+        int64_t m = m0 + (c >> 3);
+        if (m >= rows) m = rows - 1;
+        ra[p] = *(const u32x4 *)(Ag + m * K + k0 + (c & 7) * 8);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < B_PT; p++) {
+      const int c = tid + p * NT;
+      if (B_CH % NT == 0 || c < B_CH) {
+        const int64_t n = n0 + c / B_CPR;
+        if constexpr (BINT8) {
+          const int kk = k0 + (c % B_CPR) * 16;
+          rb[p] = *(const u32x4 *)(Bq + n * K + kk);
+          rs[p] = (float)Sg[n * (K / 128) + kk / 128];
+        } else {
+          rb[p] = *(const u32x4 *)(Bg + n * K + k0 + (c % B_CPR) * 8);
+        }
+      }
+    }
+  };
+  auto store_tiles = [&](int st) __attribute__((always_inline)) {
+    bf16 *sa = smem + st * STAGE;
+    bf16 *sb = sa + BM * LDK;
+#pragma unroll
+    for (int p = 0; p < A_PT; p++) {
+      const int c = tid + p * NT;
+      if (A_CH % NT == 0 || c < A_CH) *(u32x4 *)(sa + (c >> 3) * LDK + (c & 7) * 8) = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < B_PT; p++) {
+      const int c = tid + p * NT;
+      if (B_CH % NT == 0 || c < B_CH) {
+        if constexpr (BINT8) {
+          // 16 int8 codes -> 16 bf16 values s*q (one rounding)
+          const int8_t *q = (const int8_t *)&rb[p];
+          bf16x8 lo, hi;
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            lo[i] = (bf16)(rs[p] * (float)q[i]);
+            hi[i] = (bf16)(rs[p] * (float)q[8 + i]);
+          }
+          bf16 *dst = sb + (c / B_CPR) * LDK + (c % B_CPR) * 16;
+          *(bf16x8 *)dst = lo;
+          *(bf16x8 *)(dst + 8) = hi;
+        } else {
+          *(u32x4 *)(sb + (c / B_CPR) * LDK + (c % B_CPR) * 8) = rb[p];
+        }
+      }
+    }
+  };
+
+  acc_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < ACC; r++) acc[i][j][r] = 0.f;
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int ksteps = K / BK;
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; kt++) {
+    const int st = kt & 1;
+    if (kt + 1 < ksteps) load_tiles((kt + 1) * BK);
+    const bf16 *sa = smem + st * STAGE + (wm * WTM) * LDK;
+    const bf16 *sb = smem + st * STAGE + BM * LDK + (wn * WTN) * LDK;
+#pragma unroll
+    for (int s = 0; s < BK / KSTEP; s++) {
+      int row, ch;
+      if constexpr (MF == 32) {
+        row = lane & 31;
+        ch = 2 * s + (lane >> 5);
+      } else {
+        row = lane & 15;
+        ch = 4 * s + (lane >> 4);
+      }
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; i++) af[i] = *(const bf16x8 *)(sa + (i * MF + row) * LDK + ch * 8);
+#pragma unroll
+      for (int j = 0; j < TN; j++) bfr[j] = *(const bf16x8 *)(sb + (j * MF + row) * LDK + ch * 8);
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          if constexpr (MF == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < ksteps) store_tiles(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: D[m][n] of a 32x32 MFMA sits in lane n (+32 for rows 4..7 of
+  // each group of 8) -- row 8*(r/4) + 4*(lane/32) + r%4, column lane%32; of a
+  // 16x16 MFMA: row 4*(lane/16) + r, column lane%16.
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < ACC; r++) {
+        int mr, nc;
+        if constexpr (MF == 32) {
+          mr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          nc = lane & 31;
+        } else {
+          mr = 4 * (lane >> 4) + r;
+          nc = lane & 15;
+        }
+        const int64_t m = m0 + wm * WTM + i * MF + mr;
+        const int n = n0 + wn * WTN + j * MF + nc;
+        float v = acc[i][j][r];
+        if (GELU) v = gelu_f(v);
+        if (m < rows) Cg[m * N + n] = (bf16)v;
+      }
+}
+
+// fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
+// any shape (bounds-checked); the correctness path for fp32 layers.
+template <bool GELU>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  constexpr int T = 64, BKF = 16;
+  __shared__ float As[BKF][T + 1], Bs[BKF][T + 1];
+  const int tiles_n = (a.N + T - 1) / T;
+  const int tiles_m = (int)((a.M_cap + T - 1) / T);
+  const int tile = blockIdx.x;
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int64_t rows = a.M_cap;
+  if (a.rows) {
+    const int64_t r = a.rows[g];
+    rows = r < rows ? r : rows;
+  }
+  const int64_t m0 = (int64_t)tm * T;
+  if (m0 >= rows) return;
+  const int n0 = tn * T, K = a.K, N = a.N;
+  const float *Ag = (const float *)a.A + (int64_t)g * a.M_cap * K;
+  const float *Bg = (const float *)a.B + (int64_t)g * N * K;
+  float *Cg = (float *)a.C + (int64_t)g * a.M_cap * N;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BKF) {
+    for (int i = threadIdx.x; i < BKF * T; i += 256) {
+      const int r = i / BKF, kk = i % BKF;
+      const int64_t m = m0 + r;
+      const int n = n0 + r, k = k0 + kk;
+      As[kk][r] = (m < rows && k < K) ? Ag[m * K + k] : 0.f;
+      Bs[kk][r] = (n < N && k < K) ? Bg[(int64_t)n * K + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BKF; kk++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = fmaf(As[kk][ty * 4 + i], Bs[kk][tx * 4 + j], acc[i][j]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t m = m0 + ty * 4 + i;
+      const int n = n0 + tx * 4 + j;
+      if (m < rows && n < N) Cg[m * N + n] = GELU ? gelu_f(acc[i][j]) : acc[i][j];
+    }
+}
+
+}  // namespace moe
+
+namespace moe_host {
+using namespace moe;
+
+template <int BM, int BN, int WM, int WN, int MF>
+static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_t s,
+                             const char *name) {
+  const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
+  if (tiles <= 0) return hipGetLastError();
+  const dim3 grid(tiles), block(64 * WM * WN);
+  if (b_int8) {
+    if (gelu)
+      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, true, true>), grid, block, 0, s, a);
+    else
+      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, true, false>), grid, block, 0, s, a);
+  } else {
+    if (gelu)
+      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, false, true>), grid, block, 0, s, a);
+    else
+      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// Tile choice by rows per group (the capacity, or T for the dense MLP) and N.
+hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, hipStream_t s) {
+  if (a.G <= 0 || a.M_cap <= 0 || a.N <= 0) return hipGetLastError();
+  if (!act_bf16) {
+    const int tiles = a.G * (int)((a.M_cap + 63) / 64) * ((a.N + 63) / 64);
+    if (gelu)
+      MOE_LAUNCH("gemm_f32_gelu", gemm_f32_kernel<true>, dim3(tiles), dim3(256), 0, s, a);
+    else
+      MOE_LAUNCH("gemm_f32", gemm_f32_kernel<false>, dim3(tiles), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  const bool g1 = gelu != 0;
+  if (a.M_cap > 256 && a.N % 256 == 0)
+    return launch_cfg<256, 256, 2, 4, 32>(a, b_int8, gelu, s,
+                                          g1 ? "gemm_bm256_bn256_gelu" : "gemm_bm256_bn256");
+  if (a.M_cap > 64 && a.N % 128 == 0)
+    return launch_cfg<128, 128, 2, 2, 32>(a, b_int8, gelu, s,
+                                          g1 ? "gemm_bm128_bn128_gelu" : "gemm_bm128_bn128");
+  if (a.M_cap > 32 && a.N % 128 == 0)
+    return launch_cfg<64, 128, 1, 4, 32>(a, b_int8, gelu, s,
+                                         g1 ? "gemm_bm64_bn128_gelu" : "gemm_bm64_bn128");
+  if (a.M_cap > 16 && a.N % 128 == 0)
+    return launch_cfg<32, 128, 1, 4, 32>(a, b_int8, gelu, s,
+                                         g1 ? "gemm_bm32_bn128_gelu" : "gemm_bm32_bn128");
+  return launch_cfg<16, 64, 1, 4, 16>(a, b_int8, gelu, s,
+                                      g1 ? "gemm_bm16_bn64_gelu" : "gemm_bm16_bn64");
+}
+
+}  // namespace moe_host

@@ -1,0 +1,63 @@
+// kernels.h -- internal launcher declarations (host side) of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  const void *x;      // [T, d] act
+  const void *w;      // [E, d] act
+  const float *bias;  // [E] or null
+  int32_t *ids;       // [T, k]
+  float *gates;       // [T, k]
+  float *logits;      // [T, E] or null
+  float *qsum;        // [nblk, E] per-block sum of router probabilities
+  int32_t *fcount;    // [nblk, E] per-block count of first choices
+  int32_t *hist;      // [nblk, E] per-block count of all k assignments (or null)
+  int64_t T;
+  int d, E, k, normalize;
+};
+
+// Grouped "NT" GEMM: for each group g < G and row m < rows[g] (or M_cap):
+//   C[g][m][n] = epi( sum_k A[g][m][k] * B[g][n][k] )
+struct GemmArgs {
+  const void *A;        // act, [G][M_cap][K] (row stride K)
+  const void *B;        // act or int8, [G][N][K]
+  const void *Bscale;   // fp16 [G][N][K/128] (int8 only)
+  void *C;              // act, [G][M_cap][N]
+  const int32_t *rows;  // [G] valid rows per group (device) or null = M_cap
+  int64_t M_cap;
+  int N, K, G;
+};
+
+}  // namespace moe
+
+namespace moe_host {
+
+int router_blocks(int64_t T);
+hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
+hipError_t launch_aux_final(const float *qsum, const int32_t *fcount, int nblk, int E,
+                            int64_t T, float alpha, float *aux, hipStream_t s);
+
+// dispatch (token blocks of the same size as the router's)
+hipError_t launch_dispatch_count(const int32_t *ids, int64_t T, int E, int k, int32_t *hist,
+                                 hipStream_t s);
+hipError_t launch_dispatch_scan(const int32_t *hist, int nblk, int E, int64_t C, int32_t *offs,
+                                int32_t *load, int32_t *kept, hipStream_t s);
+hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
+                                 int64_t C, int32_t *slots, uint8_t *drop, hipStream_t s);
+hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots, int64_t T, int k,
+                         int64_t C, int64_t row_bytes, void *x_disp, hipStream_t s);
+
+// expert / dense GEMMs; gelu selects the GELU epilogue
+hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gelu,
+                       hipStream_t s);
+
+hipError_t launch_combine(const void *y_disp, const int32_t *ids, const int32_t *slots,
+                          const float *gates, const void *base, const void *base2, void *y,
+                          int64_t T, int d, int k, int64_t C, int E, int act_bf16,
+                          hipStream_t s);
+
+}  // namespace moe_host

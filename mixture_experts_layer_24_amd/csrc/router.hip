@@ -1,0 +1,322 @@
+// router.hip -- fused router: logits = x W_r^T (+ b), softmax, top-k gate,
+// per-block load-balance statistics and per-block assignment histogram.
+//
+// Method: "DeepSpeed MoE and Model Compression", section "DeepSpeed-MoE"
+// (p(x) = softmax(W_r x), TopK over p); "DeepSpeed-MoE vs Switch
+// Transformer", section "router computation" (logits = x W_r, softmax);
+// survey notes sec. 1.1.1.1 (renormalise after TopK) and sec. 1.1.4.1
+// (f_i, Q_i of the Switch load-balance loss); "DeepSpeed-MoE ... notes" sec.
+// 4.4 (top-k fused with the counting that feeds the cumsum mapping table).
+//
+// One block = 64 tokens x all experts (E <= 256, padded to a multiple of 32).
+// bf16: the 64 x Ep logit tile is a bf16 MFMA contraction (32x32x16, fp32
+// accumulate; the bf16 products are exact in fp32) over d in 64-wide K steps,
+// double-buffered through LDS.  fp32: plain fp32 FMA dot products.
+// The epilogue is shared: the tile goes to LDS, each wave takes 16 rows; a
+// row's E logits sit 1-4 per lane and wave shuffles give the row max, the
+// softmax sum and the arg-max rounds of the top-k.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int RBM = 64;       // tokens per block
+constexpr int RBK = 64;       // K step (elements)
+constexpr int RLDA = RBK + 8; // LDS row stride in bf16 (144 B: conflict-free b128 reads)
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// L: LDS logits tile [RBM][ldl] fp32 (bias not yet added).
+template <int MAXK>
+__device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
+                                float (*qpart)[256], int *fcnt, int *hcnt, int blk) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int E = a.E, k = a.k;
+  float q[4] = {0.f, 0.f, 0.f, 0.f};
+  float bias[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
+  }
+  for (int rr = 0; rr < RBM / 4; rr++) {
+    const int r = wave * (RBM / 4) + rr;
+    const int64_t t = (int64_t)blk * RBM + r;
+    if (t >= a.T) break;
+    float v[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e = lane + kWave * i;
+      live[i] = e < E;
+      v[i] = live[i] ? L[r * ldl + e] + bias[i] : neg_inf();
+      if (a.logits && live[i]) a.logits[t * E + e] = v[i];
+    }
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    m = wave_max(m);
+    float p[4], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      p[i] = live[i] ? expf(v[i] - m) : 0.f;
+      s += p[i];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      p[i] = p[i] / s;
+      q[i] += p[i];
+    }
+    // top-k by repeated wave arg-max (larger logit, then lower index)
+    bool taken[4] = {false, false, false, false};
+    int sel[MAXK];
+    float selp[MAXK];
+#pragma unroll
+    for (int j = 0; j < MAXK; j++) {
+      sel[j] = 0;
+      selp[j] = 0.f;
+      if (j < k) {
+        float bv = neg_inf();
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = lane + kWave * i;
+          if (live[i] && !taken[i] && (be == 0x7fffffff || v[i] > bv)) {
+            bv = v[i];
+            be = e;
+          }
+        }
+        wave_argmax(bv, be);
+        const int owner_i = be / kWave;
+        float pi = p[0];
+        if (owner_i == 1) pi = p[1];
+        if (owner_i == 2) pi = p[2];
+        if (owner_i == 3) pi = p[3];
+        selp[j] = __shfl(pi, be % kWave, kWave);
+        sel[j] = be;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (lane + kWave * i == be) taken[i] = true;
+      }
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXK; j++)
+      if (j < k) den += selp[j];
+    const bool renorm = (k >= 2) && a.normalize;
+    // lane j writes choice j
+    int my_e = 0;
+    float my_p = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXK; j++)
+      if (lane == j) {
+        my_e = sel[j];
+        my_p = selp[j];
+      }
+    if (lane < k) {
+      a.ids[t * k + lane] = my_e;
+      a.gates[t * k + lane] = renorm ? my_p / den : my_p;
+      atomicAdd(&hcnt[my_e], 1);
+      if (lane == 0) atomicAdd(&fcnt[my_e], 1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    if (e < E) qpart[wave][e] = q[i];
+  }
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e < E) {
+    const int64_t o = (int64_t)blk * E + e;
+    a.qsum[o] = ((qpart[0][e] + qpart[1][e]) + qpart[2][e]) + qpart[3][e];
+    a.fcount[o] = fcnt[e];
+    if (a.hist) a.hist[o] = hcnt[e];
+  }
+}
+
+// NTW = 32-wide expert tiles per wave (Ep <= 64 * NTW)
+template <int NTW>
+__global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
+  constexpr int EPMAX = 64 * NTW;
+  constexpr int STAGE = (RBM + EPMAX) * RLDA;  // bf16 elements per stage
+  constexpr int TILE_BYTES = 2 * STAGE * 2;
+  constexpr int LOGIT_BYTES = RBM * (EPMAX + 4) * 4;
+  constexpr int SMEM = TILE_BYTES > LOGIT_BYTES ? TILE_BYTES : LOGIT_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ float qpart[4][256];
+  __shared__ int fcnt[256], hcnt[256];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int blk = blockIdx.x;
+  const int E = a.E, Ep = (E + 31) & ~31, d = a.d;
+  for (int i = tid; i < 256; i += 256) {
+    fcnt[i] = 0;
+    hcnt[i] = 0;
+  }
+  bf16 *As = (bf16 *)smem;
+  const bf16 *X = (const bf16 *)a.x;
+  const bf16 *W = (const bf16 *)a.w;
+
+  // global -> register prefetch: x tile 64 x 64 (2 chunks/thread),
+  // W tile Ep x 64 (Ep/32 chunks/thread, at most 2*NTW)
+  const int crow = tid >> 3, cchk = tid & 7;
+  u32x4 ra[2], rw[2 * NTW];
+  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      int64_t t = (int64_t)blk * RBM + p * 32 + crow;
+      if (t >= a.T) t = a.T - 1;
+      ra[p] = *(const u32x4 *)(X + t * d + k0 + cchk * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 2 * NTW; p++) {
+      int e = p * 32 + crow;
+      if (p * 32 < Ep) {
+        if (e >= E) e = E - 1;
+        rw[p] = *(const u32x4 *)(W + (int64_t)e * d + k0 + cchk * 8);
+      }
+    }
+  };
+  auto store_tiles = [&](int st) __attribute__((always_inline)) {
+    bf16 *sa = As + st * STAGE;
+    bf16 *sw = sa + RBM * RLDA;
+#pragma unroll
+    for (int p = 0; p < 2; p++) *(u32x4 *)(sa + (p * 32 + crow) * RLDA + cchk * 8) = ra[p];
+#pragma unroll
+    for (int p = 0; p < 2 * NTW; p++)
+      if (p * 32 < Ep) *(u32x4 *)(sw + (p * 32 + crow) * RLDA + cchk * 8) = rw[p];
+  };
+
+  f32x16 acc[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; i++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
+
+  const int mt = wave & 1;  // 32-row half of the token tile
+  const int ksteps = d / RBK;
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; kt++) {
+    const int st = kt & 1;
+    if (kt + 1 < ksteps) load_tiles((kt + 1) * RBK);
+    const bf16 *sa = As + st * STAGE;
+    const bf16 *sw = sa + RBM * RLDA;
+#pragma unroll
+    for (int s = 0; s < RBK / 16; s++) {
+      const int ch = 2 * s + (lane >> 5);
+      bf16x8 av = *(const bf16x8 *)(sa + (mt * 32 + (lane & 31)) * RLDA + ch * 8);
+#pragma unroll
+      for (int i = 0; i < NTW; i++) {
+        const int nt = (wave >> 1) + 2 * i;
+        if (nt * 32 < Ep) {
+          bf16x8 bv = *(const bf16x8 *)(sw + (nt * 32 + (lane & 31)) * RLDA + ch * 8);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < ksteps) store_tiles(st ^ 1);
+    __syncthreads();
+  }
+  // accumulators -> LDS logits tile
+  float *L = (float *)smem;
+  const int ldl = EPMAX + 4;
+#pragma unroll
+  for (int i = 0; i < NTW; i++) {
+    const int nt = (wave >> 1) + 2 * i;
+    if (nt * 32 < Ep) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        L[m * ldl + nt * 32 + (lane & 31)] = acc[i][r];
+      }
+    }
+  }
+  __syncthreads();
+  if (a.k <= 2)
+    router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
+  else
+    router_epilogue<8>(a, L, ldl, qpart, fcnt, hcnt, blk);
+}
+
+// fp32 activations: plain fp32 dot products (small shapes; correctness path)
+__global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
+  __shared__ float L[RBM * 260];
+  __shared__ float qpart[4][256];
+  __shared__ int fcnt[256], hcnt[256];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int E = a.E, d = a.d, ldl = 260;
+  fcnt[tid] = 0;
+  hcnt[tid] = 0;
+  const float *X = (const float *)a.x, *W = (const float *)a.w;
+  for (int idx = tid; idx < RBM * E; idx += 256) {
+    const int r = idx / E, e = idx % E;
+    const int64_t t = (int64_t)blk * RBM + r;
+    float s = 0.f;
+    if (t < a.T)
+      for (int i = 0; i < d; i++) s = fmaf(X[t * d + i], W[(int64_t)e * d + i], s);
+    L[r * ldl + e] = s;
+  }
+  __syncthreads();
+  if (a.k <= 2)
+    router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
+  else
+    router_epilogue<8>(a, L, ldl, qpart, fcnt, hcnt, blk);
+}
+
+// Switch load-balance loss from the per-block partials, in a fixed order:
+// loss = alpha * E * sum_e (F_e / T) (Q_e / T), sums in fp64.
+__global__ __launch_bounds__(256) void aux_final_kernel(const float *qsum, const int32_t *fcount,
+                                                        int nblk, int E, int64_t T, float alpha,
+                                                        float *aux) {
+  __shared__ double term[256];
+  const int e = threadIdx.x;
+  double qe = 0.0, fe = 0.0;
+  if (e < E)
+    for (int b = 0; b < nblk; b++) {
+      qe += (double)qsum[(int64_t)b * E + e];
+      fe += (double)fcount[(int64_t)b * E + e];
+    }
+  term[e] = (e < E && T > 0) ? (fe / (double)T) * (qe / (double)T) : 0.0;
+  __syncthreads();
+  for (int s = 128; s >= 1; s >>= 1) {
+    if (e < s) term[e] += term[e + s];
+    __syncthreads();
+  }
+  if (e == 0) aux[0] = (float)((double)alpha * (double)E * term[0]);
+}
+
+}  // namespace moe
+
+namespace moe_host {
+using namespace moe;
+
+int router_blocks(int64_t T) { return (int)((T + RBM - 1) / RBM); }
+
+hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
+  const int nblk = router_blocks(a.T);
+  if (nblk > 0) {
+    if (act_bf16) {
+      const int ntw = ((a.E + 31) / 32 + 1) / 2;
+      switch (ntw) {
+        case 1: MOE_LAUNCH("router_bf16_e64", router_bf16_kernel<1>, dim3(nblk), dim3(256), 0, s, a); break;
+        case 2: MOE_LAUNCH("router_bf16_e128", router_bf16_kernel<2>, dim3(nblk), dim3(256), 0, s, a); break;
+        case 3: MOE_LAUNCH("router_bf16_e192", router_bf16_kernel<3>, dim3(nblk), dim3(256), 0, s, a); break;
+        default: MOE_LAUNCH("router_bf16_e256", router_bf16_kernel<4>, dim3(nblk), dim3(256), 0, s, a); break;
+      }
+    } else {
+      MOE_LAUNCH("router_f32", router_f32_kernel, dim3(nblk), dim3(256), 0, s, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_aux_final(const float *qsum, const int32_t *fcount, int nblk, int E, int64_t T,
+                            float alpha, float *aux, hipStream_t s) {
+  MOE_LAUNCH("aux_final", aux_final_kernel, dim3(1), dim3(256), 0, s, qsum, fcount, nblk, E, T,
+             alpha, aux);
+  return hipGetLastError();
+}
+
+}  // namespace moe_host
