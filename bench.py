@@ -1,0 +1,287 @@
+"""Benchmark: MoE-layer forward tokens/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one moe_layer_forward (router + softmax/top-k + aux loss, dispatch,
+PR-MoE dense MLP, expert FFNs, combine) over one batch of seeded synthetic
+tokens already resident in HBM.  The default workload is the 1.3B+PR-MoE-128
+layer (T=16384, d=2048, E=128 top-1 experts with d_ff=8192 plus a dense MLP
+with d_ff=8192, bf16); the other workloads are parity cases and can be timed
+with --workload.  One JSON line is printed:
+
+  value      whole-job tokens/s over the K timed steps (host clock around
+             device-synchronised steps)
+  roofline   the dominant kernel (most time per step): algorithmic bytes or
+             FLOPs per launch divided by its mean launch time, measured with
+             HIP events recorded on the launch stream around each kernel
+             during the timed steps; traffic = HBM bytes per launch from the
+             committed rocprofv3 counter summary when it was taken on the
+             current kernel source, else null
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+             (routing and dispatch on every token, expert FFN and dense MLP on a
+             seeded token sample, extrapolated linearly in tokens)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1.3B+MoE-128 shape; % bf16 MFMA peak / % HBM BW"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector/matrix, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------- algorithmic work
+def kernel_work(wl, kept, cfg_C):
+    """Algorithmic bytes and FLOPs of one launch of each kernel class.
+
+    Expert GEMM1: reads the weights of experts with >= 1 kept row once, reads
+    the kept rows of x_disp, writes the kept rows of H; FLOPs 2*N_kept*d*d_ff.
+    Expert GEMM2: weights of active experts, kept rows of H in, kept rows of
+    y_disp out; FLOPs 2*N_kept*d_ff*d.  Dense GEMM1/2: x, Wm1, Hd / Hd, Wm2,
+    D; FLOPs 2*T*d*d_ff_dense each.  int8 weights count 1 byte plus 2 bytes
+    of scale per 128.
+    """
+    sa = 4 if wl.act == "f32" else 2
+    n_kept = int(sum(kept))
+    n_act = int(sum(1 for v in kept if v > 0))
+    if wl.wfmt == "int8":
+        wbytes = n_act * wl.d * wl.d_ff * (1 + 2 / 128)
+    else:
+        wbytes = n_act * wl.d * wl.d_ff * sa
+    out = {
+        "expert_gemm1": dict(bytes=wbytes + n_kept * (wl.d + wl.d_ff) * sa,
+                             flops=2.0 * n_kept * wl.d * wl.d_ff),
+        "expert_gemm2": dict(bytes=wbytes + n_kept * (wl.d_ff + wl.d) * sa,
+                             flops=2.0 * n_kept * wl.d_ff * wl.d),
+    }
+    if wl.pr_moe:
+        T, d, F = wl.T, wl.d, wl.d_ff_dense
+        out["dense_gemm1"] = dict(bytes=(T * d + F * d + T * F) * sa, flops=2.0 * T * d * F)
+        out["dense_gemm2"] = dict(bytes=(T * F + d * F + T * d) * sa, flops=2.0 * T * d * F)
+    out["router"] = dict(bytes=(wl.T * wl.d + wl.E * wl.d) * sa + wl.T * wl.k * 8,
+                         flops=2.0 * wl.T * wl.d * wl.E)
+    out["gather"] = dict(bytes=2.0 * n_kept * wl.d * sa, flops=0.0)
+    out["combine"] = dict(bytes=(n_kept + wl.T * (1 + int(wl.add_skip) + int(wl.pr_moe)))
+                          * wl.d * sa, flops=2.0 * n_kept * wl.d)
+    return out
+
+
+def classify(name: str) -> str | None:
+    """Work class of a library kernel name (names are "<role>:<tile>" for
+    GEMMs, the kernel's own name otherwise)."""
+    for prefix, cls in (("expert_ffn1", "expert_gemm1"), ("expert_ffn2", "expert_gemm2"),
+                        ("dense_mlp1", "dense_gemm1"), ("dense_mlp2", "dense_gemm2"),
+                        ("router", "router"), ("gather", "gather"), ("combine", "combine")):
+        if name.startswith(prefix):
+            return cls
+    return None
+
+
+def src_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "mixture_experts_layer_24_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/<kernel>__<workload>__pmc.txt if its
+    recorded source hash matches the current kernels, else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__pmc.txt")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m = re.search(r"source_hash:\s*(\w+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != src_hash():
+        return None
+    return float(b.group(1))
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, inp, target_s):
+    import numpy as np
+    import torch
+
+    import oracle
+    t0 = time.perf_counter()
+    x = inp["x"].cpu()
+    b = None if inp["b_router"] is None else inp["b_router"].cpu()
+    r = oracle.route(x, inp["w_router"].cpu(), wl.k, bias=b, normalize=wl.normalize_topk)
+    oracle.aux_loss(r["ids"], r["probs"], wl.aux_alpha)
+    C = oracle.capacity(wl.T, wl.E, wl.k, wl.capacity_factor)
+    dsp = oracle.dispatch(r["ids"], wl.E, C)
+    t_route = time.perf_counter() - t0
+
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(wl.T)
+    w_cache = {}
+
+    def ffn_tokens(toks):
+        """expert FFN + dense MLP + combine for the given tokens; returns seconds"""
+        need = {}
+        for t in toks:
+            for j in range(wl.k):
+                if dsp["slots"][t, j] >= 0:
+                    need.setdefault(int(r["ids"][t, j]), []).append(int(t))
+        # weights are copied to host outside the timed part
+        for e in need:
+            if e not in w_cache:
+                s1 = None if inp["w1_scale"] is None else inp["w1_scale"][e].cpu()
+                s2 = None if inp["w2_scale"] is None else inp["w2_scale"][e].cpu()
+                w_cache[e] = (inp["w1"][e].cpu(), inp["w2"][e].cpu(), s1, s2)
+        dense_w = (inp["wm1"].cpu(), inp["wm2"].cpu()) if wl.pr_moe else None
+        t1 = time.perf_counter()
+        for e, ts in need.items():
+            w1, w2, s1, s2 = w_cache[e]
+            oracle.ffn_rows(x[ts], w1, w2, s1, s2)
+        if dense_w is not None:
+            oracle.ffn_rows(x[list(toks)], *dense_w)
+        return time.perf_counter() - t1
+
+    probe = order[:16]
+    t_probe = max(ffn_tokens(probe), 1e-3)
+    n = int(min(wl.T, max(16, (target_s - t_route) / t_probe * len(probe))))
+    sample = order[:n]
+    t_ffn = ffn_tokens(sample)
+    t_total = t_route + t_ffn * (wl.T / n)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": wl.T / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"fp64 oracle: routing, aux loss and dispatch on all {wl.T} tokens "
+                   f"({t_route:.2f} s); expert FFN{' + dense MLP' if wl.pr_moe else ''} "
+                   f"on a seeded sample of {n} tokens ({t_ffn:.2f} s), extrapolated "
+                   f"linearly to {wl.T} tokens"),
+    }
+
+
+# ------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_24_amd import binding, synth, workloads
+
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = synth.make_inputs(wl, seed=args.seed, device=dev)
+    cfg = binding.config_of(wl)
+    C = binding.capacity(cfg)
+    out = binding.alloc_outputs(cfg, dev)
+    ws = binding.alloc_workspace(cfg, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.moe_layer_forward(cfg, inp["x"], inp, out, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    # timed region: host clock around K device-synchronised steps; the library
+    # records a HIP event pair around every kernel on the launch stream
+    binding.profile_reset()
+    binding.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.profile_enable(False)
+    prof = binding.profile_read()
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.3f})",
+          file=sys.stderr, flush=True)
+
+    kept = out.kept.cpu().tolist()
+    work = kernel_work(wl, kept, C)
+    kern = {}
+    for n, (cnt, tot) in prof.items():
+        kern[n] = {"launches": cnt, "avg_ms": tot / cnt, "ms_per_step": tot / args.steps,
+                   "class": classify(n)}
+    dom_name = max(kern, key=lambda n: kern[n]["ms_per_step"])
+    dom = kern[dom_name]
+    cls = dom["class"]
+    wk = work.get(cls, {"bytes": 0.0, "flops": 0.0})
+    avg_s = dom["avg_ms"] / 1e3
+    ai = wk["flops"] / max(wk["bytes"], 1.0)
+    mfma_bound = wl.act == "bf16" and ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = wk["flops"] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = wk["bytes"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = committed_traffic(dom_name, name)
+    roof["kernel"] = dom_name
+    roof["kernel_class"] = cls
+    roof["avg_launch_ms"] = round(dom["avg_ms"], 4)
+    roof["algorithmic_bytes"] = wk["bytes"]
+    roof["algorithmic_flops"] = wk["flops"]
+
+    res = {
+        "metric": METRIC, "value": round(wl.T * args.steps / elapsed, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.act == "bf16" else "f32",
+        "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02^2), bf16 RNE)",
+        "config": {"workload": name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k,
+                   "d_ff": wl.d_ff, "d_ff_dense": wl.d_ff_dense, "capacity": C,
+                   "capacity_factor": wl.capacity_factor, "expert_weights": wl.wfmt,
+                   "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
+                   "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
+        "roofline": roof,
+        "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
+                        k["launches"] // args.steps, "class": k["class"]}
+                    for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

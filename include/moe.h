@@ -32,8 +32,9 @@
  *     is launched and no output is written.  Return 0 (MOE_OK) or a negative
  *     MOE_ERR_* code; moe_status_string() names it.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
- *   - The library keeps no state between calls; calls on different streams
- *     with disjoint buffers may run concurrently.
+ *   - Apart from the optional timing records (moe_profile_*), the library
+ *     keeps no state between calls; calls on different streams with disjoint
+ *     buffers may run concurrently.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <set>
+#include <string>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -69,13 +72,14 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 
 // ---- workspace layout
 struct Layout {
-  size_t qsum, fcount, hist, offs, x_disp, y_disp, hidden, dense, total;
+  size_t qsum, fcount, hist, offs, term, x_disp, y_disp, hidden, dense, total;
 };
 
 Layout layout(const moe_config *c, int entry) {
   Layout L{};
   const int64_t nblk = moe_host::router_blocks(c->T);
   const size_t blkE = align256((size_t)nblk * (size_t)c->E * 4);
+  const size_t termE = (size_t)c->E * sizeof(double);
   const int64_t C = capacity_of(c);
   const size_t as = act_size(c);
   size_t o = 0;
@@ -88,6 +92,7 @@ Layout layout(const moe_config *c, int entry) {
     case MOE_ENTRY_ROUTE:
       L.qsum = take(blkE);
       L.fcount = take(blkE);
+      L.term = take(termE);
       break;
     case MOE_ENTRY_DISPATCH:
       L.hist = take(blkE);
@@ -103,6 +108,7 @@ Layout layout(const moe_config *c, int entry) {
       L.fcount = take(blkE);
       L.hist = take(blkE);
       L.offs = take(blkE);
+      L.term = take(termE);
       L.x_disp = take((size_t)c->E * C * c->d * as);
       L.y_disp = take((size_t)c->E * C * c->d * as);
       size_t hid = (size_t)c->E * C * c->d_ff * as;
@@ -133,9 +139,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 char *at(void *ws, size_t off) { return (char *)ws + off; }
 
 // ---- launch sequences (arguments already validated)
-hipError_t do_route(const moe_config *c, const void *x, const void *wr, const float *br,
-                    int32_t *ids, float *gates, float *logits, float *aux, float *qsum,
-                    int32_t *fcount, int32_t *hist, hipStream_t s) {
+hipError_t do_router(const moe_config *c, const void *x, const void *wr, const float *br,
+                     int32_t *ids, float *gates, float *logits, float *qsum, int32_t *fcount,
+                     int32_t *hist, hipStream_t s) {
   RouterArgs a{};
   a.x = x;
   a.w = wr;
@@ -151,20 +157,18 @@ hipError_t do_route(const moe_config *c, const void *x, const void *wr, const fl
   a.E = (int)c->E;
   a.k = (int)c->k;
   a.normalize = c->normalize_topk;
-  hipError_t e = moe_host::launch_router(a, c->act_dtype == MOE_BF16, s);
-  if (e != hipSuccess) return e;
-  return moe_host::launch_aux_final(qsum, fcount, moe_host::router_blocks(c->T), (int)c->E, c->T,
-                                    c->aux_alpha, aux, s);
+  return moe_host::launch_router(a, c->act_dtype == MOE_BF16, s);
 }
 
+// place slots in token order and gather the kept rows; hist/offs are the
+// per-block counts and offsets ([E][blocks]); aux_term non-null -> the place
+// kernel also finishes the aux loss
 hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *ids,
-                           const int32_t *hist, int32_t *offs, int32_t *slots, uint8_t *drop,
-                           int32_t *load, int32_t *kept, void *x_disp, hipStream_t s) {
+                           const int32_t *offs, int32_t *slots, uint8_t *drop,
+                           const double *aux_term, float *aux, void *x_disp, hipStream_t s) {
   const int64_t C = capacity_of(c);
-  const int nblk = moe_host::router_blocks(c->T);
-  hipError_t e = moe_host::launch_dispatch_scan(hist, nblk, (int)c->E, C, offs, load, kept, s);
-  if (e != hipSuccess) return e;
-  e = moe_host::launch_dispatch_place(ids, offs, c->T, (int)c->E, (int)c->k, C, slots, drop, s);
+  hipError_t e = moe_host::launch_dispatch_place(ids, offs, c->T, (int)c->E, (int)c->k, C, slots,
+                                                 drop, aux_term, c->aux_alpha, aux, s);
   if (e != hipSuccess) return e;
   return moe_host::launch_gather(x, ids, slots, c->T, (int)c->k, C,
                                  c->d * (int64_t)act_size(c), x_disp, s);
@@ -177,10 +181,10 @@ hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t 
   if (C == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
   GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E};
-  hipError_t e = moe_host::launch_gemm(g1, bf, q8, 1, s);
+  hipError_t e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
   if (e != hipSuccess) return e;
   GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E};
-  return moe_host::launch_gemm(g2, bf, q8, 0, s);
+  return moe_host::launch_gemm(g2, bf, q8, 0, "expert_ffn2", s);
 }
 
 hipError_t do_dense(const moe_config *c, const void *x, const void *wm1, const void *wm2,
@@ -188,10 +192,10 @@ hipError_t do_dense(const moe_config *c, const void *x, const void *wm1, const v
   if (c->T == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16;
   GemmArgs g1{x, wm1, nullptr, hidden, nullptr, c->T, (int)c->d_ff_dense, (int)c->d, 1};
-  hipError_t e = moe_host::launch_gemm(g1, bf, 0, 1, s);
+  hipError_t e = moe_host::launch_gemm(g1, bf, 0, 1, "dense_mlp1", s);
   if (e != hipSuccess) return e;
   GemmArgs g2{hidden, wm2, nullptr, out, nullptr, c->T, (int)c->d, (int)c->d_ff_dense, 1};
-  return moe_host::launch_gemm(g2, bf, 0, 0, s);
+  return moe_host::launch_gemm(g2, bf, 0, 0, "dense_mlp2", s);
 }
 
 // ---- profiling records
@@ -217,6 +221,13 @@ hipEvent_t pool_event() {
 }  // namespace
 
 namespace moe_host {
+const char *intern_name(const char *a, const char *b) {
+  static std::mutex mu;
+  static std::set<std::string> names;  // host-side, grows with distinct names only
+  std::lock_guard<std::mutex> lock(mu);
+  return names.insert(std::string(a) + ":" + b).first->c_str();
+}
+
 void prof_begin(hipStream_t s, const char *name) {
   if (!g_prof) return;
   ProfRec r{name, pool_event(), pool_event()};
@@ -256,9 +267,17 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   rc = check_ws(cfg, MOE_ENTRY_ROUTE, ws, ws_bytes);
   if (rc != MOE_OK) return rc;
   const Layout L = layout(cfg, MOE_ENTRY_ROUTE);
-  return hip_status(do_route(cfg, x, w_router, b_router, expert_ids, gates, logits, aux_loss,
-                             (float *)at(ws, L.qsum), (int32_t *)at(ws, L.fcount), nullptr,
-                             (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  float *qsum = (float *)at(ws, L.qsum);
+  int32_t *fcount = (int32_t *)at(ws, L.fcount);
+  double *term = (double *)at(ws, L.term);
+  hipError_t e = do_router(cfg, x, w_router, b_router, expert_ids, gates, logits, qsum, fcount,
+                           nullptr, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_scan_aux(nullptr, qsum, fcount, moe_host::router_blocks(T),
+                                  (int)cfg->E, T, 0, nullptr, nullptr, nullptr, term, s);
+  if (e == hipSuccess) e = moe_host::launch_aux_sum(term, (int)cfg->E, cfg->aux_alpha, aux_loss, s);
+  return hip_status(e);
 }
 
 int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids, int32_t *slots,
@@ -277,7 +296,10 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids
   int32_t *hist = (int32_t *)at(ws, L.hist), *offs = (int32_t *)at(ws, L.offs);
   hipError_t e = moe_host::launch_dispatch_count(expert_ids, T, (int)cfg->E, (int)cfg->k, hist, s);
   if (e == hipSuccess)
-    e = do_place_gather(cfg, x, expert_ids, hist, offs, slots, drop_mask, load, kept, x_disp, s);
+    e = moe_host::launch_scan_aux(hist, nullptr, nullptr, moe_host::router_blocks(T), (int)cfg->E,
+                                  T, C, offs, load, kept, nullptr, s);
+  if (e == hipSuccess)
+    e = do_place_gather(cfg, x, expert_ids, offs, slots, drop_mask, nullptr, nullptr, x_disp, s);
   return hip_status(e);
 }
 
@@ -362,11 +384,15 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   void *dense = nullptr;
   if (cfg->pr_moe) dense = out->dense_out ? out->dense_out : at(ws, L.dense);
 
-  hipError_t e = do_route(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates,
-                          out->logits, out->aux_loss, qsum, fcount, hist, s);
+  double *term = (double *)at(ws, L.term);
+  hipError_t e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates,
+                           out->logits, qsum, fcount, hist, s);
   if (e == hipSuccess)
-    e = do_place_gather(cfg, x, out->expert_ids, hist, offs, out->slots, out->drop_mask,
-                        out->load, out->kept, x_disp, s);
+    e = moe_host::launch_scan_aux(hist, qsum, fcount, moe_host::router_blocks(T), (int)cfg->E, T,
+                                  capacity_of(cfg), offs, out->load, out->kept, term, s);
+  if (e == hipSuccess)
+    e = do_place_gather(cfg, x, out->expert_ids, offs, out->slots, out->drop_mask, term,
+                        out->aux_loss, x_disp, s);
   if (e == hipSuccess && cfg->pr_moe) e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden, s);
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,

@@ -73,12 +73,35 @@ struct ActTraits<bf16> {
 
 // Blocks are spread over the 8 XCDs round-robin by hardware: block b runs on
 // XCD b % 8.  Remap so each XCD receives a contiguous range of logical tiles
-// (tiles of one expert then share that XCD's L2).  Bijective on [0, n).
+// (neighbouring tiles then share that XCD's L2).  Bijective on [0, n).
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   constexpr int X = 8;
   const int per = n / X, rem = n % X;
   const int x = b % X, i = b / X;
   return x * per + (x < rem ? x : rem) + i;
+}
+
+// Grouped variant for G groups of `per_group` tiles with G % 8 == 0: XCD x
+// takes groups x, x+8, x+16, ... and runs each group's tiles back to back, so
+// one expert's tiles share an L2 while skewed per-expert work is dealt evenly
+// over the XCDs.  Returns the logical tile g * per_group + r.  Bijective.
+__device__ __forceinline__ int xcd_remap_grouped(int b, int G, int per_group) {
+  constexpr int X = 8;
+  const int x = b % X, i = b / X;
+  const int lg = i / per_group, r = i - lg * per_group;
+  return (lg * X + x) * per_group + r;
+}
+
+// Switch load-balance loss, final step: aux = alpha * E * sum_e term[e],
+// summed by one wave in a fixed order (every lane ends with the same sum).
+__device__ __forceinline__ void aux_sum_wave(const double *term, int E, float alpha,
+                                             float *aux) {
+  const int lane = lane_id();
+  double v = 0.0;
+  for (int e = lane; e < E; e += kWave) v += term[e];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  if (lane == 0) aux[0] = (float)((double)alpha * (double)E * v);
 }
 
 }  // namespace moe

@@ -13,8 +13,9 @@
 // that come before it in token order; it is kept iff slot < C.  Computed
 // deterministically without order-dependent atomics:
 //   count : per 64-token block, an integer histogram over experts
-//   scan  : exclusive prefix over blocks, per expert -> block offsets,
-//           load[e] = total, kept[e] = min(load[e], C)
+//   scan  : one block per expert: exclusive prefix over the token blocks ->
+//           block offsets, load[e] = total, kept[e] = min(load[e], C) (the
+//           per-block counts are stored expert-major so this read is contiguous)
 //   place : one wave per block walks its 64*k assignments in order in chunks
 //           of 64; within a chunk, lanes with equal expert ids are grouped
 //           with ballots, ranked by lane order (popcount of the lower lanes),
@@ -45,23 +46,67 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t *ids,
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (tid < E) hist[(int64_t)blk * E + tid] = cnt[tid];
+  if (tid < E) hist[(int64_t)tid * gridDim.x + blk] = cnt[tid];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t *hist, int nblk, int E,
-                                                            int64_t C, int32_t *offs,
-                                                            int32_t *load, int32_t *kept) {
-  const int e = threadIdx.x;
-  if (e >= E) return;
-  int run = 0;
-  for (int b = 0; b < nblk; b++) {
-    const int64_t o = (int64_t)b * E + e;
-    const int h = hist[o];
-    offs[o] = run;
-    run += h;
+// One block per expert e: exclusive prefix of hist[e][*] over the token
+// blocks (each thread scans a contiguous chunk, chunk totals are scanned
+// across the block), load[e], kept[e]; with router partials also the
+// expert's aux-loss term f_e * Q_e, summed in a fixed order in fp64.
+__global__ __launch_bounds__(256) void scan_aux_kernel(const int32_t *hist, const float *qsum,
+                                                       const int32_t *fcount, int nblk, int E,
+                                                       int64_t T, int64_t C, int32_t *offs,
+                                                       int32_t *load, int32_t *kept,
+                                                       double *term) {
+  __shared__ int wsum[4];
+  __shared__ double red[2][256];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int chunk = (nblk + 255) / 256;
+  const int b0 = tid * chunk;
+  const int b1 = min(b0 + chunk, nblk);
+  const int64_t base = (int64_t)e * nblk;
+  if (hist) {
+    int tot = 0;
+    for (int b = b0; b < b1; b++) tot += hist[base + b];
+    // inclusive scan of chunk totals within the wave, then across waves
+    int inc = tot;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += v;
+    }
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    int run = inc - tot;
+    for (int w = 0; w < wave; w++) run += wsum[w];
+    for (int b = b0; b < b1; b++) {
+      const int h = hist[base + b];
+      offs[base + b] = run;
+      run += h;
+    }
+    if (tid == 255) {
+      load[e] = run;
+      kept[e] = (int64_t)run < C ? run : (int32_t)C;
+    }
   }
-  load[e] = run;
-  kept[e] = (int64_t)run < C ? run : (int32_t)C;
+  if (qsum) {
+    double q = 0.0, f = 0.0;
+    for (int b = b0; b < b1; b++) {
+      q += (double)qsum[base + b];
+      f += (double)fcount[base + b];
+    }
+    red[0][tid] = q;
+    red[1][tid] = f;
+    __syncthreads();
+    for (int st = 128; st >= 1; st >>= 1) {
+      if (tid < st) {
+        red[0][tid] += red[0][tid + st];
+        red[1][tid] += red[1][tid + st];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) term[e] = T > 0 ? (red[1][0] / (double)T) * (red[0][0] / (double)T) : 0.0;
+  }
 }
 
 __device__ __forceinline__ int sel4(int v0, int v1, int v2, int v3, int i) {
@@ -70,16 +115,19 @@ __device__ __forceinline__ int sel4(int v0, int v1, int v2, int v3, int i) {
 
 __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, const int32_t *offs,
                                                             int64_t T, int E, int k, int64_t C,
-                                                            int32_t *slots, uint8_t *drop) {
-  const int lane = lane_id(), blk = blockIdx.x;
+                                                            int32_t *slots, uint8_t *drop,
+                                                            const double *aux_term,
+                                                            float aux_alpha, float *aux) {
+  const int lane = lane_id(), blk = blockIdx.x, nblk = gridDim.x;
+  // the layer's aux loss is finished here, by block 0, when asked
+  if (aux && blk == 0) aux_sum_wave(aux_term, E, aux_alpha, aux);
   // running slot of expert e = lane + 64 i, starting at this block's offset
   int run0 = 0, run1 = 0, run2 = 0, run3 = 0;
   {
-    const int64_t o = (int64_t)blk * E;
-    if (lane < E) run0 = offs[o + lane];
-    if (lane + 64 < E) run1 = offs[o + lane + 64];
-    if (lane + 128 < E) run2 = offs[o + lane + 128];
-    if (lane + 192 < E) run3 = offs[o + lane + 192];
+    if (lane < E) run0 = offs[(int64_t)lane * nblk + blk];
+    if (lane + 64 < E) run1 = offs[(int64_t)(lane + 64) * nblk + blk];
+    if (lane + 128 < E) run2 = offs[(int64_t)(lane + 128) * nblk + blk];
+    if (lane + 192 < E) run3 = offs[(int64_t)(lane + 192) * nblk + blk];
   }
   const int64_t a0 = (int64_t)blk * DBT * k;
   int64_t a1 = a0 + (int64_t)DBT * k;
@@ -148,19 +196,23 @@ hipError_t launch_dispatch_count(const int32_t *ids, int64_t T, int E, int k, in
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_scan(const int32_t *hist, int nblk, int E, int64_t C, int32_t *offs,
-                                int32_t *load, int32_t *kept, hipStream_t s) {
-  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(256), 0, s, hist, nblk, E, C,
-             offs, load, kept);
+hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t *fcount,
+                           int nblk, int E, int64_t T, int64_t C, int32_t *offs, int32_t *load,
+                           int32_t *kept, double *term, hipStream_t s) {
+  MOE_LAUNCH("scan_aux", scan_aux_kernel, dim3(E), dim3(256), 0, s, hist, qsum, fcount, nblk, E,
+             T, C, offs, load, kept, term);
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
-                                 int64_t C, int32_t *slots, uint8_t *drop, hipStream_t s) {
+                                 int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
+                                 float aux_alpha, float *aux, hipStream_t s) {
   const int nblk = (int)((T + DBT - 1) / DBT);
   if (nblk > 0)
     MOE_LAUNCH("dispatch_place", dispatch_place_kernel, dim3(nblk), dim3(64), 0, s, ids, offs, T,
-               E, k, C, slots, drop);
+               E, k, C, slots, drop, aux_term, aux_alpha, aux);
+  else if (aux)
+    return launch_aux_sum(aux_term, E, aux_alpha, aux, s);
   return hipGetLastError();
 }
 

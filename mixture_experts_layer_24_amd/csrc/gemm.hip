@@ -22,8 +22,10 @@
 // are clamped to the last valid row) nor written; blocks whose first row is
 // past rows[g] exit at once, so only kept rows cost MFMA time, and only
 // experts with at least one kept row stream their weights.
-// Blocks are mapped to tiles XCD by XCD (contiguous tile ranges per XCD), so
-// the N-tiles of one expert share that XCD's L2 for their A rows.
+// Blocks are mapped to tiles XCD by XCD: with a multiple of 8 groups, XCD x
+// takes experts x, x+8, ... (skewed loads spread evenly) and runs each
+// expert's tiles back to back so they share its L2 for their A rows;
+// otherwise each XCD takes a contiguous range of tiles.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +57,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
   const int tiles_n = a.N / BN;
   const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
   const int total = a.G * tiles_m * tiles_n;
-  const int tile = xcd_remap(blockIdx.x, total);
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
+                                  : xcd_remap(blockIdx.x, total);
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
   const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
@@ -264,10 +267,11 @@ using namespace moe;
 
 template <int BM, int BN, int WM, int WN, int MF>
 static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_t s,
-                             const char *name) {
+                             const char *role, const char *tile) {
   const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
+  const char *name = intern_name(role, tile);
   if (b_int8) {
     if (gelu)
       MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, true, true>), grid, block, 0, s, a);
@@ -283,31 +287,27 @@ static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_
 }
 
 // Tile choice by rows per group (the capacity, or T for the dense MLP) and N.
-hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, const char *role,
+                       hipStream_t s) {
   if (a.G <= 0 || a.M_cap <= 0 || a.N <= 0) return hipGetLastError();
   if (!act_bf16) {
     const int tiles = a.G * (int)((a.M_cap + 63) / 64) * ((a.N + 63) / 64);
+    const char *name = intern_name(role, "f32");
     if (gelu)
-      MOE_LAUNCH("gemm_f32_gelu", gemm_f32_kernel<true>, dim3(tiles), dim3(256), 0, s, a);
+      MOE_LAUNCH(name, gemm_f32_kernel<true>, dim3(tiles), dim3(256), 0, s, a);
     else
-      MOE_LAUNCH("gemm_f32", gemm_f32_kernel<false>, dim3(tiles), dim3(256), 0, s, a);
+      MOE_LAUNCH(name, gemm_f32_kernel<false>, dim3(tiles), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const bool g1 = gelu != 0;
   if (a.M_cap > 256 && a.N % 256 == 0)
-    return launch_cfg<256, 256, 2, 4, 32>(a, b_int8, gelu, s,
-                                          g1 ? "gemm_bm256_bn256_gelu" : "gemm_bm256_bn256");
+    return launch_cfg<256, 256, 2, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm256_bn256_i8" : "bm256_bn256");
   if (a.M_cap > 64 && a.N % 128 == 0)
-    return launch_cfg<128, 128, 2, 2, 32>(a, b_int8, gelu, s,
-                                          g1 ? "gemm_bm128_bn128_gelu" : "gemm_bm128_bn128");
+    return launch_cfg<128, 128, 2, 2, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm128_bn128_i8" : "bm128_bn128");
   if (a.M_cap > 32 && a.N % 128 == 0)
-    return launch_cfg<64, 128, 1, 4, 32>(a, b_int8, gelu, s,
-                                         g1 ? "gemm_bm64_bn128_gelu" : "gemm_bm64_bn128");
+    return launch_cfg<64, 128, 1, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm64_bn128_i8" : "bm64_bn128");
   if (a.M_cap > 16 && a.N % 128 == 0)
-    return launch_cfg<32, 128, 1, 4, 32>(a, b_int8, gelu, s,
-                                         g1 ? "gemm_bm32_bn128_gelu" : "gemm_bm32_bn128");
-  return launch_cfg<16, 64, 1, 4, 16>(a, b_int8, gelu, s,
-                                      g1 ? "gemm_bm16_bn64_gelu" : "gemm_bm16_bn64");
+    return launch_cfg<32, 128, 1, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm32_bn128_i8" : "bm32_bn128");
+  return launch_cfg<16, 64, 1, 4, 16>(a, b_int8, gelu, s, role, b_int8 ? "bm16_bn64_i8" : "bm16_bn64");
 }
 
 }  // namespace moe_host

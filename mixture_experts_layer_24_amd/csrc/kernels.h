@@ -13,9 +13,9 @@ struct RouterArgs {
   int32_t *ids;       // [T, k]
   float *gates;       // [T, k]
   float *logits;      // [T, E] or null
-  float *qsum;        // [nblk, E] per-block sum of router probabilities
-  int32_t *fcount;    // [nblk, E] per-block count of first choices
-  int32_t *hist;      // [nblk, E] per-block count of all k assignments (or null)
+  float *qsum;        // [E, nblk] per-block sum of router probabilities
+  int32_t *fcount;    // [E, nblk] per-block count of first choices
+  int32_t *hist;      // [E, nblk] per-block count of all k assignments (or null)
   int64_t T;
   int d, E, k, normalize;
 };
@@ -38,22 +38,30 @@ namespace moe_host {
 
 int router_blocks(int64_t T);
 hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
-hipError_t launch_aux_final(const float *qsum, const int32_t *fcount, int nblk, int E,
-                            int64_t T, float alpha, float *aux, hipStream_t s);
+hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s);
 
 // dispatch (token blocks of the same size as the router's)
 hipError_t launch_dispatch_count(const int32_t *ids, int64_t T, int E, int k, int32_t *hist,
                                  hipStream_t s);
-hipError_t launch_dispatch_scan(const int32_t *hist, int nblk, int E, int64_t C, int32_t *offs,
-                                int32_t *load, int32_t *kept, hipStream_t s);
+// per-expert scan of the block histograms (hist may be null: aux only) and
+// the aux-loss term per expert (qsum null: no aux)
+hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t *fcount,
+                           int nblk, int E, int64_t T, int64_t C, int32_t *offs, int32_t *load,
+                           int32_t *kept, double *term, hipStream_t s);
+// slots in token order; block 0 also finishes the aux loss when aux != null
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
-                                 int64_t C, int32_t *slots, uint8_t *drop, hipStream_t s);
+                                 int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
+                                 float aux_alpha, float *aux, hipStream_t s);
 hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots, int64_t T, int k,
                          int64_t C, int64_t row_bytes, void *x_disp, hipStream_t s);
 
-// expert / dense GEMMs; gelu selects the GELU epilogue
+// expert / dense GEMMs; gelu selects the GELU epilogue; role names the launch
+// in the per-kernel timing ("expert_ffn1", "expert_ffn2", "dense_mlp1", ...)
 hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gelu,
-                       hipStream_t s);
+                       const char *role, hipStream_t s);
+
+// a stable C string for a profiling name built at run time
+const char *intern_name(const char *a, const char *b);
 
 hipError_t launch_combine(const void *y_disp, const int32_t *ids, const int32_t *slots,
                           const float *gates, const void *base, const void *base2, void *y,

@@ -1,5 +1,6 @@
 // router.hip -- fused router: logits = x W_r^T (+ b), softmax, top-k gate,
-// per-block load-balance statistics and per-block assignment histogram.
+// per-block load-balance statistics and per-block assignment histogram
+// (both stored expert-major, [E][blocks], for the per-expert scan).
 //
 // Method: "DeepSpeed MoE and Model Compression", section "DeepSpeed-MoE"
 // (p(x) = softmax(W_r x), TopK over p); "DeepSpeed-MoE vs Switch
@@ -10,8 +11,9 @@
 //
 // One block = 64 tokens x all experts (E <= 256, padded to a multiple of 32).
 // bf16: the 64 x Ep logit tile is a bf16 MFMA contraction (32x32x16, fp32
-// accumulate; the bf16 products are exact in fp32) over d in 64-wide K steps,
-// double-buffered through LDS.  fp32: plain fp32 FMA dot products.
+// accumulate; the bf16 products are exact in fp32) over d in 128- or 64-wide
+// K steps, double-buffered through LDS (rows padded by 16 bytes so the
+// 16-byte operand reads are free of bank conflicts).  fp32: plain fp32 FMA dot products.
 // The epilogue is shared: the tile goes to LDS, each wave takes 16 rows; a
 // row's E logits sit 1-4 per lane and wave shuffles give the row max, the
 // softmax sum and the arg-max rounds of the top-k.
@@ -20,9 +22,7 @@
 
 namespace moe {
 
-constexpr int RBM = 64;       // tokens per block
-constexpr int RBK = 64;       // K step (elements)
-constexpr int RLDA = RBK + 8; // LDS row stride in bf16 (144 B: conflict-free b128 reads)
+constexpr int RBM = 64;  // tokens per block
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -127,18 +127,25 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
   __syncthreads();
   const int e = threadIdx.x;
   if (e < E) {
-    const int64_t o = (int64_t)blk * E + e;
+    const int64_t o = (int64_t)e * gridDim.x + blk;  // expert-major [E][nblk]
     a.qsum[o] = ((qpart[0][e] + qpart[1][e]) + qpart[2][e]) + qpart[3][e];
     a.fcount[o] = fcnt[e];
     if (a.hist) a.hist[o] = hcnt[e];
   }
 }
 
-// NTW = 32-wide expert tiles per wave (Ep <= 64 * NTW)
-template <int NTW>
+// NTW = 32-wide expert tiles per wave (Ep <= 64 * NTW).  BK = K step (64,
+// or 128 when d allows it and the two stages fit LDS, i.e. Ep <= 128).
+template <int NTW, int BK>
 __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
   constexpr int EPMAX = 64 * NTW;
-  constexpr int STAGE = (RBM + EPMAX) * RLDA;  // bf16 elements per stage
+  static_assert(BK == 64 || (BK == 128 && NTW <= 2), "router tile does not fit LDS");
+  constexpr int LDA = BK + 8;                   // bf16 elements per LDS row
+  constexpr int CPR = BK / 8;                   // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;                // rows per load pass
+  constexpr int XP = RBM / RPP;                 // x passes
+  constexpr int WP = EPMAX / RPP;               // W passes (at most)
+  constexpr int STAGE = (RBM + EPMAX) * LDA;    // bf16 elements per stage
   constexpr int TILE_BYTES = 2 * STAGE * 2;
   constexpr int LOGIT_BYTES = RBM * (EPMAX + 4) * 4;
   constexpr int SMEM = TILE_BYTES > LOGIT_BYTES ? TILE_BYTES : LOGIT_BYTES;
@@ -149,29 +156,26 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int blk = blockIdx.x;
   const int E = a.E, Ep = (E + 31) & ~31, d = a.d;
-  for (int i = tid; i < 256; i += 256) {
-    fcnt[i] = 0;
-    hcnt[i] = 0;
-  }
+  fcnt[tid] = 0;
+  hcnt[tid] = 0;
   bf16 *As = (bf16 *)smem;
   const bf16 *X = (const bf16 *)a.x;
   const bf16 *W = (const bf16 *)a.w;
 
-  // global -> register prefetch: x tile 64 x 64 (2 chunks/thread),
-  // W tile Ep x 64 (Ep/32 chunks/thread, at most 2*NTW)
-  const int crow = tid >> 3, cchk = tid & 7;
-  u32x4 ra[2], rw[2 * NTW];
+  // global -> register prefetch of the next K step
+  const int crow = tid / CPR, cchk = tid % CPR;
+  u32x4 ra[XP], rw[WP];
   auto load_tiles = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      int64_t t = (int64_t)blk * RBM + p * 32 + crow;
+    for (int p = 0; p < XP; p++) {
+      int64_t t = (int64_t)blk * RBM + p * RPP + crow;
       if (t >= a.T) t = a.T - 1;
       ra[p] = *(const u32x4 *)(X + t * d + k0 + cchk * 8);
     }
 #pragma unroll
-    for (int p = 0; p < 2 * NTW; p++) {
-      int e = p * 32 + crow;
-      if (p * 32 < Ep) {
+    for (int p = 0; p < WP; p++) {
+      int e = p * RPP + crow;
+      if (p * RPP < Ep) {
         if (e >= E) e = E - 1;
         rw[p] = *(const u32x4 *)(W + (int64_t)e * d + k0 + cchk * 8);
       }
@@ -179,12 +183,12 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
   };
   auto store_tiles = [&](int st) __attribute__((always_inline)) {
     bf16 *sa = As + st * STAGE;
-    bf16 *sw = sa + RBM * RLDA;
+    bf16 *sw = sa + RBM * LDA;
 #pragma unroll
-    for (int p = 0; p < 2; p++) *(u32x4 *)(sa + (p * 32 + crow) * RLDA + cchk * 8) = ra[p];
+    for (int p = 0; p < XP; p++) *(u32x4 *)(sa + (p * RPP + crow) * LDA + cchk * 8) = ra[p];
 #pragma unroll
-    for (int p = 0; p < 2 * NTW; p++)
-      if (p * 32 < Ep) *(u32x4 *)(sw + (p * 32 + crow) * RLDA + cchk * 8) = rw[p];
+    for (int p = 0; p < WP; p++)
+      if (p * RPP < Ep) *(u32x4 *)(sw + (p * RPP + crow) * LDA + cchk * 8) = rw[p];
   };
 
   f32x16 acc[NTW];
@@ -194,24 +198,24 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
 
   const int mt = wave & 1;  // 32-row half of the token tile
-  const int ksteps = d / RBK;
+  const int ksteps = d / BK;
   load_tiles(0);
   store_tiles(0);
   __syncthreads();
   for (int kt = 0; kt < ksteps; kt++) {
     const int st = kt & 1;
-    if (kt + 1 < ksteps) load_tiles((kt + 1) * RBK);
+    if (kt + 1 < ksteps) load_tiles((kt + 1) * BK);
     const bf16 *sa = As + st * STAGE;
-    const bf16 *sw = sa + RBM * RLDA;
+    const bf16 *sw = sa + RBM * LDA;
 #pragma unroll
-    for (int s = 0; s < RBK / 16; s++) {
+    for (int s = 0; s < BK / 16; s++) {
       const int ch = 2 * s + (lane >> 5);
-      bf16x8 av = *(const bf16x8 *)(sa + (mt * 32 + (lane & 31)) * RLDA + ch * 8);
+      bf16x8 av = *(const bf16x8 *)(sa + (mt * 32 + (lane & 31)) * LDA + ch * 8);
 #pragma unroll
       for (int i = 0; i < NTW; i++) {
         const int nt = (wave >> 1) + 2 * i;
         if (nt * 32 < Ep) {
-          bf16x8 bv = *(const bf16x8 *)(sw + (nt * 32 + (lane & 31)) * RLDA + ch * 8);
+          bf16x8 bv = *(const bf16x8 *)(sw + (nt * 32 + (lane & 31)) * LDA + ch * 8);
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
         }
       }
@@ -265,26 +269,10 @@ __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
     router_epilogue<8>(a, L, ldl, qpart, fcnt, hcnt, blk);
 }
 
-// Switch load-balance loss from the per-block partials, in a fixed order:
-// loss = alpha * E * sum_e (F_e / T) (Q_e / T), sums in fp64.
-__global__ __launch_bounds__(256) void aux_final_kernel(const float *qsum, const int32_t *fcount,
-                                                        int nblk, int E, int64_t T, float alpha,
-                                                        float *aux) {
-  __shared__ double term[256];
-  const int e = threadIdx.x;
-  double qe = 0.0, fe = 0.0;
-  if (e < E)
-    for (int b = 0; b < nblk; b++) {
-      qe += (double)qsum[(int64_t)b * E + e];
-      fe += (double)fcount[(int64_t)b * E + e];
-    }
-  term[e] = (e < E && T > 0) ? (fe / (double)T) * (qe / (double)T) : 0.0;
-  __syncthreads();
-  for (int s = 128; s >= 1; s >>= 1) {
-    if (e < s) term[e] += term[e + s];
-    __syncthreads();
-  }
-  if (e == 0) aux[0] = (float)((double)alpha * (double)E * term[0]);
+// Switch load-balance loss, final step (moe_route): see aux_sum_wave.
+__global__ __launch_bounds__(64) void aux_sum_kernel(const double *term, int E, float alpha,
+                                                     float *aux) {
+  aux_sum_wave(term, E, alpha, aux);
 }
 
 }  // namespace moe
@@ -299,11 +287,19 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (nblk > 0) {
     if (act_bf16) {
       const int ntw = ((a.E + 31) / 32 + 1) / 2;
+      const bool k128 = a.d % 128 == 0;  // the bf16 path guarantees d % 64 == 0
+      const dim3 g(nblk), b(256);
       switch (ntw) {
-        case 1: MOE_LAUNCH("router_bf16_e64", router_bf16_kernel<1>, dim3(nblk), dim3(256), 0, s, a); break;
-        case 2: MOE_LAUNCH("router_bf16_e128", router_bf16_kernel<2>, dim3(nblk), dim3(256), 0, s, a); break;
-        case 3: MOE_LAUNCH("router_bf16_e192", router_bf16_kernel<3>, dim3(nblk), dim3(256), 0, s, a); break;
-        default: MOE_LAUNCH("router_bf16_e256", router_bf16_kernel<4>, dim3(nblk), dim3(256), 0, s, a); break;
+        case 1:
+          if (k128) MOE_LAUNCH("router_bf16_e64", (router_bf16_kernel<1, 128>), g, b, 0, s, a);
+          else MOE_LAUNCH("router_bf16_e64", (router_bf16_kernel<1, 64>), g, b, 0, s, a);
+          break;
+        case 2:
+          if (k128) MOE_LAUNCH("router_bf16_e128", (router_bf16_kernel<2, 128>), g, b, 0, s, a);
+          else MOE_LAUNCH("router_bf16_e128", (router_bf16_kernel<2, 64>), g, b, 0, s, a);
+          break;
+        case 3: MOE_LAUNCH("router_bf16_e192", (router_bf16_kernel<3, 64>), g, b, 0, s, a); break;
+        default: MOE_LAUNCH("router_bf16_e256", (router_bf16_kernel<4, 64>), g, b, 0, s, a); break;
       }
     } else {
       MOE_LAUNCH("router_f32", router_f32_kernel, dim3(nblk), dim3(256), 0, s, a);
@@ -312,10 +308,8 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_aux_final(const float *qsum, const int32_t *fcount, int nblk, int E, int64_t T,
-                            float alpha, float *aux, hipStream_t s) {
-  MOE_LAUNCH("aux_final", aux_final_kernel, dim3(1), dim3(256), 0, s, qsum, fcount, nblk, E, T,
-             alpha, aux);
+hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s) {
+  MOE_LAUNCH("aux_sum", aux_sum_kernel, dim3(1), dim3(64), 0, s, term, E, alpha, aux);
   return hipGetLastError();
 }
 
