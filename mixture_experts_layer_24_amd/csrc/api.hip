@@ -72,7 +72,7 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 
 // ---- workspace layout
 struct Layout {
-  size_t qsum, fcount, hist, offs, term, x_disp, y_disp, hidden, dense, total;
+  size_t qsum, fcount, hist, offs, term, x_disp, y_disp, hidden, hidden_dense, dense, total;
 };
 
 Layout layout(const moe_config *c, int entry) {
@@ -111,13 +111,11 @@ Layout layout(const moe_config *c, int entry) {
       L.term = take(termE);
       L.x_disp = take((size_t)c->E * C * c->d * as);
       L.y_disp = take((size_t)c->E * C * c->d * as);
-      size_t hid = (size_t)c->E * C * c->d_ff * as;
+      L.hidden = take((size_t)c->E * C * c->d_ff * as);
       if (c->pr_moe) {
-        const size_t hd = (size_t)c->T * c->d_ff_dense * as;
-        if (hd > hid) hid = hd;
+        L.hidden_dense = take((size_t)c->T * c->d_ff_dense * as);
         L.dense = take((size_t)c->T * c->d * as);
       }
-      L.hidden = take(hid);
       break;
     }
     default:
@@ -384,16 +382,18 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   void *dense = nullptr;
   if (cfg->pr_moe) dense = out->dense_out ? out->dense_out : at(ws, L.dense);
 
+  hipError_t e = hipSuccess;
+  if (cfg->pr_moe) e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), s);
   double *term = (double *)at(ws, L.term);
-  hipError_t e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates,
-                           out->logits, qsum, fcount, hist, s);
+  if (e == hipSuccess)
+    e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates, out->logits,
+                  qsum, fcount, hist, s);
   if (e == hipSuccess)
     e = moe_host::launch_scan_aux(hist, qsum, fcount, moe_host::router_blocks(T), (int)cfg->E, T,
                                   capacity_of(cfg), offs, out->load, out->kept, term, s);
   if (e == hipSuccess)
     e = do_place_gather(cfg, x, out->expert_ids, offs, out->slots, out->drop_mask, term,
                         out->aux_loss, x_disp, s);
-  if (e == hipSuccess && cfg->pr_moe) e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden, s);
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
                       hidden, s);

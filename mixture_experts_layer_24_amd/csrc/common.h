@@ -53,9 +53,27 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
 __device__ __forceinline__ float bf2f(bf16 b) { return (float)b; }
 __device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }  // RNE
 
-// exact (erf) GELU in fp32 using the device library's erff
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0 (odd extension), |error| <= 1.5e-7 -- far
+// below the bf16 rounding of the GELU output; about a third of the
+// instructions of the device library's erff on the GEMM epilogue.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  // exp(-x^2) = 2^(-x^2 * log2 e)
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
+}
+
+// GELU with the exact (erf) form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2))
 __device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752440f));
 }
 
 template <typename T>

@@ -12,10 +12,10 @@
 // B: weights [G][N][K] ([out, in], K contiguous), bf16 or int8 + fp16 scale
 //    per 128 K-elements of a row.  epi = GELU (first layer) or identity.
 //
-// bf16 path: a BM x BN block tile, 64-wide K steps double-buffered through
-// LDS (rows padded to 144 B so the 16-byte MFMA operand reads are free of
-// bank conflicts), register prefetch of the next K step while the MFMAs run
-// on the current one.  Each wave owns a WTM x WTN sub-tile of 32x32x16 (or
+// Register-staged kernel (int8 weights, and shapes the DMA kernel does not
+// tile): a BM x BN block tile, 64-wide K steps double-buffered through LDS
+// (rows padded to 144 B so the 16-byte MFMA operand reads are free of bank
+// conflicts), register prefetch of the next K step while the MFMAs run.  Each wave owns a WTM x WTN sub-tile of 32x32x16 (or
 // 16x16x32) bf16 MFMAs accumulating in fp32.  int8 weights are converted to
 // bf16 (s * q rounded once) on their way into LDS, so the MFMA loop is the
 // same as for bf16 weights.  Rows past rows[g] are neither read (their loads
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 
   u32x4 ra[A_PT], rb[B_PT];
   float rs[BINT8 ? B_PT : 1];
-  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+  auto load_tiles = [&](u32x4 (&ra)[A_PT], u32x4 (&rb)[B_PT], float (&rs)[BINT8 ? B_PT : 1],
+                        int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < A_PT; p++) {
       const int c = tid + p * NT;
@@ -105,7 +106,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
   };
-  auto store_tiles = [&](int st) __attribute__((always_inline)) {
+  auto store_tiles = [&](const u32x4 (&ra)[A_PT], const u32x4 (&rb)[B_PT],
+                         const float (&rs)[BINT8 ? B_PT : 1], int st) __attribute__((always_inline)) {
     bf16 *sa = smem + st * STAGE;
     bf16 *sb = sa + BM * LDK;
 #pragma unroll
@@ -146,12 +148,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 
   const int wm = wave / WN, wn = wave % WN;
   const int ksteps = K / BK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-  for (int kt = 0; kt < ksteps; kt++) {
-    const int st = kt & 1;
-    if (kt + 1 < ksteps) load_tiles((kt + 1) * BK);
+  // MFMAs on one LDS stage
+  auto compute = [&](int st) __attribute__((always_inline)) {
     const bf16 *sa = smem + st * STAGE + (wm * WTM) * LDK;
     const bf16 *sb = smem + st * STAGE + BM * LDK + (wn * WTN) * LDK;
 #pragma unroll
@@ -179,7 +177,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < ksteps) store_tiles(st ^ 1);
+  };
+  // one K step in flight: load kt+1 while computing kt
+  load_tiles(ra, rb, rs, 0);
+  store_tiles(ra, rb, rs, 0);
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; kt++) {
+    const int st = kt & 1;
+    if (kt + 1 < ksteps) load_tiles(ra, rb, rs, (kt + 1) * BK);
+    compute(st);
+    if (kt + 1 < ksteps) store_tiles(ra, rb, rs, st ^ 1);
     __syncthreads();
   }
 
@@ -206,6 +213,197 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
         if (GELU) v = gelu_f(v);
         if (m < rows) Cg[m * N + n] = (bf16)v;
       }
+}
+
+// ---------------------------------------------------------------------------
+// DMA-pipelined bf16 GEMM.  Both operands travel global -> LDS with gfx950's
+// global_load_lds_dwordx4 (each lane's 16 bytes land at M0 + 16 * lane), so no
+// registers stage the tiles and NS - 1 K steps can be in flight per block.
+// LDS tiles hold 64-wide K steps as 128-byte rows of eight 16-byte chunks;
+// chunk c of row R sits in slot c ^ f(R), f(R) = (R & 7) ^ ((R >> 3) & 1),
+// which keeps the 16-byte MFMA operand reads free of bank conflicts with 32
+// or 64 banks (any 8 aligned rows, and the 8 same-parity rows of any aligned
+// 16, hit distinct slots).  The DMA lane -> (row, slot) placement is fixed,
+// so each lane fetches the global chunk that belongs in its slot.
+// The DMA loads are issued from inline assembly (they have no register
+// results); their completion is awaited with explicit vmcnt waits before the
+// barrier that publishes a stage, because the compiler would otherwise wait
+// for every outstanding load before each LDS read.
+__device__ __forceinline__ int swz_slot(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+
+// NT: non-temporal (streamed once, e.g. expert weights: ~7.0 vs ~6.2 TB/s
+// for plain streaming reads on MI355X).  The compiler treats m0 as reserved
+// and ignores the clobber; that is safe here because compiler-generated code
+// in these kernels never uses m0 (tests/test_isa_cpu.py checks the ISA).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) with the other counters left open (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// NTB: load the weight operand non-temporally (read once)
+template <int BM, int BN, int WM, int WN, int NS, bool NTB, bool GELU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
+  constexpr int W = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int ROWB = 128;                       // bytes per tile row (64 bf16)
+  constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
+  constexpr int NCH = (BM + BN) / 8;              // 1 KB DMA chunks per stage
+  constexpr int CPW = NCH / W;                    // chunks per wave per stage
+  static_assert(NCH % W == 0 && TM >= 1 && TN >= 1, "tile");
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (SGPR)
+  const int tiles_n = a.N / BN;
+  const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
+  const int total = a.G * tiles_m * tiles_n;
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
+                                  : xcd_remap(blockIdx.x, total);
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int64_t rows = a.M_cap;
+  if (a.rows) {
+    const int64_t r = a.rows[g];
+    rows = r < rows ? r : rows;
+  }
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= rows) return;
+  const int n0 = tn * BN;
+  const int K = a.K, N = a.N;
+  // per-tile operand bases: every per-lane offset below is < 2^32 bytes
+  const char *Abase = (const char *)a.A + ((int64_t)g * a.M_cap + m0) * K * 2;
+  const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K * 2;
+  bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+
+  // this lane's source offset for each of its wave's chunks (K step 0)
+  uint32_t voff[CPW];
+  const int lr = lane >> 3, slot = lane & 7;
+#pragma unroll
+  for (int i = 0; i < CPW; i++) {
+    const int q = wave * CPW + i;
+    if (q < BM / 8) {
+      const int R = 8 * q + lr;
+      int64_t m = R;
+      if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
+      voff[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot(R)) << 4));
+    } else {
+      const int R = 8 * (q - BM / 8) + lr;
+      voff[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot(R)) << 4));
+    }
+  }
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPW; i++) {
+      const int q = wave * CPW + i;  // wave-uniform
+      const uint32_t dst = lds0 + st * STAGE + q * 1024;
+      if (q < BM / 8)
+        dma16<false>(Abase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
+      else
+        dma16<NTB>(Bbase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int ksteps = K / 64;
+#pragma unroll
+  for (int p = 0; p < NS - 1; p++)
+    if (p < ksteps) issue(p, p);
+  for (int kt = 0; kt < ksteps; kt++) {
+    // this wave's chunks of step kt have landed once at most the later
+    // steps' chunks are outstanding; the barrier publishes every wave's
+    if (kt + NS - 2 < ksteps)
+      wait_vmcnt<(NS - 2) * CPW>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
+    const char *sa = smem + (kt % NS) * STAGE;
+    const char *sb = sa + BM * ROWB;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const int c = 2 * s + (lane >> 5);
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int R = wm * WTM + i * 32 + (lane & 31);
+        af[i] = *(const bf16x8 *)(sa + R * ROWB + ((c ^ swz_slot(R)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const int R = wn * WTN + j * 32 + (lane & 31);
+        bfr[j] = *(const bf16x8 *)(sb + R * ROWB + ((c ^ swz_slot(R)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: the tile goes through LDS (bf16, rows padded by 16 bytes) so
+  // the output is written with coalesced 16-byte stores, one row band of
+  // WTM rows (the waves with the same wm) at a time.  32x32 MFMA layout:
+  // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
+  static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
+  constexpr int CPR = BN / 8;        // 16-byte chunks per output row
+  for (int band = 0; band < WM; band++) {
+    __syncthreads();  // stage buffers (or the previous band) no longer read
+    if (wm == band) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int Cc = wn * WTN + j * 32 + (lane & 31);
+            float v = acc[i][j][r];
+            if (GELU) v = gelu_f(v);
+            *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
+          }
+    }
+    __syncthreads();
+    const int64_t r0 = m0 + band * WTM;
+    const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
+    for (int idx = tid; idx < WTM * CPR; idx += 64 * W) {
+      const int R = idx / CPR, ch = idx - R * CPR;
+      if (R < mrows)
+        *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+    }
+  }
 }
 
 // fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
@@ -286,7 +484,30 @@ static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_
   return hipGetLastError();
 }
 
-// Tile choice by rows per group (the capacity, or T for the dense MLP) and N.
+template <int BM, int BN, int WM, int WN, int NS>
+static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t s,
+                             const char *role, const char *tile) {
+  const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
+  if (tiles <= 0) return hipGetLastError();
+  const dim3 grid(tiles), block(64 * WM * WN);
+  const char *name = intern_name(role, tile);
+  if (nt_b) {
+    if (gelu)
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, true, true>), grid, block, 0, s, a);
+    else
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, true, false>), grid, block, 0, s, a);
+  } else {
+    if (gelu)
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, false, true>), grid, block, 0, s, a);
+    else
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// Tile choice (measured on MI355X at the workload shapes) by rows per group
+// (the capacity, or T for the dense MLP), N, and whether the weights are
+// streamed once (expert GEMMs: non-temporal weight loads).
 hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, const char *role,
                        hipStream_t s) {
   if (a.G <= 0 || a.M_cap <= 0 || a.N <= 0) return hipGetLastError();
@@ -299,15 +520,25 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
       MOE_LAUNCH(name, gemm_f32_kernel<false>, dim3(tiles), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (a.M_cap > 256 && a.N % 256 == 0)
-    return launch_cfg<256, 256, 2, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm256_bn256_i8" : "bm256_bn256");
-  if (a.M_cap > 64 && a.N % 128 == 0)
-    return launch_cfg<128, 128, 2, 2, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm128_bn128_i8" : "bm128_bn128");
-  if (a.M_cap > 32 && a.N % 128 == 0)
-    return launch_cfg<64, 128, 1, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm64_bn128_i8" : "bm64_bn128");
-  if (a.M_cap > 16 && a.N % 128 == 0)
-    return launch_cfg<32, 128, 1, 4, 32>(a, b_int8, gelu, s, role, b_int8 ? "bm32_bn128_i8" : "bm32_bn128");
-  return launch_cfg<16, 64, 1, 4, 16>(a, b_int8, gelu, s, role, b_int8 ? "bm16_bn64_i8" : "bm16_bn64");
+  const int nt = a.rows != nullptr;  // grouped expert GEMM: weights read once
+  if (b_int8) {  // int8 groups: N and K are multiples of 128 (validated)
+    if (a.M_cap <= 32) return launch_cfg<32, 128, 1, 4, 32>(a, 1, gelu, s, role, "bm32_bn128_i8");
+    if (a.M_cap <= 64) return launch_cfg<64, 128, 1, 4, 32>(a, 1, gelu, s, role, "bm64_bn128_i8");
+    if (a.M_cap <= 128 || a.N % 256)
+      return launch_cfg<128, 128, 2, 2, 32>(a, 1, gelu, s, role, "bm128_bn128_i8");
+    return launch_cfg<256, 256, 2, 4, 32>(a, 1, gelu, s, role, "bm256_bn256_i8");
+  }
+  if (a.N % 128 == 0) {
+    if (a.M_cap <= 32) return launch_dma<32, 128, 1, 4, 4>(a, nt, gelu, s, role, "dma32x128");
+    if (a.M_cap <= 64) return launch_dma<64, 128, 1, 4, 2>(a, nt, gelu, s, role, "dma64x128");
+    if (a.M_cap <= 128 && a.N % 256 == 0)
+      return launch_dma<128, 256, 2, 4, 3>(a, nt, gelu, s, role, "dma128x256");
+    if (a.M_cap > 128 && a.N % 256 == 0)
+      return launch_dma<256, 256, 2, 4, 2>(a, nt, gelu, s, role, "dma256x256");
+    return launch_dma<128, 128, 2, 2, 2>(a, nt, gelu, s, role, "dma128x128");
+  }
+  // any N that is a multiple of 64
+  return launch_cfg<16, 64, 1, 4, 16>(a, 0, gelu, s, role, "bm16_bn64");
 }
 
 }  // namespace moe_host

@@ -211,12 +211,17 @@ def test_dispatch_alone(T, E, k, C):
                 assert np.array_equal(xdn[ids[t, j], ref["slots"][t, j]], xn[t])
 
 
-FFN_CASES = [(10, 128, 256), (20, 128, 256), (50, 128, 256), (100, 256, 384), (300, 256, 512)]
+# (C, d, d_ff): weight-streaming tiles for C <= 32 / 64 / 128, 256x256 and
+# 128x128 block tiles above, the 16x64 tile when N is not a multiple of 128
+FFN_CASES = [(10, 128, 256), (20, 128, 256), (50, 128, 256), (100, 256, 384), (128, 128, 128),
+             (300, 256, 512), (200, 384, 384), (40, 192, 320)]
 
 
 @pytest.mark.parametrize("wfmt", ["plain", "int8"])
 @pytest.mark.parametrize("C,d,F", FFN_CASES)
 def test_expert_ffn_alone(C, d, F, wfmt):
+    if wfmt == "int8" and (d % 128 or F % 128):
+        pytest.skip("int8 groups need d and d_ff multiples of 128")
     E = 4
     wl = W("f", T=C, d=d, E=E, k=1, d_ff=F, capacity_factor=float(E), wfmt=wfmt)
     cfg = binding.config_of(wl)
