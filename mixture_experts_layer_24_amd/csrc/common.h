@@ -110,6 +110,20 @@ __device__ __forceinline__ int xcd_remap_grouped(int b, int G, int per_group) {
   return (lg * X + x) * per_group + r;
 }
 
+// Tile r of a group with tiles_m x tiles_n tiles, in grouped order: GM
+// row-tiles are swept column by column (r -> (tm, tn)), so the tiles that
+// run at the same time share both operand slabs in L2 instead of each reading
+// its own weight slab.  Bijective on [0, tiles_m * tiles_n).
+__device__ __forceinline__ void grouped_tile(int r, int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int GM = 8;
+  const int q = r / (GM * tiles_n);
+  const int tm0 = q * GM;
+  const int gm = tiles_m - tm0 < GM ? tiles_m - tm0 : GM;
+  const int local = r - tm0 * tiles_n;
+  tm = tm0 + local % gm;
+  tn = local / gm;
+}
+
 // Switch load-balance loss, final step: aux = alpha * E * sum_e term[e],
 // summed by one wave in a fixed order (every lane ends with the same sum).
 __device__ __forceinline__ void aux_sum_wave(const double *term, int E, float alpha,

@@ -61,7 +61,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
                                   : xcd_remap(blockIdx.x, total);
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
-  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t rows = a.M_cap;
   if (a.rows) {
     const int64_t r = a.rows[g];
@@ -219,17 +220,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 // DMA-pipelined bf16 GEMM.  Both operands travel global -> LDS with gfx950's
 // global_load_lds_dwordx4 (each lane's 16 bytes land at M0 + 16 * lane), so no
 // registers stage the tiles and NS - 1 K steps can be in flight per block.
-// LDS tiles hold 64-wide K steps as 128-byte rows of eight 16-byte chunks;
-// chunk c of row R sits in slot c ^ f(R), f(R) = (R & 7) ^ ((R >> 3) & 1),
-// which keeps the 16-byte MFMA operand reads free of bank conflicts with 32
-// or 64 banks (any 8 aligned rows, and the 8 same-parity rows of any aligned
-// 16, hit distinct slots).  The DMA lane -> (row, slot) placement is fixed,
-// so each lane fetches the global chunk that belongs in its slot.
+// LDS tiles hold BK-wide K steps as rows of BK/8 16-byte chunks (BK = 64:
+// 128-byte rows, or 32: 64-byte rows, which halves a stage so large tiles
+// can keep more steps in flight).  Chunk c of row R sits in slot c ^ f(R):
+//   BK = 64: f(R) = (R & 7) ^ ((R >> 3) & 1)
+//   BK = 32: f(R) = ((R >> 1) ^ (R >> 3)) & 3
+// which keeps the 16-byte MFMA operand reads (32 consecutive rows, one
+// logical chunk) free of bank conflicts with 32 banks (128 bytes per pass) or
+// 64 banks (256 bytes per pass).  The DMA lane -> (row, slot) placement is
+// fixed (16 bytes per lane, consecutive), so each lane fetches the global
+// chunk that belongs in its slot.
 // The DMA loads are issued from inline assembly (they have no register
 // results); their completion is awaited with explicit vmcnt waits before the
 // barrier that publishes a stage, because the compiler would otherwise wait
 // for every outstanding load before each LDS read.
-__device__ __forceinline__ int swz_slot(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+template <int BK>
+__device__ __forceinline__ int swz_slot(int R) {
+  if constexpr (BK == 64)
+    return (R & 7) ^ ((R >> 3) & 1);
+  else
+    return ((R >> 1) ^ (R >> 3)) & 3;
+}
 
 // NT: non-temporal (streamed once, e.g. expert weights: ~7.0 vs ~6.2 TB/s
 // for plain streaming reads on MI355X).  The compiler treats m0 as reserved
@@ -260,17 +271,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // NTB: load the weight operand non-temporally (read once)
-template <int BM, int BN, int WM, int WN, int NS, bool NTB, bool GELU>
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, bool GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
+  static_assert(BK == 64 || BK == 32, "K step");
   constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int ROWB = 128;                       // bytes per tile row (64 bf16)
+  constexpr int ROWB = BK * 2;                    // bytes per tile row
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int RPC = 1024 / ROWB;                // rows per 1 KB DMA chunk
   constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
-  constexpr int NCH = (BM + BN) / 8;              // 1 KB DMA chunks per stage
+  constexpr int NCH = (BM + BN) / RPC;            // 1 KB DMA chunks per stage
   constexpr int CPW = NCH / W;                    // chunks per wave per stage
-  static_assert(NCH % W == 0 && TM >= 1 && TN >= 1, "tile");
+  static_assert(NCH % W == 0 && BM % RPC == 0 && TM >= 1 && TN >= 1, "tile");
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert((NS - 2) * CPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = lane_id();
@@ -282,7 +297,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
                                   : xcd_remap(blockIdx.x, total);
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
-  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t rows = a.M_cap;
   if (a.rows) {
     const int64_t r = a.rows[g];
@@ -300,18 +316,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 
   // this lane's source offset for each of its wave's chunks (K step 0)
   uint32_t voff[CPW];
-  const int lr = lane >> 3, slot = lane & 7;
+  const int lr = lane / CPR, slot = lane % CPR;
 #pragma unroll
   for (int i = 0; i < CPW; i++) {
     const int q = wave * CPW + i;
-    if (q < BM / 8) {
-      const int R = 8 * q + lr;
+    if (q < BM / RPC) {
+      const int R = RPC * q + lr;
       int64_t m = R;
       if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
-      voff[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot(R)) << 4));
+      voff[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
     } else {
-      const int R = 8 * (q - BM / 8) + lr;
-      voff[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot(R)) << 4));
+      const int R = RPC * (q - BM / RPC) + lr;
+      voff[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
     }
   }
   auto issue = [&](int st, int kt) __attribute__((always_inline)) {
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
     for (int i = 0; i < CPW; i++) {
       const int q = wave * CPW + i;  // wave-uniform
       const uint32_t dst = lds0 + st * STAGE + q * 1024;
-      if (q < BM / 8)
+      if (q < BM / RPC)
         dma16<false>(Abase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
       else
         dma16<NTB>(Bbase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
   const int wm = wave / WN, wn = wave % WN;
-  const int ksteps = K / 64;
+  const int ksteps = K / BK;
 #pragma unroll
   for (int p = 0; p < NS - 1; p++)
     if (p < ksteps) issue(p, p);
@@ -351,18 +367,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
     const char *sa = smem + (kt % NS) * STAGE;
     const char *sb = sa + BM * ROWB;
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
+    for (int s = 0; s < BK / 16; s++) {
       const int c = 2 * s + (lane >> 5);
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; i++) {
         const int R = wm * WTM + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8 *)(sa + R * ROWB + ((c ^ swz_slot(R)) << 4));
+        af[i] = *(const bf16x8 *)(sa + R * ROWB + ((c ^ swz_slot<BK>(R)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < TN; j++) {
         const int R = wn * WTN + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8 *)(sb + R * ROWB + ((c ^ swz_slot(R)) << 4));
+        bfr[j] = *(const bf16x8 *)(sb + R * ROWB + ((c ^ swz_slot<BK>(R)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < TM; i++)
@@ -378,7 +394,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
-  constexpr int CPR = BN / 8;        // 16-byte chunks per output row
+  constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
   for (int band = 0; band < WM; band++) {
     __syncthreads();  // stage buffers (or the previous band) no longer read
     if (wm == band) {
@@ -398,8 +414,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
     __syncthreads();
     const int64_t r0 = m0 + band * WTM;
     const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
-    for (int idx = tid; idx < WTM * CPR; idx += 64 * W) {
-      const int R = idx / CPR, ch = idx - R * CPR;
+    for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
+      const int R = idx / OCPR, ch = idx - R * OCPR;
       if (R < mrows)
         *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
     }
@@ -417,7 +433,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   const int tile = blockIdx.x;
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
-  const int tm = rem / tiles_n, tn = rem - tm * tiles_n;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t rows = a.M_cap;
   if (a.rows) {
     const int64_t r = a.rows[g];
@@ -484,7 +501,7 @@ static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t s,
                              const char *role, const char *tile) {
   const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
@@ -493,14 +510,14 @@ static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t 
   const char *name = intern_name(role, tile);
   if (nt_b) {
     if (gelu)
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, true, true>), grid, block, 0, s, a);
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, true>), grid, block, 0, s, a);
     else
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, true, false>), grid, block, 0, s, a);
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, false>), grid, block, 0, s, a);
   } else {
     if (gelu)
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, false, true>), grid, block, 0, s, a);
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, true>), grid, block, 0, s, a);
     else
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, NS, false, false>), grid, block, 0, s, a);
+      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -529,13 +546,13 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
     return launch_cfg<256, 256, 2, 4, 32>(a, 1, gelu, s, role, "bm256_bn256_i8");
   }
   if (a.N % 128 == 0) {
-    if (a.M_cap <= 32) return launch_dma<32, 128, 1, 4, 4>(a, nt, gelu, s, role, "dma32x128");
-    if (a.M_cap <= 64) return launch_dma<64, 128, 1, 4, 2>(a, nt, gelu, s, role, "dma64x128");
+    if (a.M_cap <= 32) return launch_dma<32, 128, 1, 4, 64, 4>(a, nt, gelu, s, role, "dma32x128");
+    if (a.M_cap <= 64) return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");
     if (a.M_cap <= 128 && a.N % 256 == 0)
-      return launch_dma<128, 256, 2, 4, 3>(a, nt, gelu, s, role, "dma128x256");
+      return launch_dma<128, 256, 2, 4, 64, 3>(a, nt, gelu, s, role, "dma128x256");
     if (a.M_cap > 128 && a.N % 256 == 0)
-      return launch_dma<256, 256, 2, 4, 2>(a, nt, gelu, s, role, "dma256x256");
-    return launch_dma<128, 128, 2, 2, 2>(a, nt, gelu, s, role, "dma128x128");
+      return launch_dma<256, 256, 2, 4, 64, 2>(a, nt, gelu, s, role, "dma256x256");
+    return launch_dma<128, 128, 2, 2, 64, 2>(a, nt, gelu, s, role, "dma128x128");
   }
   // any N that is a multiple of 64
   return launch_cfg<16, 64, 1, 4, 16>(a, 0, gelu, s, role, "bm16_bn64");
