@@ -1,7 +1,9 @@
 """Benchmark: MoE-layer forward tokens/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--copy-calibration GIB]
+    python bench.py --pmc-summary FETCH.csv WRITE.csv --label L --symbol RE
+                    --workload NAME --copy-gib G --command "..."   (no GPU)
 
 A step is one moe_layer_forward (router + softmax/top-k + aux loss, dispatch,
 PR-MoE dense MLP, expert FFNs, combine) over one batch of seeded synthetic
@@ -21,6 +23,13 @@ with --workload.  One JSON line is printed:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
              (routing and dispatch on every token, expert FFN and dense MLP on a
              seeded token sample, extrapolated linearly in tokens)
+
+--copy-calibration G copies a G GiB device buffer three times before the
+warmup, so that a rocprofv3 --pmc run of the same command also counts a plain
+copy of known size.  --pmc-summary turns the counter_collection.csv files of
+a FETCH_SIZE run and a WRITE_SIZE run into profiles/<label>__<workload>__pmc.txt:
+HBM bytes per launch of the kernel whose symbol matches RE, scaled by
+(known copy bytes / counted copy bytes) of the calibration copy.
 """
 from __future__ import annotations
 
@@ -51,6 +60,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--label")
+    p.add_argument("--symbol")
+    p.add_argument("--copy-gib", type=float, default=1.0)
+    p.add_argument("--command", default="")
     return p.parse_args()
 
 
@@ -113,7 +128,7 @@ def src_hash():
 def committed_traffic(kernel: str, workload: str):
     """HBM bytes per launch from profiles/<kernel>__<workload>__pmc.txt if its
     recorded source hash matches the current kernels, else None."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__pmc.txt")
+    p = os.path.join(ROOT, "profiles", f"{kernel.replace(':', '_')}__{workload}__pmc.txt")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
@@ -182,8 +197,61 @@ def cpu_baseline(wl, inp, target_s):
 
 
 # ------------------------------------------------------------- main
+def pmc_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3
+    counter_collection.csv (counter values of one dispatch summed)."""
+    import csv
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            nm = r["Kernel_Name"]
+            v = float(r["Counter_Value"])
+            if key in per:
+                per[key] = (nm, per[key][1] + v)
+            else:
+                per[key] = (nm, v)
+    return list(per.values())
+
+
+def pmc_summary(args):
+    """Write profiles/<label>__<workload>__pmc.txt from a FETCH_SIZE and a
+    WRITE_SIZE counter run (values in KiB per dispatch)."""
+    known = args.copy_gib * (1 << 30)
+    out = {}
+    for ctr, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.pmc_summary):
+        rows = pmc_rows(path)
+        # the calibration copies: copy kernels whose count is within a factor of
+        # four of the known size (the other copies are input uploads of <= 64 MiB)
+        cal = [v * 1024.0 for n, v in rows if "copy" in n.lower() and v * 1024.0 > 0.25 * known]
+        if not cal:
+            raise SystemExit(f"{path}: no calibration copy of ~{known:.0f} bytes found")
+        factor = known / (sum(cal) / len(cal))
+        mine = [v * 1024.0 for n, v in rows if re.search(args.symbol, n)]
+        if not mine:
+            raise SystemExit(f"{path}: no dispatch of a kernel matching {args.symbol!r}")
+        raw = sum(mine) / len(mine)
+        out[ctr] = (raw, factor, len(mine), len(cal))
+    hbm = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][1] + out["WRITE_SIZE"][0] * out["WRITE_SIZE"][1]
+    lines = [f"# rocprofv3 HBM traffic -- kernel {args.label}, workload {args.workload}",
+             f"# command: {args.command}",
+             f"source_hash: {src_hash()}",
+             f"symbol_regex: {args.symbol}"]
+    for ctr, (raw, factor, n, ncal) in out.items():
+        lines.append(f"{ctr}: {raw:.6e} bytes per dispatch counted (mean of {n} dispatches); "
+                     f"calibration copy of {known:.0f} bytes counted {known / factor:.6e} "
+                     f"({ncal} copies) -> scale {factor:.4f}")
+    lines.append(f"hbm_bytes_per_launch: {hbm:.6e}")
+    dst = os.path.join(ROOT, "profiles",
+                       f"{args.label.replace(':', '_')}__{args.workload}__pmc.txt")
+    open(dst, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        return pmc_summary(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
@@ -205,6 +273,16 @@ def main():
 
     def step():
         binding.moe_layer_forward(cfg, inp["x"], inp, out, ws, stream)
+
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30))
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copies of {n} bytes done", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         step()
