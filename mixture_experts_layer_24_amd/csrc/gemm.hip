@@ -263,6 +263,15 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// 32-row fragments of a wave's TM-fragment row band holding at least one
+// valid row, given `left` = valid rows from the band's first row (uniform).
+template <int TM>
+__device__ __forceinline__ int live_frags(int64_t left) {
+  if (left <= 0) return 0;
+  const int64_t f = (left + 31) / 32;
+  return f < TM ? (int)f : TM;
+}
+
 // s_waitcnt vmcnt(N) with the other counters left open (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -282,8 +291,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int RPC = 1024 / ROWB;                // rows per 1 KB DMA chunk
   constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
   constexpr int NCH = (BM + BN) / RPC;            // 1 KB DMA chunks per stage
-  constexpr int CPW = NCH / W;                    // chunks per wave per stage
-  static_assert(NCH % W == 0 && BM % RPC == 0 && TM >= 1 && TN >= 1, "tile");
+  constexpr int A_PW = BM / RPC / W;             // activation chunks per wave per stage
+  constexpr int B_PW = BN / RPC / W;             // weight chunks per wave per stage
+  constexpr int CPW = A_PW + B_PW;
+  static_assert(A_PW * W * RPC == BM && B_PW * W * RPC == BN && TM >= 1 && TN >= 1, "tile");
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
   static_assert((NS - 2) * CPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
@@ -314,32 +325,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
-  // this lane's source offset for each of its wave's chunks (K step 0)
-  uint32_t voff[CPW];
+  // Every wave moves A_PW chunks of the activation tile and B_PW chunks of
+  // the weight tile per stage (chunk = 1 KB = RPC tile rows), so the issue
+  // sequence is the same straight-line code in every wave.
+  // this lane's source offset for each of its chunks (K step 0)
+  uint32_t voffa[A_PW], voffb[B_PW];
   const int lr = lane / CPR, slot = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < CPW; i++) {
-    const int q = wave * CPW + i;
-    if (q < BM / RPC) {
-      const int R = RPC * q + lr;
-      int64_t m = R;
-      if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
-      voff[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
-    } else {
-      const int R = RPC * (q - BM / RPC) + lr;
-      voff[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
-    }
+  for (int i = 0; i < A_PW; i++) {
+    const int R = RPC * (wave * A_PW + i) + lr;
+    int64_t m = R;
+    if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
+    voffa[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
   }
-  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CPW; i++) {
-      const int q = wave * CPW + i;  // wave-uniform
-      const uint32_t dst = lds0 + st * STAGE + q * 1024;
-      if (q < BM / RPC)
-        dma16<false>(Abase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
-      else
-        dma16<NTB>(Bbase + (int64_t)kt * ROWB, voff[i], __builtin_amdgcn_readfirstlane(dst));
-    }
+  for (int i = 0; i < B_PW; i++) {
+    const int R = RPC * (wave * B_PW + i) + lr;
+    voffb[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
+  }
+  const uint32_t dsta = lds0 + wave * A_PW * 1024;
+  const uint32_t dstb = lds0 + BM * ROWB + wave * B_PW * 1024;
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+    const char *ga = Abase + (int64_t)kt * ROWB;
+    const char *gb = Bbase + (int64_t)kt * ROWB;
+#pragma unroll
+    for (int i = 0; i < A_PW; i++)
+      dma16<false>(ga, voffa[i], __builtin_amdgcn_readfirstlane(dsta + st * STAGE + i * 1024));
+#pragma unroll
+    for (int i = 0; i < B_PW; i++)
+      dma16<NTB>(gb, voffb[i], __builtin_amdgcn_readfirstlane(dstb + st * STAGE + i * 1024));
   };
 
   f32x16 acc[TM][TN];
@@ -397,6 +411,216 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
   for (int band = 0; band < WM; band++) {
     __syncthreads();  // stage buffers (or the previous band) no longer read
+    if (wm == band) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int Cc = wn * WTN + j * 32 + (lane & 31);
+            float v = acc[i][j][r];
+            if (GELU) v = gelu_f(v);
+            *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
+          }
+    }
+    __syncthreads();
+    const int64_t r0 = m0 + band * WTM;
+    const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
+    for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
+      const int R = idx / OCPR, ch = idx - R * OCPR;
+      if (R < mrows)
+        *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DMA-pipelined GEMM with int8 weights (symmetric codes q, one fp16 scale s
+// per 128 consecutive K elements of a weight row; weight = s * q).
+// The activations (bf16, 128-byte tile rows) and the int8 codes (64-byte
+// tile rows: one 64-wide K step) both travel global -> LDS by DMA, NS - 1 K
+// steps ahead, exactly like gemm_dma_kernel; the scales of the tile's BN
+// weight rows arrive by DMA in blocks of 8 groups (1024 K elements, 16 bytes
+// per row), double-buffered.  Each wave turns its own B fragments into bf16
+// in registers just before the MFMAs: bf16(s * q) with s * q rounded once
+// to fp32 (computed as fma(q + 128, s, -128 s), which is exact up to that
+// one rounding), so the arithmetic is that of a bf16 GEMM on the
+// dequantised weights and half the weight bytes cross LDS.
+// Code tile rows: chunk c (16 codes) of row R sits in slot c ^ ((R >> 2) & 3),
+// which spreads 16 consecutive rows over all 64 banks for the 8-byte operand
+// reads.  Requires K % 1024 == 0 and N % BN == 0.
+// Fragments past the group's valid rows skip their reads and MFMAs, so a
+// partly filled tile costs MFMA time at 32-row granularity.
+__device__ __forceinline__ int swz_q(int R) { return (R >> 2) & 3; }
+
+__device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, float nsc) {
+  lo ^= 0x80808080u;  // q + 128 in each byte
+  hi ^= 0x80808080u;
+  bf16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    r[b] = (bf16)fmaf((float)((lo >> (8 * b)) & 0xffu), sc, nsc);
+    r[4 + b] = (bf16)fmaf((float)((hi >> (8 * b)) & 0xffu), sc, nsc);
+  }
+  return r;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, bool GELU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
+  constexpr int BK = 64;
+  constexpr int W = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int AROWB = BK * 2;                 // bytes per activation tile row
+  constexpr int BROWB = BK;                     // bytes per code tile row
+  constexpr int A_CH = BM * AROWB / 1024;       // 1 KB DMA chunks per stage
+  constexpr int B_CH = BN * BROWB / 1024;
+  constexpr int A_PW = A_CH / W, B_PW = B_CH / W;  // chunks per wave per stage
+  constexpr int CPW = A_PW + B_PW;
+  constexpr int ASTAGE = BM * AROWB;
+  constexpr int STAGE = ASTAGE + BN * BROWB;
+  constexpr int SCB = BN * 16;                  // one scale block (8 groups)
+  constexpr int SC_CH = SCB / 1024;
+  static_assert(A_PW * W == A_CH && B_PW * W == B_CH && TM >= 1 && TN >= 1 && SC_CH <= W, "tile");
+  static_assert(NS >= 2 && NS * STAGE + 2 * SCB <= 160 * 1024, "LDS budget");
+  static_assert((NS - 2) * CPW < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + 2 * SCB];
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tiles_n = a.N / BN;
+  const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
+  const int total = a.G * tiles_m * tiles_n;
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
+                                  : xcd_remap(blockIdx.x, total);
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
+  int64_t rows = a.M_cap;
+  if (a.rows) {
+    const int64_t r = a.rows[g];
+    rows = r < rows ? r : rows;
+  }
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= rows) return;
+  const int n0 = tn * BN;
+  const int K = a.K, N = a.N, KG = K / 128;
+  const char *Abase = (const char *)a.A + ((int64_t)g * a.M_cap + m0) * K * 2;
+  const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K;
+  const char *Sbase = (const char *)a.Bscale + ((int64_t)g * N + n0) * (int64_t)KG * 2;
+  bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  const uint32_t lds_sc = lds0 + NS * STAGE;
+
+  // every wave moves A_PW activation chunks and B_PW code chunks per stage
+  uint32_t voffa[A_PW], voffb[B_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; i++) {
+    const int R = 8 * (wave * A_PW + i) + lane / 8, slot = lane % 8;
+    int64_t m = R;
+    if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
+    voffa[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<64>(R)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < B_PW; i++) {
+    const int R = 16 * (wave * B_PW + i) + lane / 4, slot = lane % 4;
+    voffb[i] = (uint32_t)((int64_t)R * K + ((slot ^ swz_q(R)) << 4));
+  }
+  const uint32_t soff = (uint32_t)((64 * wave + lane) * KG * 2);  // scale chunk of wave < SC_CH
+  const uint32_t dsta = lds0 + wave * A_PW * 1024;
+  const uint32_t dstb = lds0 + ASTAGE + wave * B_PW * 1024;
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+    const char *ga = Abase + (int64_t)kt * AROWB;
+    const char *gb = Bbase + (int64_t)kt * BROWB;
+#pragma unroll
+    for (int i = 0; i < A_PW; i++)
+      dma16<false>(ga, voffa[i], __builtin_amdgcn_readfirstlane(dsta + st * STAGE + i * 1024));
+#pragma unroll
+    for (int i = 0; i < B_PW; i++)
+      dma16<false>(gb, voffb[i], __builtin_amdgcn_readfirstlane(dstb + st * STAGE + i * 1024));
+  };
+  auto issue_scales = [&](int blk) __attribute__((always_inline)) {
+    if (wave < SC_CH)
+      dma16<false>(Sbase + blk * 16, soff,
+                   __builtin_amdgcn_readfirstlane(lds_sc + (blk & 1) * SCB + wave * 1024));
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int ksteps = K / BK;
+  const int live = live_frags<TM>(rows - m0 - wm * WTM);
+  issue_scales(0);
+#pragma unroll
+  for (int p = 0; p < NS - 1; p++)
+    if (p < ksteps) issue(p, p);
+  for (int kt = 0; kt < ksteps; kt++) {
+    if (kt + NS - 2 < ksteps)
+      wait_vmcnt<(NS - 2) * CPW>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    // the next scale block's buffer was last read in the previous block
+    if ((kt & 15) == 0 && kt + 16 < ksteps) issue_scales((kt >> 4) + 1);
+    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
+    if (live == 0) continue;
+    const char *sa = smem + (kt % NS) * STAGE;
+    const char *sb = sa + ASTAGE;
+    const char *ss = smem + NS * STAGE + ((kt >> 4) & 1) * SCB + ((kt >> 1) & 7) * 2;
+    float sc[TN], nsc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      const int R = wn * WTN + j * 32 + (lane & 31);
+      sc[j] = (float)*(const _Float16 *)(ss + R * 16);
+      nsc[j] = -128.f * sc[j];
+    }
+    // the MFMA body for LV live fragments, free of branches so that operand
+    // reads and MFMAs can be interleaved; one copy per fragment count
+    auto body = [&](auto LV) __attribute__((always_inline)) {
+      constexpr int L = decltype(LV)::value;
+#pragma unroll
+      for (int s = 0; s < BK / 16; s++) {
+        const int c = 2 * s + (lane >> 5);
+        bf16x8 af[L], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < L; i++) {
+          const int R = wm * WTM + i * 32 + (lane & 31);
+          af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          const int R = wn * WTN + j * 32 + (lane & 31);
+          const uint32_t *qp =
+              (const uint32_t *)(sb + R * BROWB + ((s ^ swz_q(R)) << 4) + 8 * (lane >> 5));
+          bfr[j] = dequant8(qp[0], qp[1], sc[j], nsc[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < L; i++)
+#pragma unroll
+          for (int j = 0; j < TN; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        // keep each sub-step's operands live only for its own MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    body(std::integral_constant<int, TM>{});
+  }
+
+  // epilogue as in gemm_dma_kernel
+  constexpr int CROW = BN * 2 + 16;
+  static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
+  constexpr int OCPR = BN / 8;
+  for (int band = 0; band < WM; band++) {
+    __syncthreads();
     if (wm == band) {
 #pragma unroll
       for (int i = 0; i < TM; i++)
@@ -522,6 +746,20 @@ static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t 
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int NS>
+static hipError_t launch_dma_i8(const GemmArgs &a, int gelu, hipStream_t s, const char *role,
+                                const char *tile) {
+  const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
+  if (tiles <= 0) return hipGetLastError();
+  const dim3 grid(tiles), block(64 * WM * WN);
+  const char *name = intern_name(role, tile);
+  if (gelu)
+    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, true>), grid, block, 0, s, a);
+  else
+    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 // Tile choice (measured on MI355X at the workload shapes) by rows per group
 // (the capacity, or T for the dense MLP), N, and whether the weights are
 // streamed once (expert GEMMs: non-temporal weight loads).
@@ -539,6 +777,10 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
   }
   const int nt = a.rows != nullptr;  // grouped expert GEMM: weights read once
   if (b_int8) {  // int8 groups: N and K are multiples of 128 (validated)
+    if (a.K % 1024 == 0 && a.N % 256 == 0) {
+      if (a.M_cap > 128) return launch_dma_i8<256, 256, 2, 4, 3>(a, gelu, s, role, "dma256x256_i8");
+      return launch_dma_i8<128, 256, 2, 4, 4>(a, gelu, s, role, "dma128x256_i8");
+    }
     if (a.M_cap <= 32) return launch_cfg<32, 128, 1, 4, 32>(a, 1, gelu, s, role, "bm32_bn128_i8");
     if (a.M_cap <= 64) return launch_cfg<64, 128, 1, 4, 32>(a, 1, gelu, s, role, "bm64_bn128_i8");
     if (a.M_cap <= 128 || a.N % 256)

@@ -214,7 +214,9 @@ def test_dispatch_alone(T, E, k, C):
 # (C, d, d_ff): weight-streaming tiles for C <= 32 / 64 / 128, 256x256 and
 # 128x128 block tiles above, the 16x64 tile when N is not a multiple of 128
 FFN_CASES = [(10, 128, 256), (20, 128, 256), (50, 128, 256), (100, 256, 384), (128, 128, 128),
-             (300, 256, 512), (200, 384, 384), (40, 192, 320)]
+             (300, 256, 512), (200, 384, 384), (40, 192, 320),
+             # K a multiple of 1024: the DMA int8 tiles (256- and 128-row), partial tiles
+             (300, 1024, 1024), (100, 1024, 2048)]
 
 
 @pytest.mark.parametrize("wfmt", ["plain", "int8"])
@@ -318,8 +320,10 @@ def test_layer_is_deterministic_and_ignores_unwritten_rows():
     assert torch.isfinite(b.y.float()).all()
 
 
-def test_int8_path_equals_bf16_path_on_power_of_two_scales():
-    wl = W("q", T=400, d=256, E=4, k=2, d_ff=384, capacity_factor=1.0, wfmt="int8")
+@pytest.mark.parametrize("T,d,F", [(400, 256, 384), (400, 1024, 2048), (200, 1024, 2048)])
+def test_int8_path_equals_bf16_path_on_power_of_two_scales(T, d, F):
+    # same tile shape on both paths -> same MFMA order -> bit-identical outputs
+    wl = W("q", T=T, d=d, E=4, k=2, d_ff=F, capacity_factor=1.0, wfmt="int8")
     inp = synth.make_inputs(wl, seed=4, pow2_scales=True)
     deq = {}
     for n in ("w1", "w2"):
