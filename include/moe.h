@@ -32,9 +32,15 @@
  *     is launched and no output is written.  Return 0 (MOE_OK) or a negative
  *     MOE_ERR_* code; moe_status_string() names it.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
- *   - Apart from the optional timing records (moe_profile_*), the library
- *     keeps no state between calls; calls on different streams with disjoint
- *     buffers may run concurrently.
+ *   - Apart from the optional timing records (moe_profile_*) and the side
+ *     stream below, the library keeps no state between calls; calls on
+ *     different streams with disjoint buffers may run concurrently.
+ *   - moe_layer_forward with pr_moe and overlap_dense runs the dense MLP on a
+ *     library-owned side stream (non-blocking, default priority; one per
+ *     device, created with its two events on the first such call and kept
+ *     until the process ends), forked from and joined back into `stream`
+ *     with events, so the call stays asynchronous and ordered on `stream` as
+ *     a whole.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -89,6 +95,9 @@ typedef struct moe_config {
   int32_t add_skip;       /* 1 = add x (the residual a dropped token rides) */
   int32_t drop_policy;    /* MOE_DROP_TOKEN_ORDER */
   float aux_alpha;        /* alpha of the load-balance loss */
+  int32_t overlap_dense;  /* pr_moe, moe_layer_forward: 1 = run the dense MLP on
+                             the library's side stream, concurrently with the
+                             expert path; 0 = everything in order on `stream` */
 } moe_config;
 
 typedef struct moe_weights {

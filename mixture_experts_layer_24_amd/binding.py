@@ -45,7 +45,7 @@ class Config(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("expert_wfmt", ctypes.c_int32),
                 ("normalize_topk", ctypes.c_int32), ("pr_moe", ctypes.c_int32),
                 ("add_skip", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-                ("aux_alpha", ctypes.c_float)]
+                ("aux_alpha", ctypes.c_float), ("overlap_dense", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -117,14 +117,14 @@ def _check(fn: str, status: int):
 # ------------------------------------------------------------------ config
 def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16",
                 wfmt="plain", d_ff_dense=0, pr_moe=False, add_skip=True,
-                normalize_topk=True, aux_alpha=1.0) -> Config:
+                normalize_topk=True, aux_alpha=1.0, overlap_dense=True) -> Config:
     return Config(T=T, d=d, E=E, k=k, d_ff=d_ff, d_ff_dense=d_ff_dense,
                   capacity_factor=capacity_factor, capacity=capacity,
                   act_dtype=MOE_F32 if act == "f32" else MOE_BF16,
                   expert_wfmt=MOE_W_INT8_G128 if wfmt == "int8" else MOE_W_PLAIN,
                   normalize_topk=int(normalize_topk), pr_moe=int(pr_moe),
                   add_skip=int(add_skip), drop_policy=MOE_DROP_TOKEN_ORDER,
-                  aux_alpha=aux_alpha)
+                  aux_alpha=aux_alpha, overlap_dense=int(overlap_dense))
 
 
 def config_of(wl: Workload, **override) -> Config:

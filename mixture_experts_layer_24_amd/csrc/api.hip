@@ -349,6 +349,36 @@ int moe_combine(const moe_config *cfg, const void *y_disp, const int32_t *expert
                                              (hipStream_t)stream));
 }
 
+// PR-MoE: the dense MLP depends only on x, the expert path only on x and the
+// router, so the layer forks the dense MLP (MFMA-bound) onto a second stream
+// beside the expert path (weight-streaming) and joins it before the combine.
+// One non-blocking side stream (default priority) and one fork/join event
+// pair per device, created on first use and kept for the life of the process;
+// the mutex keeps the record/wait pairs of concurrent callers from
+// interleaving (their dense MLPs queue on the one side stream).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+static std::mutex g_side_mu;
+static std::vector<SideStream> g_side;
+
+static hipError_t side_stream(SideStream **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  SideStream &r = g_side[dev];
+  if (!r.s) {
+    e = hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  *out = &r;
+  return hipSuccess;
+}
+
 int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w,
                       moe_outputs *out, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_config(cfg);
@@ -383,7 +413,20 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   if (cfg->pr_moe) dense = out->dense_out ? out->dense_out : at(ws, L.dense);
 
   hipError_t e = hipSuccess;
-  if (cfg->pr_moe) e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), s);
+  // fork: the dense MLP on the side stream
+  std::unique_lock<std::mutex> side_lock;
+  SideStream *side = nullptr;
+  if (cfg->pr_moe && cfg->overlap_dense && T > 0) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mu);
+    e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e == hipSuccess)
+      e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), side->s);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+  } else if (cfg->pr_moe) {
+    e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), s);
+  }
   double *term = (double *)at(ws, L.term);
   if (e == hipSuccess)
     e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates, out->logits,
@@ -397,6 +440,8 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
                       hidden, s);
+  // join: the combine reads D(x)
+  if (e == hipSuccess && side) e = hipStreamWaitEvent(s, side->join, 0);
   if (e == hipSuccess)
     e = moe_host::launch_combine(y_disp, out->expert_ids, out->slots, out->gates,
                                  cfg->add_skip ? x : nullptr, dense, out->y, T, (int)cfg->d,

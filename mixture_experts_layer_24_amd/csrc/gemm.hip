@@ -224,10 +224,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 // 128-byte rows, or 32: 64-byte rows, which halves a stage so large tiles
 // can keep more steps in flight).  Chunk c of row R sits in slot c ^ f(R):
 //   BK = 64: f(R) = (R & 7) ^ ((R >> 3) & 1)
-//   BK = 32: f(R) = ((R >> 1) ^ (R >> 3)) & 3
+//   BK = 32: f(R) = (R >> 2) & 3
 // which keeps the 16-byte MFMA operand reads (32 consecutive rows, one
-// logical chunk) free of bank conflicts with 32 banks (128 bytes per pass) or
-// 64 banks (256 bytes per pass).  The DMA lane -> (row, slot) placement is
+// logical chunk) free of bank conflicts on gfx950's LDS (checked with the
+// SQ_LDS_BANK_CONFLICT counter).  The DMA lane -> (row, slot) placement is
 // fixed (16 bytes per lane, consecutive), so each lane fetches the global
 // chunk that belongs in its slot.
 // The DMA loads are issued from inline assembly (they have no register
@@ -239,7 +239,7 @@ __device__ __forceinline__ int swz_slot(int R) {
   if constexpr (BK == 64)
     return (R & 7) ^ ((R >> 3) & 1);
   else
-    return ((R >> 1) ^ (R >> 3)) & 3;
+    return (R >> 2) & 3;
 }
 
 // NT: non-temporal (streamed once, e.g. expert weights: ~7.0 vs ~6.2 TB/s
@@ -290,7 +290,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
   constexpr int RPC = 1024 / ROWB;                // rows per 1 KB DMA chunk
   constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
-  constexpr int NCH = (BM + BN) / RPC;            // 1 KB DMA chunks per stage
   constexpr int A_PW = BM / RPC / W;             // activation chunks per wave per stage
   constexpr int B_PW = BN / RPC / W;             // weight chunks per wave per stage
   constexpr int CPW = A_PW + B_PW;

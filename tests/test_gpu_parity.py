@@ -25,8 +25,8 @@ def _cpu(inp):
     return {k: (None if v is None else v.cpu()) for k, v in inp.items()}
 
 
-def _run_layer(wl, inp, **alloc):
-    cfg = binding.config_of(wl)
+def _run_layer(wl, inp, overlap_dense=True, **alloc):
+    cfg = binding.config_of(wl, overlap_dense=overlap_dense)
     out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True,
                                 dense_out=True, **alloc)
     ws = binding.alloc_workspace(cfg)
@@ -340,6 +340,19 @@ def test_int8_path_equals_bf16_path_on_power_of_two_scales(T, d, F):
     assert torch.equal(out_q.kept, out_b.kept)
     for e, n in enumerate(out_q.kept.tolist()):  # rows past kept[e] are never written
         assert torch.equal(out_q.y_disp[e, :n], out_b.y_disp[e, :n])
+
+
+def test_dense_overlap_matches_in_order_layer():
+    # the dense MLP on the side stream (fork/join) gives the same bits as the
+    # dense MLP in order on the caller's stream, over repeated calls
+    wl = W("ov", T=700, d=256, E=8, k=2, d_ff=512, capacity_factor=1.0, d_ff_dense=512,
+           pr_moe=True, add_skip=True)
+    dinp = {k: (None if v is None else v.to(DEV)) for k, v in synth.make_inputs(wl, seed=11).items()}
+    _, ref, _ = _run_layer(wl, dinp, overlap_dense=False)
+    for _ in range(3):
+        _, out, _ = _run_layer(wl, dinp, overlap_dense=True)
+        assert torch.equal(out.y, ref.y)
+        assert torch.equal(out.dense_out, ref.dense_out)
 
 
 def test_empty_batch():
