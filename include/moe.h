@@ -70,7 +70,13 @@ extern "C" {
                              weight = s * q (survey notes sec. 1.2.2) */
 
 /* capacity overflow policy */
-#define MOE_DROP_TOKEN_ORDER 0 /* first come, first served in token order */
+#define MOE_DROP_TOKEN_ORDER 0   /* first come, first served in token order */
+#define MOE_DROP_GATE_PRIORITY 1 /* an expert keeps the C assignments with the
+                                    largest gates, ties to the earlier token;
+                                    slot = rank in that order ("DeepSpeed-MoE
+                                    vs Switch Transformer", capacity example in
+                                    which the lower-probability token is the
+                                    one dropped) */
 
 /* workspace query selectors */
 #define MOE_ENTRY_ROUTE 0
@@ -93,7 +99,7 @@ typedef struct moe_config {
   int32_t normalize_topk; /* k >= 2: 1 = gates renormalised over the k */
   int32_t pr_moe;         /* 1 = add the fixed dense MLP D(x) */
   int32_t add_skip;       /* 1 = add x (the residual a dropped token rides) */
-  int32_t drop_policy;    /* MOE_DROP_TOKEN_ORDER */
+  int32_t drop_policy;    /* MOE_DROP_TOKEN_ORDER | MOE_DROP_GATE_PRIORITY */
   float aux_alpha;        /* alpha of the load-balance loss */
   int32_t overlap_dense;  /* pr_moe, moe_layer_forward: 1 = run the dense MLP on
                              the library's side stream, concurrently with the
@@ -124,6 +130,7 @@ typedef struct moe_outputs {
   void *x_disp;        /* [E, C, d] act; NULL = in the workspace */
   void *y_disp;        /* [E, C, d] act; NULL = in the workspace */
   void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
+  float *z_loss;       /* [1] router z-loss                     optional */
 } moe_outputs;
 
 /* Capacity C of the configuration, or a negative MOE_ERR_* code. */
@@ -137,23 +144,31 @@ size_t moe_workspace_bytes(const moe_config *cfg, int entry);
  * Transformer", section "router computation"; survey notes sec. 1.1.1.1 and
  * 1.1.4.1).  x [T, d], w_router [E, d] act; b_router [E] or NULL.
  * Out: expert_ids [T, k], gates [T, k], logits [T, E] (NULL = not written),
- * aux_loss [1].  Logits accumulate in fp32. */
+ * aux_loss [1], z_loss [1] (NULL = not computed): the router z-loss
+ * ("DeepSpeed-MoE vs Switch Transformer", section "Router Z-loss"), the mean
+ * over tokens of the squared log-sum-exp of the token's logits (+ bias).
+ * Logits accumulate in fp32; the log-sum-exp is fp32 per token, the mean is
+ * summed in fp64 in a fixed order. */
 int moe_route(const moe_config *cfg, const void *x, const void *w_router,
               const float *b_router, int32_t *expert_ids, float *gates,
-              float *logits, float *aux_loss, void *ws, size_t ws_bytes,
-              void *stream);
+              float *logits, float *aux_loss, float *z_loss, void *ws,
+              size_t ws_bytes, void *stream);
 
-/* Capacity-limited dispatch in token order and the layout transform into
- * the expert-major buffer ("DeepSpeed MoE and Model Compression",
- * pack_by_expert; "DeepSpeed-MoE ... notes" sec. 4.4 cumsum mapping table
- * and layout transformation).  x [T, d], expert_ids [T, k].
+/* Capacity-limited dispatch and the layout transform into the expert-major
+ * buffer ("DeepSpeed MoE and Model Compression", pack_by_expert;
+ * "DeepSpeed-MoE ... notes" sec. 4.4 cumsum mapping table and layout
+ * transformation).  x [T, d], expert_ids [T, k]; gates [T, k] fp32 (used by
+ * MOE_DROP_GATE_PRIORITY, where it is required and must be finite; may be
+ * NULL for MOE_DROP_TOKEN_ORDER).
  * Out: slots [T, k] (-1 = dropped), drop_mask [T, k] (NULL ok), load [E],
  * kept [E], x_disp [E, C, d]: row (e, s) = x[t] for the assignment with slot
- * s in expert e; rows s >= kept[e] are not written. */
+ * s in expert e; rows s >= kept[e] are not written.  Token order: an
+ * expert's n-th assignment in token order gets slot n.  Gate priority: slot
+ * = rank by (gate descending, token ascending). */
 int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids,
-                 int32_t *slots, uint8_t *drop_mask, int32_t *load,
-                 int32_t *kept, void *x_disp, void *ws, size_t ws_bytes,
-                 void *stream);
+                 const float *gates, int32_t *slots, uint8_t *drop_mask,
+                 int32_t *load, int32_t *kept, void *x_disp, void *ws,
+                 size_t ws_bytes, void *stream);
 
 /* Every expert's two-layer GELU FFN over its kept rows (survey notes sec.
  * 1.1.2.1; weight-only int8 dequantisation, survey notes sec. 1.2.3.1).

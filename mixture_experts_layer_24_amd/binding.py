@@ -24,6 +24,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_W_PLAIN, MOE_W_INT8_G128 = 0, 1
 MOE_DROP_TOKEN_ORDER = 0
+MOE_DROP_GATE_PRIORITY = 1
 ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER = range(5)
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch",
@@ -56,7 +57,7 @@ class Weights(ctypes.Structure):
 class Outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("y", "expert_ids", "gates", "slots", "load", "kept", "aux_loss", "drop_mask",
-                 "logits", "x_disp", "y_disp", "dense_out")]
+                 "logits", "x_disp", "y_disp", "dense_out", "z_loss")]
 
 
 _lock = threading.Lock()
@@ -80,9 +81,9 @@ def lib():
             L.moe_workspace_bytes.restype = sz
             L.moe_workspace_bytes.argtypes = [cfgp, i32]
             L.moe_route.restype = i32
-            L.moe_route.argtypes = [cfgp] + [vp] * 7 + [vp, sz, vp]
+            L.moe_route.argtypes = [cfgp] + [vp] * 8 + [vp, sz, vp]
             L.moe_dispatch.restype = i32
-            L.moe_dispatch.argtypes = [cfgp] + [vp] * 7 + [vp, sz, vp]
+            L.moe_dispatch.argtypes = [cfgp] + [vp] * 8 + [vp, sz, vp]
             L.moe_expert_ffn.restype = i32
             L.moe_expert_ffn.argtypes = [cfgp] + [vp] * 7 + [vp, sz, vp]
             L.moe_dense_mlp.restype = i32
@@ -117,13 +118,18 @@ def _check(fn: str, status: int):
 # ------------------------------------------------------------------ config
 def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16",
                 wfmt="plain", d_ff_dense=0, pr_moe=False, add_skip=True,
-                normalize_topk=True, aux_alpha=1.0, overlap_dense=True) -> Config:
+                normalize_topk=True, aux_alpha=1.0, overlap_dense=True,
+                drop_policy="token_order") -> Config:
+    if drop_policy not in ("token_order", "gate_priority"):
+        raise ValueError(f"drop_policy {drop_policy!r}")
     return Config(T=T, d=d, E=E, k=k, d_ff=d_ff, d_ff_dense=d_ff_dense,
                   capacity_factor=capacity_factor, capacity=capacity,
                   act_dtype=MOE_F32 if act == "f32" else MOE_BF16,
                   expert_wfmt=MOE_W_INT8_G128 if wfmt == "int8" else MOE_W_PLAIN,
                   normalize_topk=int(normalize_topk), pr_moe=int(pr_moe),
-                  add_skip=int(add_skip), drop_policy=MOE_DROP_TOKEN_ORDER,
+                  add_skip=int(add_skip),
+                  drop_policy=(MOE_DROP_GATE_PRIORITY if drop_policy == "gate_priority"
+                               else MOE_DROP_TOKEN_ORDER),
                   aux_alpha=aux_alpha, overlap_dense=int(overlap_dense))
 
 
@@ -192,7 +198,7 @@ def _wdtype(cfg):
 
 # ------------------------------------------------------------------ entry points
 def moe_route(cfg, x, w_router, b_router, expert_ids, gates, logits, aux_loss, ws,
-              stream=None):
+              stream=None, z_loss=None):
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     a = _act_dtype(cfg)
     wsp, wsn = _ws(ws)
@@ -202,17 +208,21 @@ def moe_route(cfg, x, w_router, b_router, expert_ids, gates, logits, aux_loss, w
         _ptr(expert_ids, (T, k), torch.int32, "expert_ids"),
         _ptr(gates, (T, k), torch.float32, "gates"),
         _ptr(logits, (T, E), torch.float32, "logits", True),
-        _ptr(aux_loss, (1,), torch.float32, "aux_loss"), wsp, wsn, _stream(stream)))
+        _ptr(aux_loss, (1,), torch.float32, "aux_loss"),
+        _ptr(z_loss, (1,), torch.float32, "z_loss", True), wsp, wsn, _stream(stream)))
 
 
-def moe_dispatch(cfg, x, expert_ids, slots, drop_mask, load, kept, x_disp, ws, stream=None):
+def moe_dispatch(cfg, x, expert_ids, slots, drop_mask, load, kept, x_disp, ws, stream=None,
+                 gates=None):
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     C = capacity(cfg)
     a = _act_dtype(cfg)
     wsp, wsn = _ws(ws)
+    gp = cfg.drop_policy == MOE_DROP_GATE_PRIORITY
     _check("moe_dispatch", lib().moe_dispatch(
         ctypes.byref(cfg), _ptr(x, (T, d), a, "x"),
         _ptr(expert_ids, (T, k), torch.int32, "expert_ids"),
+        _ptr(gates, (T, k), torch.float32, "gates", not gp),
         _ptr(slots, (T, k), torch.int32, "slots"),
         _ptr(drop_mask, (T, k), torch.uint8, "drop_mask", True),
         _ptr(load, (E,), torch.int32, "load"), _ptr(kept, (E,), torch.int32, "kept"),
@@ -270,10 +280,11 @@ class LayerOutputs:
     x_disp: torch.Tensor | None = None
     y_disp: torch.Tensor | None = None
     dense_out: torch.Tensor | None = None
+    z_loss: torch.Tensor | None = None
 
 
 def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
-                  x_disp=False, y_disp=False, dense_out=False) -> LayerOutputs:
+                  x_disp=False, y_disp=False, dense_out=False, z_loss=False) -> LayerOutputs:
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     C = capacity(cfg)
     a = _act_dtype(cfg)
@@ -285,7 +296,8 @@ def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
         drop_mask=e(T, k, dt=torch.uint8) if drop_mask else None,
         logits=e(T, E, dt=torch.float32) if logits else None,
         x_disp=e(E, C, d) if x_disp else None, y_disp=e(E, C, d) if y_disp else None,
-        dense_out=e(T, d) if (dense_out and cfg.pr_moe) else None)
+        dense_out=e(T, d) if (dense_out and cfg.pr_moe) else None,
+        z_loss=e(1, dt=torch.float32) if z_loss else None)
 
 
 def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):
@@ -318,7 +330,8 @@ def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None)
         logits=_ptr(out.logits, (T, E), torch.float32, "logits", True),
         x_disp=_ptr(out.x_disp, (E, C, d), a, "x_disp", True),
         y_disp=_ptr(out.y_disp, (E, C, d), a, "y_disp", True),
-        dense_out=_ptr(out.dense_out, (T, d), a, "dense_out", True))
+        dense_out=_ptr(out.dense_out, (T, d), a, "dense_out", True),
+        z_loss=_ptr(out.z_loss, (1,), torch.float32, "z_loss", True))
     wsp, wsn = _ws(ws)
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), _ptr(x, (T, d), a, "x"), ctypes.byref(W), ctypes.byref(O),

@@ -36,8 +36,10 @@ int check_config(const moe_config *c) {
     return MOE_ERR_INVALID_ARG;
   if (c->pr_moe && c->d_ff_dense < 1) return MOE_ERR_INVALID_ARG;
   if (!isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
-  if (c->drop_policy != MOE_DROP_TOKEN_ORDER) return MOE_ERR_UNSUPPORTED;
+  if (c->drop_policy != MOE_DROP_TOKEN_ORDER && c->drop_policy != MOE_DROP_GATE_PRIORITY)
+    return MOE_ERR_INVALID_ARG;
   if (c->E > 256 || c->k > 8 || c->T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (c->T * c->k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;  // int32 slots/positions
   if (c->d > (1 << 20) || c->d_ff > (1 << 20) || c->d_ff_dense > (1 << 20))
     return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_BF16) {
@@ -72,7 +74,8 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 
 // ---- workspace layout
 struct Layout {
-  size_t qsum, fcount, hist, offs, term, x_disp, y_disp, hidden, hidden_dense, dense, total;
+  size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
+      total;
 };
 
 Layout layout(const moe_config *c, int entry) {
@@ -88,15 +91,19 @@ Layout layout(const moe_config *c, int entry) {
     o += align256(bytes);
     return at;
   };
+  const bool gp = c->drop_policy == MOE_DROP_GATE_PRIORITY;
+  const size_t segB = (size_t)c->T * (size_t)c->k * 4;
   switch (entry) {
     case MOE_ENTRY_ROUTE:
       L.qsum = take(blkE);
       L.fcount = take(blkE);
       L.term = take(termE);
+      L.zpart = take((size_t)nblk * 4);
       break;
     case MOE_ENTRY_DISPATCH:
       L.hist = take(blkE);
       L.offs = take(blkE);
+      if (gp) L.seg = take(segB);
       break;
     case MOE_ENTRY_EXPERT_FFN:
       L.hidden = take((size_t)c->E * C * c->d_ff * as);
@@ -109,6 +116,8 @@ Layout layout(const moe_config *c, int entry) {
       L.hist = take(blkE);
       L.offs = take(blkE);
       L.term = take(termE);
+      L.zpart = take((size_t)nblk * 4);
+      if (gp) L.seg = take(segB);
       L.x_disp = take((size_t)c->E * C * c->d * as);
       L.y_disp = take((size_t)c->E * C * c->d * as);
       L.hidden = take((size_t)c->E * C * c->d_ff * as);
@@ -139,7 +148,7 @@ char *at(void *ws, size_t off) { return (char *)ws + off; }
 // ---- launch sequences (arguments already validated)
 hipError_t do_router(const moe_config *c, const void *x, const void *wr, const float *br,
                      int32_t *ids, float *gates, float *logits, float *qsum, int32_t *fcount,
-                     int32_t *hist, hipStream_t s) {
+                     int32_t *hist, float *zpart, float *z_loss, hipStream_t s) {
   RouterArgs a{};
   a.x = x;
   a.w = wr;
@@ -155,18 +164,27 @@ hipError_t do_router(const moe_config *c, const void *x, const void *wr, const f
   a.E = (int)c->E;
   a.k = (int)c->k;
   a.normalize = c->normalize_topk;
-  return moe_host::launch_router(a, c->act_dtype == MOE_BF16, s);
+  a.zpart = z_loss ? zpart : nullptr;
+  hipError_t e = moe_host::launch_router(a, c->act_dtype == MOE_BF16, s);
+  if (e == hipSuccess && z_loss)
+    e = moe_host::launch_zloss_sum(zpart, moe_host::router_blocks(c->T), c->T, z_loss, s);
+  return e;
 }
 
-// place slots in token order and gather the kept rows; hist/offs are the
-// per-block counts and offsets ([E][blocks]); aux_term non-null -> the place
-// kernel also finishes the aux loss
+// place slots (token order, or gate priority through the segment array
+// `seg`, which needs gates and load) and gather the kept rows; hist/offs are
+// the per-block counts and offsets ([E][blocks]); aux_term non-null -> the
+// place kernel also finishes the aux loss
 hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *ids,
-                           const int32_t *offs, int32_t *slots, uint8_t *drop,
-                           const double *aux_term, float *aux, void *x_disp, hipStream_t s) {
+                           const float *gates, const int32_t *offs, const int32_t *load,
+                           int32_t *seg, int32_t *slots, uint8_t *drop, const double *aux_term,
+                           float *aux, void *x_disp, hipStream_t s) {
   const int64_t C = capacity_of(c);
+  const bool gp = c->drop_policy == MOE_DROP_GATE_PRIORITY;
   hipError_t e = moe_host::launch_dispatch_place(ids, offs, c->T, (int)c->E, (int)c->k, C, slots,
-                                                 drop, aux_term, c->aux_alpha, aux, s);
+                                                 drop, aux_term, c->aux_alpha, aux, s,
+                                                 gp ? gates : nullptr, gp ? load : nullptr,
+                                                 gp ? seg : nullptr);
   if (e != hipSuccess) return e;
   return moe_host::launch_gather(x, ids, slots, c->T, (int)c->k, C,
                                  c->d * (int64_t)act_size(c), x_disp, s);
@@ -253,14 +271,14 @@ size_t moe_workspace_bytes(const moe_config *cfg, int entry) {
 }
 
 int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *b_router,
-              int32_t *expert_ids, float *gates, float *logits, float *aux_loss, void *ws,
-              size_t ws_bytes, void *stream) {
+              int32_t *expert_ids, float *gates, float *logits, float *aux_loss, float *z_loss,
+              void *ws, size_t ws_bytes, void *stream) {
   int rc = check_config(cfg);
   if (rc != MOE_OK) return rc;
   const int64_t T = cfg->T, Tk = T * cfg->k;
   if (!need(x, T, 16) || !need(w_router, 1, 16) || !opt(b_router, 4) ||
       !need(expert_ids, Tk, 4) || !need(gates, Tk, 4) || !opt(logits, 4) ||
-      !need(aux_loss, 1, 4))
+      !need(aux_loss, 1, 4) || !opt(z_loss, 4))
     return MOE_ERR_INVALID_ARG;
   rc = check_ws(cfg, MOE_ENTRY_ROUTE, ws, ws_bytes);
   if (rc != MOE_OK) return rc;
@@ -270,7 +288,7 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   int32_t *fcount = (int32_t *)at(ws, L.fcount);
   double *term = (double *)at(ws, L.term);
   hipError_t e = do_router(cfg, x, w_router, b_router, expert_ids, gates, logits, qsum, fcount,
-                           nullptr, s);
+                           nullptr, (float *)at(ws, L.zpart), z_loss, s);
   if (e == hipSuccess)
     e = moe_host::launch_scan_aux(nullptr, qsum, fcount, moe_host::router_blocks(T),
                                   (int)cfg->E, T, 0, nullptr, nullptr, nullptr, term, s);
@@ -278,14 +296,16 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   return hip_status(e);
 }
 
-int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids, int32_t *slots,
-                 uint8_t *drop_mask, int32_t *load, int32_t *kept, void *x_disp, void *ws,
-                 size_t ws_bytes, void *stream) {
+int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids,
+                 const float *gates, int32_t *slots, uint8_t *drop_mask, int32_t *load,
+                 int32_t *kept, void *x_disp, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_config(cfg);
   if (rc != MOE_OK) return rc;
   const int64_t T = cfg->T, Tk = T * cfg->k, C = capacity_of(cfg);
+  const bool gp = cfg->drop_policy == MOE_DROP_GATE_PRIORITY;
   if (!need(x, T, 16) || !need(expert_ids, Tk, 4) || !need(slots, Tk, 4) || !opt(drop_mask, 1) ||
-      !need(load, 1, 4) || !need(kept, 1, 4) || !need(x_disp, cfg->E * C, 16))
+      !need(load, 1, 4) || !need(kept, 1, 4) || !need(x_disp, cfg->E * C, 16) ||
+      (gp ? !need(gates, Tk, 4) : !opt(gates, 4)))
     return MOE_ERR_INVALID_ARG;
   rc = check_ws(cfg, MOE_ENTRY_DISPATCH, ws, ws_bytes);
   if (rc != MOE_OK) return rc;
@@ -297,7 +317,9 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids
     e = moe_host::launch_scan_aux(hist, nullptr, nullptr, moe_host::router_blocks(T), (int)cfg->E,
                                   T, C, offs, load, kept, nullptr, s);
   if (e == hipSuccess)
-    e = do_place_gather(cfg, x, expert_ids, offs, slots, drop_mask, nullptr, nullptr, x_disp, s);
+    e = do_place_gather(cfg, x, expert_ids, gates, offs, load,
+                        gp ? (int32_t *)at(ws, L.seg) : nullptr, slots, drop_mask, nullptr,
+                        nullptr, x_disp, s);
   return hip_status(e);
 }
 
@@ -396,7 +418,8 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   if (!need(out->y, T, 16) || !need(out->expert_ids, Tk, 4) || !need(out->gates, Tk, 4) ||
       !need(out->slots, Tk, 4) || !need(out->load, 1, 4) || !need(out->kept, 1, 4) ||
       !need(out->aux_loss, 1, 4) || !opt(out->drop_mask, 1) || !opt(out->logits, 4) ||
-      !opt(out->x_disp, 16) || !opt(out->y_disp, 16) || !opt(out->dense_out, 16))
+      !opt(out->x_disp, 16) || !opt(out->y_disp, 16) || !opt(out->dense_out, 16) ||
+      !opt(out->z_loss, 4))
     return MOE_ERR_INVALID_ARG;
   (void)rowsE;
   rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
@@ -430,13 +453,15 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   double *term = (double *)at(ws, L.term);
   if (e == hipSuccess)
     e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates, out->logits,
-                  qsum, fcount, hist, s);
+                  qsum, fcount, hist, (float *)at(ws, L.zpart), out->z_loss, s);
   if (e == hipSuccess)
     e = moe_host::launch_scan_aux(hist, qsum, fcount, moe_host::router_blocks(T), (int)cfg->E, T,
                                   capacity_of(cfg), offs, out->load, out->kept, term, s);
   if (e == hipSuccess)
-    e = do_place_gather(cfg, x, out->expert_ids, offs, out->slots, out->drop_mask, term,
-                        out->aux_loss, x_disp, s);
+    e = do_place_gather(cfg, x, out->expert_ids, out->gates, offs, out->load,
+                        cfg->drop_policy == MOE_DROP_GATE_PRIORITY ? (int32_t *)at(ws, L.seg)
+                                                                   : nullptr,
+                        out->slots, out->drop_mask, term, out->aux_loss, x_disp, s);
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
                       hidden, s);

@@ -113,14 +113,44 @@ __device__ __forceinline__ int sel4(int v0, int v1, int v2, int v3, int i) {
   return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
 }
 
+// Token-order position of every assignment within its expert (the n-th
+// assignment of expert e in token order has position n), from the per-block
+// offsets; a wave ranks 64 assignments at a time with ballots.
+// Token order (seg == null): slot = position if < C, else dropped.
+// Gate priority (seg != null): no capacity here; the position goes to
+// slots[] and the assignment index to seg[ebase[e] + position], where ebase
+// is the exclusive prefix of load[] over experts, for rank_gate_kernel.
 __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, const int32_t *offs,
                                                             int64_t T, int E, int k, int64_t C,
                                                             int32_t *slots, uint8_t *drop,
                                                             const double *aux_term,
-                                                            float aux_alpha, float *aux) {
+                                                            float aux_alpha, float *aux,
+                                                            const int32_t *load, int32_t *seg) {
   const int lane = lane_id(), blk = blockIdx.x, nblk = gridDim.x;
   // the layer's aux loss is finished here, by block 0, when asked
   if (aux && blk == 0) aux_sum_wave(aux_term, E, aux_alpha, aux);
+  // segment base of expert lane + 64 i (gate priority)
+  int eb0 = 0, eb1 = 0, eb2 = 0, eb3 = 0;
+  if (seg) {
+    int carry = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e = lane + 64 * i;
+      const int v = e < E ? load[e] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += u;
+      }
+      const int b = carry + inc - v;
+      if (i == 0) eb0 = b;
+      else if (i == 1) eb1 = b;
+      else if (i == 2) eb2 = b;
+      else eb3 = b;
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
   // running slot of expert e = lane + 64 i, starting at this block's offset
   int run0 = 0, run1 = 0, run2 = 0, run3 = 0;
   {
@@ -138,7 +168,7 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
     int e = (a < a1) ? ids[a] : -1;
     const bool valid = e >= 0 && e < E;
     if (!valid) e = -1;
-    int slot = -1;
+    int slot = -1, ebase = 0;
     uint64_t rem = __ballot(valid);
     while (rem) {
       const int leader = __ffsll((long long)rem) - 1;
@@ -146,7 +176,11 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
       const uint64_t mask = __ballot(e == el);
       const int ri = el >> 6, rl = el & 63;
       const int start = __builtin_amdgcn_readlane(sel4(run0, run1, run2, run3, ri), rl);
-      if (e == el) slot = start + __popcll(mask & lower);
+      const int eb = __builtin_amdgcn_readlane(sel4(eb0, eb1, eb2, eb3, ri), rl);
+      if (e == el) {
+        slot = start + __popcll(mask & lower);
+        ebase = eb;
+      }
       if (lane == rl) {
         const int add = __popcll(mask);
         if (ri == 0) run0 += add;
@@ -157,10 +191,93 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
       rem &= ~mask;
     }
     if (a < a1) {
-      const bool keep = valid && (int64_t)slot < C;
-      slots[a] = keep ? slot : -1;
-      if (drop) drop[a] = keep ? 0 : 1;
+      if (seg) {
+        slots[a] = valid ? slot : -1;
+        if (valid) seg[ebase + slot] = (int32_t)a;
+        else if (drop) drop[a] = 1;
+      } else {
+        const bool keep = valid && (int64_t)slot < C;
+        slots[a] = keep ? slot : -1;
+        if (drop) drop[a] = keep ? 0 : 1;
+      }
     }
+  }
+}
+
+// Gate-priority capacity: within expert e, assignment p (token-order
+// position) has rank = #{q in e : gate_q > gate_p, or gate_q == gate_p and
+// q < p}; it is kept, with slot = rank, iff rank < C.  Blocks take 256
+// consecutive positions of one expert (expert tiles laid end to end) and
+// compare them with the expert's whole segment, 256 gates at a time through
+// LDS.  Work per expert grows as load^2; exact and deterministic.
+__global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, const float *gates,
+                                                        const int32_t *load, int E, int64_t C,
+                                                        int32_t *slots, uint8_t *drop) {
+  __shared__ int ebase[257], tbase[257];
+  __shared__ int wtot[2][4];
+  __shared__ float cg[256];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  // exclusive prefixes over experts of load and of 256-position tiles
+  const int L = tid < E ? load[tid] : 0;
+  const int nt = (L + 255) / 256;
+  int incl = L, inct = nt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave), w = __shfl_up(inct, o, kWave);
+    if (lane >= o) {
+      incl += u;
+      inct += w;
+    }
+  }
+  if (lane == kWave - 1) {
+    wtot[0][wave] = incl;
+    wtot[1][wave] = inct;
+  }
+  __syncthreads();
+  int bl = 0, bt = 0;
+  for (int w = 0; w < wave; w++) {
+    bl += wtot[0][w];
+    bt += wtot[1][w];
+  }
+  ebase[tid] = bl + incl - L;
+  tbase[tid] = bt + inct - nt;
+  if (tid == 255) {
+    ebase[256] = bl + incl;
+    tbase[256] = bt + inct;
+  }
+  __syncthreads();
+  const int b = blockIdx.x;
+  if (b >= tbase[256]) return;
+  // expert of this block: the last e with tbase[e] <= b (tiles of empty
+  // experts have zero length, so that e has load > 0)
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tbase[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int Le = load[e];
+  const int p = (b - tbase[e]) * 256 + tid;
+  const int32_t *sg = seg + ebase[e];
+  const float g = p < Le ? gates[sg[p]] : 0.f;
+  int rank = 0;
+  for (int c0 = 0; c0 < Le; c0 += 256) {
+    __syncthreads();
+    const int q = c0 + tid;
+    cg[tid] = q < Le ? gates[sg[q]] : 0.f;
+    __syncthreads();
+    const int n = Le - c0 < 256 ? Le - c0 : 256;
+    for (int j = 0; j < n; j++) {
+      const float h = cg[j];
+      rank += (h > g || (h == g && c0 + j < p)) ? 1 : 0;
+    }
+  }
+  if (p < Le) {
+    const int32_t a = sg[p];
+    const bool keep = (int64_t)rank < C;
+    slots[a] = keep ? rank : -1;
+    if (drop) drop[a] = keep ? 0 : 1;
   }
 }
 
@@ -206,13 +323,20 @@ hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t
 
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
                                  int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
-                                 float aux_alpha, float *aux, hipStream_t s) {
+                                 float aux_alpha, float *aux, hipStream_t s, const float *gates,
+                                 const int32_t *load, int32_t *seg) {
   const int nblk = (int)((T + DBT - 1) / DBT);
   if (nblk > 0)
     MOE_LAUNCH("dispatch_place", dispatch_place_kernel, dim3(nblk), dim3(64), 0, s, ids, offs, T,
-               E, k, C, slots, drop, aux_term, aux_alpha, aux);
+               E, k, C, slots, drop, aux_term, aux_alpha, aux, load, seg);
   else if (aux)
     return launch_aux_sum(aux_term, E, aux_alpha, aux, s);
+  if (seg && T > 0) {
+    // tiles of 256 positions, at most T*k/256 + E of them
+    const int64_t tiles = (T * k + 255) / 256 + E;
+    MOE_LAUNCH("rank_gate", rank_gate_kernel, dim3((unsigned)tiles), dim3(256), 0, s, seg, gates,
+               load, E, C, slots, drop);
+  }
   return hipGetLastError();
 }
 

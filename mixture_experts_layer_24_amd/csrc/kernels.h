@@ -16,6 +16,7 @@ struct RouterArgs {
   float *qsum;        // [E, nblk] per-block sum of router probabilities
   int32_t *fcount;    // [E, nblk] per-block count of first choices
   int32_t *hist;      // [E, nblk] per-block count of all k assignments (or null)
+  float *zpart;       // [nblk] per-block sum of squared log-sum-exp (or null)
   int64_t T;
   int d, E, k, normalize;
 };
@@ -39,6 +40,7 @@ namespace moe_host {
 int router_blocks(int64_t T);
 hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
 hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s);
+hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, hipStream_t s);
 
 // dispatch (token blocks of the same size as the router's)
 hipError_t launch_dispatch_count(const int32_t *ids, int64_t T, int E, int k, int32_t *hist,
@@ -49,9 +51,13 @@ hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t
                            int nblk, int E, int64_t T, int64_t C, int32_t *offs, int32_t *load,
                            int32_t *kept, double *term, hipStream_t s);
 // slots in token order; block 0 also finishes the aux loss when aux != null
+// seg == null: token-order capacity.  seg != null: gate priority (gates and
+// load required; seg is workspace of T*k int32).
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
                                  int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
-                                 float aux_alpha, float *aux, hipStream_t s);
+                                 float aux_alpha, float *aux, hipStream_t s,
+                                 const float *gates = nullptr, const int32_t *load = nullptr,
+                                 int32_t *seg = nullptr);
 hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots, int64_t T, int k,
                          int64_t C, int64_t row_bytes, void *x_disp, hipStream_t s);
 

@@ -32,7 +32,9 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
                                 float (*qpart)[256], int *fcnt, int *hcnt, int blk) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int E = a.E, k = a.k;
+  __shared__ float zw[4];
   float q[4] = {0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
   float bias[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -61,6 +63,10 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
       s += p[i];
     }
     s = wave_sum(s);
+    if (a.zpart) {  // z-loss term: (log sum_e exp v_e)^2 = (m + log s)^2
+      const float lz = m + logf(s);
+      zacc += lz * lz;
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       p[i] = p[i] / s;
@@ -124,7 +130,9 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
     const int e = lane + kWave * i;
     if (e < E) qpart[wave][e] = q[i];
   }
+  if (lane == 0) zw[wave] = zacc;
   __syncthreads();
+  if (a.zpart && threadIdx.x == 0) a.zpart[blk] = ((zw[0] + zw[1]) + zw[2]) + zw[3];
   const int e = threadIdx.x;
   if (e < E) {
     const int64_t o = (int64_t)e * gridDim.x + blk;  // expert-major [E][nblk]
@@ -275,12 +283,36 @@ __global__ __launch_bounds__(64) void aux_sum_kernel(const double *term, int E, 
   aux_sum_wave(term, E, alpha, aux);
 }
 
+// Router z-loss, final step: the mean over tokens of the per-block sums,
+// added in fp64 in a fixed order (contiguous chunks, then a tree).
+__global__ __launch_bounds__(256) void zloss_sum_kernel(const float *zpart, int nblk, int64_t T,
+                                                        float *z) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  const int chunk = (nblk + 255) / 256;
+  const int b0 = tid * chunk, b1 = min(b0 + chunk, nblk);
+  double v = 0.0;
+  for (int b = b0; b < b1; b++) v += (double)zpart[b];
+  red[tid] = v;
+  __syncthreads();
+  for (int st = 128; st >= 1; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) z[0] = T > 0 ? (float)(red[0] / (double)T) : 0.f;
+}
+
 }  // namespace moe
 
 namespace moe_host {
 using namespace moe;
 
 int router_blocks(int64_t T) { return (int)((T + RBM - 1) / RBM); }
+
+hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, hipStream_t s) {
+  MOE_LAUNCH("zloss_sum", zloss_sum_kernel, dim3(1), dim3(256), 0, s, zpart, nblk, T, z);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   const int nblk = router_blocks(a.T);

@@ -97,22 +97,44 @@ def test_bad_config_rejected_before_launch(L, over, status):
     assert L.moe_capacity(ctypes.byref(cfg)) == status
     assert L.moe_workspace_bytes(ctypes.byref(cfg), binding.ENTRY_LAYER) == 0
     fake = 1 << 20  # never dereferenced: validation fails first
-    rc = L.moe_route(ctypes.byref(cfg), fake, fake, None, fake, fake, None, fake, fake,
+    rc = L.moe_route(ctypes.byref(cfg), fake, fake, None, fake, fake, None, fake, None, fake,
                      1 << 30, None)
     assert rc == status
 
 
-def test_drop_policy_other_than_token_order_unsupported(L):
-    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128)
-    cfg.drop_policy = 1
-    assert L.moe_capacity(ctypes.byref(cfg)) == binding.MOE_ERR_UNSUPPORTED
+def test_drop_policies(L):
+    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, drop_policy="gate_priority")
+    assert cfg.drop_policy == binding.MOE_DROP_GATE_PRIORITY
+    assert L.moe_capacity(ctypes.byref(cfg)) == 4
+    # gate priority needs T*k int32 of workspace more for dispatch and the layer
+    tok = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128)
+    for entry in (binding.ENTRY_DISPATCH, binding.ENTRY_LAYER):
+        assert L.moe_workspace_bytes(ctypes.byref(cfg), entry) >= \
+            L.moe_workspace_bytes(ctypes.byref(tok), entry) + 16 * 4
+    cfg.drop_policy = 2
+    assert L.moe_capacity(ctypes.byref(cfg)) == binding.MOE_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, drop_policy="random")
+
+
+def test_gate_priority_dispatch_requires_gates(L):
+    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, drop_policy="gate_priority")
+    ok = 1 << 20
+    ws = binding.workspace_bytes(cfg, binding.ENTRY_DISPATCH)
+    # x, ids, gates=NULL, slots, drop, load, kept, x_disp
+    rc = L.moe_dispatch(ctypes.byref(cfg), ok, ok, None, ok, None, ok, ok, ok, ok, ws, None)
+    assert rc == binding.MOE_ERR_INVALID_ARG
+    tok = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128)
+    rc = L.moe_dispatch(ctypes.byref(tok), ok, ok, ok + 2, ok, None, ok, ok, ok, ok,
+                        binding.workspace_bytes(tok, binding.ENTRY_DISPATCH), None)
+    assert rc == binding.MOE_ERR_INVALID_ARG  # misaligned optional gates
 
 
 def test_null_and_misaligned_pointers_rejected(L):
     cfg = binding.make_config(T=16, d=128, E=4, k=2, d_ff=128)
     ok = 1 << 20
     ws = binding.workspace_bytes(cfg, binding.ENTRY_ROUTE)
-    args = [ok, ok, None, ok, ok, None, ok, ok, ws, None]
+    args = [ok, ok, None, ok, ok, None, ok, None, ok, ws, None]
     for i in (0, 1, 3, 4, 6):  # x, w_router, ids, gates, aux_loss
         a = list(args)
         a[i] = None
@@ -120,12 +142,15 @@ def test_null_and_misaligned_pointers_rejected(L):
     a = list(args)
     a[0] = ok + 2  # x not 16-byte aligned
     assert L.moe_route(ctypes.byref(cfg), *a) == binding.MOE_ERR_INVALID_ARG
+    a = list(args)
+    a[7] = ok + 2  # z_loss misaligned
+    assert L.moe_route(ctypes.byref(cfg), *a) == binding.MOE_ERR_INVALID_ARG
     # workspace missing or too small
     a = list(args)
-    a[7] = None
+    a[8] = None
     assert L.moe_route(ctypes.byref(cfg), *a) == binding.MOE_ERR_WORKSPACE
     a = list(args)
-    a[8] = ws - 1
+    a[9] = ws - 1
     assert L.moe_route(ctypes.byref(cfg), *a) == binding.MOE_ERR_WORKSPACE
     # int8 scales given for plain weights
     rc = L.moe_expert_ffn(ctypes.byref(cfg), ok, ok, ok, ok, ok, None, ok, ok, 1 << 40, None)
