@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--drop-policy", default="token_order", choices=["token_order", "gate_priority"])
+    p.add_argument("--z-loss", action="store_true", help="also compute the router z-loss")
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
@@ -267,9 +269,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = synth.make_inputs(wl, seed=args.seed, device=dev)
-    cfg = binding.config_of(wl, overlap_dense=not args.serial)
+    cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy)
     C = binding.capacity(cfg)
-    out = binding.alloc_outputs(cfg, dev)
+    out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss)
     ws = binding.alloc_workspace(cfg, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -351,6 +353,7 @@ def main():
                    "capacity_factor": wl.capacity_factor, "expert_weights": wl.wfmt,
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
+                   "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":

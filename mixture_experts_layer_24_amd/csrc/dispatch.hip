@@ -204,22 +204,52 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
   }
 }
 
-// Gate-priority capacity: within expert e, assignment p (token-order
+// Gate-priority capacity.  Within expert e, assignment p (token-order
 // position) has rank = #{q in e : gate_q > gate_p, or gate_q == gate_p and
-// q < p}; it is kept, with slot = rank, iff rank < C.  Blocks take 256
-// consecutive positions of one expert (expert tiles laid end to end) and
-// compare them with the expert's whole segment, 256 gates at a time through
-// LDS.  Work per expert grows as load^2; exact and deterministic.
-__global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, const float *gates,
-                                                        const int32_t *load, int E, int64_t C,
-                                                        int32_t *slots, uint8_t *drop) {
-  __shared__ int ebase[257], tbase[257];
-  __shared__ int wtot[2][4];
-  __shared__ float cg[256];
+// q < p}; it is kept, with slot = rank, iff rank < C.  Two steps:
+//  select_gate_kernel (one block per expert with load > C): radix-selects
+//    the C-th largest gate, keeps the assignments with a larger gate and the
+//    first ones in token order with an equal gate, drops the rest, and
+//    compacts the kept ones (still in token order) to the front of the
+//    expert's segment;
+//  rank_gate_kernel: ranks each kept assignment among the expert's
+//    min(load, C) kept ones (256 per block, the list through LDS).
+// Exact and deterministic; about load + min(load, C)^2 comparisons per
+// expert.  Gates compare as floats (-0 equals +0); they must be finite.
+
+// monotone unsigned key of a float (-0 mapped to +0)
+__device__ __forceinline__ uint32_t gate_key(float g) {
+  uint32_t b = __float_as_uint(g);
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// exclusive count of `f` over the block's threads in order, and the total
+__device__ __forceinline__ int block_excl_count(bool f, int *wsum, int &total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint64_t m = __ballot(f);
+  const int in = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    if (w < wave) off += wsum[w];
+    total += wsum[w];
+  }
+  __syncthreads();
+  return off + in;
+}
+
+// exclusive prefix over experts of load[] (and of min(load, C) tiles) into
+// LDS; 256 threads, E <= 256
+__device__ __forceinline__ void expert_prefix(const int32_t *load, int E, int64_t C, int *ebase,
+                                              int *tbase, int (*wtot)[4]) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  // exclusive prefixes over experts of load and of 256-position tiles
   const int L = tid < E ? load[tid] : 0;
-  const int nt = (L + 255) / 256;
+  const int K = (int64_t)L < C ? L : (int)C;
+  const int nt = (K + 255) / 256;
   int incl = L, inct = nt;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -246,10 +276,85 @@ __global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, cons
     tbase[256] = bt + inct;
   }
   __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void select_gate_kernel(int32_t *seg, const float *gates,
+                                                          const int32_t *load, int E, int64_t C,
+                                                          int32_t *slots, uint8_t *drop) {
+  __shared__ int ebase[257], tbase[257];
+  __shared__ int wtot[2][4], wsum[4];
+  __shared__ int hist[256];
+  __shared__ int sel_bucket, sel_rem;
+  const int tid = threadIdx.x, e = blockIdx.x;
+  expert_prefix(load, E, C, ebase, tbase, wtot);
+  const int L = load[e];
+  if ((int64_t)L <= C) return;  // every assignment kept; the segment is the list
+  int32_t *sg = seg + ebase[e];
+  // radix select, 8 bits at a time from the top: the key of the C-th largest
+  uint32_t prefix = 0, pmask = 0;
+  int rem = (int)C;  // rank sought among the candidates (1 = largest)
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < L; i += 256) {
+      const uint32_t k = gate_key(gates[sg[i]]);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, b = 255;
+      for (; b > 0; b--) {
+        if (cum + hist[b] >= rem) break;
+        cum += hist[b];
+      }
+      sel_bucket = b;
+      sel_rem = rem - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel_bucket << shift;
+    pmask |= 0xFFu << shift;
+    rem = sel_rem;
+  }
+  // keep key > prefix, and the first `rem` (token order) with key == prefix;
+  // compact the kept to the front of the segment, in place (each chunk is
+  // read before any of it is overwritten; writes never pass the read point)
+  int carry_eq = 0, carry_k = 0;
+  for (int c0 = 0; c0 < L; c0 += 256) {
+    const int i = c0 + tid;
+    const bool valid = i < L;
+    const int32_t a = valid ? sg[i] : 0;
+    const uint32_t k = valid ? gate_key(gates[a]) : 0u;
+    const bool gt = valid && k > prefix, eq = valid && k == prefix;
+    int n_eq, n_keep;
+    const int eq_before = carry_eq + block_excl_count(eq, wsum, n_eq);
+    const bool keep = gt || (eq && eq_before < rem);
+    const int kidx = carry_k + block_excl_count(keep, wsum, n_keep);
+    if (valid) {
+      if (keep) {
+        sg[kidx] = a;
+      } else {
+        slots[a] = -1;
+        if (drop) drop[a] = 1;
+      }
+    }
+    carry_eq += n_eq;
+    carry_k += n_keep;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, const float *gates,
+                                                        const int32_t *load, int E, int64_t C,
+                                                        int32_t *slots, uint8_t *drop) {
+  __shared__ int ebase[257], tbase[257];
+  __shared__ int wtot[2][4];
+  __shared__ float cg[256];
+  const int tid = threadIdx.x;
+  expert_prefix(load, E, C, ebase, tbase, wtot);
   const int b = blockIdx.x;
   if (b >= tbase[256]) return;
-  // expert of this block: the last e with tbase[e] <= b (tiles of empty
-  // experts have zero length, so that e has load > 0)
+  // expert of this block: the last e with tbase[e] <= b (experts without
+  // kept assignments have no tiles, so that e has some)
   int lo = 0, hi = E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -257,27 +362,26 @@ __global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, cons
     else hi = mid - 1;
   }
   const int e = lo;
-  const int Le = load[e];
+  const int K = (int64_t)load[e] < C ? load[e] : (int)C;
   const int p = (b - tbase[e]) * 256 + tid;
   const int32_t *sg = seg + ebase[e];
-  const float g = p < Le ? gates[sg[p]] : 0.f;
+  const float g = p < K ? gates[sg[p]] : 0.f;
   int rank = 0;
-  for (int c0 = 0; c0 < Le; c0 += 256) {
+  for (int c0 = 0; c0 < K; c0 += 256) {
     __syncthreads();
     const int q = c0 + tid;
-    cg[tid] = q < Le ? gates[sg[q]] : 0.f;
+    cg[tid] = q < K ? gates[sg[q]] : 0.f;
     __syncthreads();
-    const int n = Le - c0 < 256 ? Le - c0 : 256;
+    const int n = K - c0 < 256 ? K - c0 : 256;
     for (int j = 0; j < n; j++) {
       const float h = cg[j];
       rank += (h > g || (h == g && c0 + j < p)) ? 1 : 0;
     }
   }
-  if (p < Le) {
+  if (p < K) {
     const int32_t a = sg[p];
-    const bool keep = (int64_t)rank < C;
-    slots[a] = keep ? rank : -1;
-    if (drop) drop[a] = keep ? 0 : 1;
+    slots[a] = rank;
+    if (drop) drop[a] = 0;
   }
 }
 
@@ -332,7 +436,9 @@ hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_
   else if (aux)
     return launch_aux_sum(aux_term, E, aux_alpha, aux, s);
   if (seg && T > 0) {
-    // tiles of 256 positions, at most T*k/256 + E of them
+    MOE_LAUNCH("select_gate", select_gate_kernel, dim3(E), dim3(256), 0, s, seg, gates, load, E, C,
+               slots, drop);
+    // tiles of 256 kept positions, at most T*k/256 + E of them
     const int64_t tiles = (T * k + 255) / 256 + E;
     MOE_LAUNCH("rank_gate", rank_gate_kernel, dim3((unsigned)tiles), dim3(256), 0, s, seg, gates,
                load, E, C, slots, drop);

@@ -163,3 +163,43 @@ def test_gate_priority_layer(wl):
         for t, j in zip(*np.nonzero(mask)):
             got[t, j] = yd[ids[t, j], rep["slots"][t, j]]
         check_close("y_disp", got[mask], rows[mask], TAU[wl.act])
+
+
+@pytest.mark.parametrize("name", ["prmoe128_1p3b", "skewed_top2_int8"])
+def test_full_size_zloss_and_gate_priority(name):
+    # router inputs of the full-size workload (the expert widths do not enter)
+    wl = workloads.WORKLOADS[name]
+    small = wl.replace(d_ff=128, d_ff_dense=128 if wl.pr_moe else 0, wfmt="plain")
+    print(f"[full_size_gp] {name}", flush=True)
+    inp = synth.make_inputs(small, seed=0, device=DEV)
+    ids, gates, logits, aux, zl = _route(wl, inp)
+    x = inp["x"].cpu()
+    b = None if inp["b_router"] is None else inp["b_router"].cpu()
+    r = oracle.route(x, inp["w_router"].cpu(), wl.k, bias=b, normalize=wl.normalize_topk)
+    bad, _ = check_ids(ids, r["ids"], r["logits"], wl.k)
+    assert len(bad) == 0
+    assert float(zl.item()) == pytest.approx(oracle.z_loss(r["logits"]), rel=2e-5)
+    cfg = binding.config_of(wl, drop_policy="gate_priority")
+    C = binding.capacity(cfg)
+    T, E, k, d = wl.T, wl.E, wl.k, wl.d
+    slots = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    drop = torch.empty(T, k, dtype=torch.uint8, device=DEV)
+    load = torch.empty(E, dtype=torch.int32, device=DEV)
+    kept = torch.empty(E, dtype=torch.int32, device=DEV)
+    xd = torch.empty((E, C, d), dtype=torch.bfloat16, device=DEV)
+    binding.moe_dispatch(cfg, inp["x"], ids, slots, drop, load, kept, xd,
+                         binding.alloc_workspace(cfg, binding.ENTRY_DISPATCH), gates=gates)
+    torch.cuda.synchronize()
+    rep = oracle.dispatch(to_np(ids), E, C, gates=to_np(gates).astype(np.float64),
+                          policy=oracle.DROP_GATE_PRIORITY)
+    assert np.array_equal(to_np(slots), rep["slots"])
+    assert np.array_equal(to_np(drop), rep["drop"])
+    assert np.array_equal(to_np(load), rep["load"])
+    assert np.array_equal(to_np(kept), rep["kept"])
+    # sampled rows of the expert-major buffer
+    rng = np.random.default_rng(1)
+    kt = np.argwhere(rep["slots"] >= 0)
+    for t, j in kt[rng.choice(len(kt), size=min(64, len(kt)), replace=False)]:
+        assert torch.equal(xd[int(ids[t, j]), int(rep["slots"][t, j])].cpu(), x[t])
+    del inp, xd
+    torch.cuda.empty_cache()
