@@ -184,11 +184,18 @@ def cpu_baseline(wl, inp, target_s):
             oracle.ffn_rows(x[list(toks)], *dense_w)
         return time.perf_counter() - t1
 
-    probe = order[:16]
-    t_probe = max(ffn_tokens(probe), 1e-3)
-    n = int(min(wl.T, max(16, (target_s - t_route) / t_probe * len(probe))))
-    sample = order[:n]
-    t_ffn = ffn_tokens(sample)
+    # grow the sample in rounds sized from the rate measured so far, until it
+    # has used about the time budget (small rounds parallelise worse, so the
+    # first estimate is low)
+    budget = max(target_s - t_route, 1.0)
+    n, t_ffn = 0, 0.0
+    step = 64
+    while n < wl.T and t_ffn < 0.8 * budget:
+        m = int(min(wl.T - n, max(16, step)))
+        t_ffn += ffn_tokens(order[n:n + m])
+        n += m
+        rate = t_ffn / n
+        step = (budget - t_ffn) / max(rate, 1e-9)
     t_total = t_route + t_ffn * (wl.T / n)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
