@@ -35,7 +35,7 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, F64 = 0, 1, 2, 3
 DROP_TOKEN_ORDER, DROP_GATE_PRIORITY = 0, 1
 
 
@@ -75,6 +75,10 @@ def _load(path: str | None = None):
         lib.oracle_layer_forward.argtypes = (
             [i64] * 6 + [dbl, i64] + [i32] * 4 + [dbl, vp, i32, vp, vp, vp, vp, i32, vp, vp,
                                                   vp, vp] + [vp] * 13)
+        lib.oracle_layer_backward.restype = i32
+        lib.oracle_layer_backward.argtypes = (
+            [i64] * 5 + [i64, dbl, i64] + [i32] * 4 + [dbl, vp, i32] + [vp] * 6 +
+            [vp, dbl, dbl] + [vp] * 7)
         lib.oracle_z_loss.restype = dbl
         lib.oracle_z_loss.argtypes = [i64, i64, vp]
         lib.oracle_quantize_sym_int8.restype = i32
@@ -106,8 +110,7 @@ def _np(a):
     if a.dtype == np.int8:
         return a, I8
     if a.dtype == np.float64:
-        raise TypeError("the oracle takes the device formats (f32, bf16, int8), "
-                        "not float64 inputs")
+        return a, F64
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -275,4 +278,44 @@ def layer_forward(x, w_router, w1, w2, *, k: int, capacity_factor: float,
         raise ValueError("oracle_layer_forward rejected its arguments")
     out["aux"] = float(out["aux"][0])
     out["capacity"] = capacity(T, E, k, capacity_factor, capacity_override)
+    return out
+
+
+def layer_backward(x, w_router, w1, w2, dy, *, k: int, capacity_factor: float,
+                   capacity_override: int = 0, bias=None, wm1=None, wm2=None,
+                   normalize: bool = True, pr_moe: bool = False, add_skip: bool = True,
+                   policy: int = DROP_TOKEN_ORDER, alpha: float = 1.0, g_aux: float = 0.0,
+                   g_z: float = 0.0):
+    """Gradients of <dy, y> + g_aux * aux + g_z * z_loss with respect to x and
+    every weight (plain weights in the activation format); returns a dict."""
+    xa, xf = _np(x)
+    wra, wrf = _np(w_router)
+    w1a, f1 = _np(w1)
+    w2a, f2 = _np(w2)
+    assert wrf == xf and f1 == xf and f2 == xf, "the backward takes one format"
+    T, D = xa.shape
+    E, F = w1a.shape[0], w1a.shape[1]
+    Fd = 0
+    m1 = m2 = None
+    if pr_moe:
+        m1, fm1 = _np(wm1)
+        m2, fm2 = _np(wm2)
+        assert fm1 == xf and fm2 == xf
+        Fd = m1.shape[0]
+    b = None if bias is None else np.ascontiguousarray(_np(bias)[0], dtype=np.float32)
+    g = np.ascontiguousarray(np.asarray(dy, dtype=np.float64).reshape(T, D))
+    out = dict(dx=np.zeros((T, D)), dw_router=np.zeros((E, D)), db_router=np.zeros(E),
+               dw1=np.zeros((E, F, D)), dw2=np.zeros((E, D, F)),
+               dwm1=np.zeros((max(Fd, 1), D)), dwm2=np.zeros((D, max(Fd, 1))))
+    rc = _load().oracle_layer_backward(
+        T, D, E, k, F, Fd, float(capacity_factor), int(capacity_override), int(normalize),
+        int(pr_moe), int(add_skip), int(policy), float(alpha), xa.ctypes.data, xf,
+        wra.ctypes.data, _p(b), w1a.ctypes.data, w2a.ctypes.data, _p(m1), _p(m2),
+        g.ctypes.data, float(g_aux), float(g_z), out["dx"].ctypes.data,
+        out["dw_router"].ctypes.data, out["db_router"].ctypes.data, out["dw1"].ctypes.data,
+        out["dw2"].ctypes.data, out["dwm1"].ctypes.data, out["dwm2"].ctypes.data)
+    if rc:
+        raise ValueError("oracle_layer_backward rejected its arguments")
+    if not pr_moe:
+        out["dwm1"] = out["dwm2"] = None
     return out

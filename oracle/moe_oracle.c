@@ -38,13 +38,15 @@
  *   OR_BF16 : bfloat16 bit patterns (uint16), the upper half of a binary32
  *   OR_I8   : signed 8-bit codes, with one float32 scale per 128 consecutive
  *             input-dimension elements of each output row (symmetric int8)
+ *   OR_F64  : IEEE binary64 (lets the finite-difference checks of the
+ *             backward perturb inputs by tiny steps)
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_F64 = 3 };
 enum { OR_DROP_TOKEN_ORDER = 0, OR_DROP_GATE_PRIORITY = 1 };
 
 #define OR_GROUP 128
@@ -52,6 +54,7 @@ enum { OR_DROP_TOKEN_ORDER = 0, OR_DROP_GATE_PRIORITY = 1 };
 /* value of element i of an array in one of the formats above */
 static double elem(const void *p, int fmt, int64_t i) {
   if (fmt == OR_F32) return (double)((const float *)p)[i];
+  if (fmt == OR_F64) return ((const double *)p)[i];
   if (fmt == OR_BF16) {
     uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16; /* [SRV] 1.2.1 */
     float f;
@@ -342,7 +345,7 @@ int oracle_layer_forward(int64_t T, int64_t D, int64_t E, int64_t k,
   rc = oracle_dispatch(T, E, k, C, ids, gates, policy, slots, drop, load, kept);
   if (rc) return rc;
 
-  size_t ws = (w_fmt == OR_F32) ? 4 : (w_fmt == OR_BF16 ? 2 : 1);
+  size_t ws = (w_fmt == OR_F64) ? 8 : (w_fmt == OR_F32) ? 4 : (w_fmt == OR_BF16 ? 2 : 1);
   if (w_fmt == OR_I8 && (!s1 || !s2 || D % OR_GROUP || F % OR_GROUP)) return -1;
   memset(expert_out, 0, (size_t)(T * k * D) * sizeof(double));
 #pragma omp parallel
@@ -433,4 +436,200 @@ int oracle_quantize_sym_int8(int64_t N, int64_t K, const double *w,
       }
     }
   return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer: the gradients of the scalar
+ *   L = sum_{t,o} dy[t,o] y[t,o] + g_aux * aux + g_z * z
+ * (z the router z-loss above) with respect to x, W_r, b, W1, W2, Wm1, Wm2,
+ * by the chain rule through the forward stages, written out directly.
+ *  - A kept assignment (t, j) adds g_tj * E_e(x_t) to y_t, so
+ *      dg_tj = <dy_t, E_e(x_t)>   and the expert sees d(out) = g_tj dy_t;
+ *    a dropped assignment adds nothing and gets no gradient ([DvS] overflow:
+ *    the token skips the expert).
+ *  - An FFN out = W2 GELU(W1 x) (the experts, and the PR-MoE dense MLP with
+ *    d(out) = dy_t): with a = W1 x and h = GELU(a),
+ *      dh = W2^T d(out),  da = dh * GELU'(a),  GELU'(a) = Phi(a) + a phi(a),
+ *      dx += W1^T da,  dW2 += d(out) h^T,  dW1 += da x^T.
+ *  - Gates from probabilities: g_j = p_{e_j} (k = 1, or no renormalisation);
+ *    renormalised ([SRV] 1.1.1.1) g_j = p_{e_j} / S with S the sum of the k
+ *    chosen p, so  dp_{e_i} += (dg_i - sum_j dg_j g_j) / S.
+ *  - aux = alpha E sum_e f_e Q_e with Q_e = (1/T) sum_t p_e(t) ([SRV]
+ *    1.1.4.1); f counts argmax decisions and is piecewise constant:
+ *      dp_e(t) += g_aux alpha E f_e / T.
+ *  - Softmax: dlogit_e = p_e (dp_e - sum_i p_i dp_i).
+ *  - z = (1/T) sum_t lse_t^2: dlogit_e(t) += g_z (2/T) lse_t p_e(t).
+ *  - logits = W_r x + b: dx += W_r^T dlogit, dW_r += dlogit x^T, db += dlogit.
+ * The discrete decisions (top-k, capacity) are held where the forward put
+ * them (their derivative is zero almost everywhere).  Plain weights (x_fmt)
+ * only.  Outputs are doubles: dx [T, D], dwr [E, D], db [E] (may be NULL),
+ * dw1 [E, F, D], dw2 [E, D, F], dwm1 [Fd, D], dwm2 [D, Fd] (pr_moe only).
+ * ---------------------------------------------------------------------- */
+static double gelu_grad(double z) {
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * inv_sqrt_2pi * exp(-0.5 * z * z);
+}
+
+/* one FFN row backward; accumulates into dx_row, dw1 [F, D], dw2 [D, F] */
+static void ffn_row_backward(int64_t D, int64_t F, const void *x, int fmt, int64_t row,
+                             const void *w1, const void *w2, const double *dout,
+                             double *a, double *dh, double *dx_row, double *dw1,
+                             double *dw2) {
+  for (int64_t f = 0; f < F; f++) {
+    double s = 0.0;
+    for (int64_t i = 0; i < D; i++) s += elem(w1, fmt, f * D + i) * elem(x, fmt, row * D + i);
+    a[f] = s;
+  }
+  for (int64_t f = 0; f < F; f++) {
+    double s = 0.0;
+    for (int64_t o = 0; o < D; o++) s += elem(w2, fmt, o * F + f) * dout[o];
+    dh[f] = s * gelu_grad(a[f]); /* da */
+  }
+  for (int64_t i = 0; i < D; i++) {
+    double s = 0.0;
+    for (int64_t f = 0; f < F; f++) s += elem(w1, fmt, f * D + i) * dh[f];
+    dx_row[i] += s;
+  }
+  for (int64_t f = 0; f < F; f++) {
+    const double hf = gelu(a[f]);
+    for (int64_t o = 0; o < D; o++) dw2[o * F + f] += dout[o] * hf;
+  }
+  for (int64_t f = 0; f < F; f++)
+    for (int64_t i = 0; i < D; i++) dw1[f * D + i] += dh[f] * elem(x, fmt, row * D + i);
+}
+
+int oracle_layer_backward(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                          int64_t Fd, double cf, int64_t cap_override, int normalize,
+                          int pr_moe, int add_skip, int policy, double alpha,
+                          const void *x, int fmt, const void *wr, const float *bias,
+                          const void *w1, const void *w2, const void *wm1, const void *wm2,
+                          const double *dy, double g_aux, double g_z, double *dx,
+                          double *dwr, double *db, double *dw1, double *dw2,
+                          double *dwm1, double *dwm2) {
+  if (fmt == OR_I8) return -1;
+  const int64_t TE = T * E > 0 ? T * E : 1, Tk = T * k > 0 ? T * k : 1;
+  const int64_t TD = T * D > 0 ? T * D : 1;
+  double *logits = (double *)malloc((size_t)TE * sizeof(double));
+  double *probs = (double *)malloc((size_t)TE * sizeof(double));
+  int32_t *ids = (int32_t *)malloc((size_t)Tk * sizeof(int32_t));
+  double *gates = (double *)malloc((size_t)Tk * sizeof(double));
+  int32_t *slots = (int32_t *)malloc((size_t)Tk * sizeof(int32_t));
+  uint8_t *drop = (uint8_t *)malloc((size_t)Tk);
+  int32_t *load = (int32_t *)malloc((size_t)(E > 0 ? E : 1) * sizeof(int32_t));
+  int32_t *kept = (int32_t *)malloc((size_t)(E > 0 ? E : 1) * sizeof(int32_t));
+  double *eo = (double *)malloc((size_t)(Tk * D) * sizeof(double));
+  double *m = (double *)malloc((size_t)TD * sizeof(double));
+  double *dense = (double *)malloc((size_t)TD * sizeof(double));
+  double *y = (double *)malloc((size_t)TD * sizeof(double));
+  double *f = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+  double *dxa = (double *)calloc((size_t)(Tk * D), sizeof(double)); /* per assignment */
+  double *dlog = (double *)calloc((size_t)TE, sizeof(double));
+  double aux = 0.0;
+  int rc = oracle_layer_forward(T, D, E, k, F, Fd, cf, cap_override, normalize, pr_moe,
+                                add_skip, policy, alpha, x, fmt, wr, bias, w1, w2, fmt, NULL,
+                                NULL, wm1, wm2, logits, probs, ids, gates, slots, drop, load,
+                                kept, eo, m, dense, y, &aux);
+  if (rc) goto done;
+  oracle_aux_loss(T, E, k, ids, probs, alpha, f, NULL);
+  const size_t es = fmt == OR_F64 ? 8 : (fmt == OR_F32 ? 4 : 2);
+
+  /* experts: each expert's kept assignments in token order */
+  memset(dw1, 0, (size_t)(E * F * D) * sizeof(double));
+  memset(dw2, 0, (size_t)(E * D * F) * sizeof(double));
+#pragma omp parallel
+  {
+    double *a = (double *)malloc((size_t)(F > 0 ? F : 1) * sizeof(double));
+    double *dh = (double *)malloc((size_t)(F > 0 ? F : 1) * sizeof(double));
+    double *dout = (double *)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t e = 0; e < E; e++) {
+      const void *w1e = (const char *)w1 + (size_t)(e * F * D) * es;
+      const void *w2e = (const char *)w2 + (size_t)(e * D * F) * es;
+      for (int64_t q = 0; q < T * k; q++) {
+        if (ids[q] != e || slots[q] < 0) continue;
+        const int64_t t = q / k;
+        for (int64_t o = 0; o < D; o++) dout[o] = gates[q] * dy[t * D + o];
+        ffn_row_backward(D, F, x, fmt, t, w1e, w2e, dout, a, dh, dxa + q * D,
+                         dw1 + e * F * D, dw2 + e * D * F);
+      }
+    }
+    free(a);
+    free(dh);
+    free(dout);
+  }
+
+  /* dense MLP over every token */
+  if (pr_moe) {
+    memset(dwm1, 0, (size_t)(Fd * D) * sizeof(double));
+    memset(dwm2, 0, (size_t)(D * Fd) * sizeof(double));
+    double *a = (double *)malloc((size_t)(Fd > 0 ? Fd : 1) * sizeof(double));
+    double *dh = (double *)malloc((size_t)(Fd > 0 ? Fd : 1) * sizeof(double));
+    memset(dx, 0, (size_t)TD * sizeof(double));
+    for (int64_t t = 0; t < T; t++)
+      ffn_row_backward(D, Fd, x, fmt, t, wm1, wm2, dy + t * D, a, dh, dx + t * D, dwm1, dwm2);
+    free(a);
+    free(dh);
+  } else {
+    memset(dx, 0, (size_t)TD * sizeof(double));
+  }
+
+  /* router: gates -> probabilities -> logits */
+#pragma omp parallel
+  {
+    double *dp = (double *)malloc((size_t)(E > 0 ? E : 1) * sizeof(double));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+      const double *p = probs + t * E, *l = logits + t * E;
+      for (int64_t e = 0; e < E; e++) dp[e] = g_aux * alpha * (double)E * f[e] / (double)T;
+      double dg[64], S = 0.0, sdg = 0.0;
+      for (int64_t j = 0; j < k; j++) {
+        const int64_t q = t * k + j;
+        double v = 0.0;
+        if (slots[q] >= 0)
+          for (int64_t o = 0; o < D; o++) v += dy[t * D + o] * eo[q * D + o];
+        dg[j] = v;
+        S += p[ids[q]];
+        sdg += v * gates[q];
+      }
+      const int renorm = k >= 2 && normalize;
+      for (int64_t j = 0; j < k; j++)
+        dp[ids[t * k + j]] += renorm ? (dg[j] - sdg) / S : dg[j];
+      double pdp = 0.0;
+      for (int64_t e = 0; e < E; e++) pdp += p[e] * dp[e];
+      double mx = l[0];
+      for (int64_t e = 1; e < E; e++)
+        if (l[e] > mx) mx = l[e];
+      double se = 0.0;
+      for (int64_t e = 0; e < E; e++) se += exp(l[e] - mx);
+      const double lse = mx + log(se);
+      for (int64_t e = 0; e < E; e++)
+        dlog[t * E + e] = p[e] * (dp[e] - pdp) + g_z * 2.0 / (double)T * lse * p[e];
+    }
+    free(dp);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t i = 0; i < D; i++) {
+      double s = add_skip ? dy[t * D + i] : 0.0;
+      for (int64_t j = 0; j < k; j++) s += dxa[(t * k + j) * D + i];
+      for (int64_t e = 0; e < E; e++) s += dlog[t * E + e] * elem(wr, fmt, e * D + i);
+      dx[t * D + i] += s;
+    }
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < E; e++) {
+    for (int64_t i = 0; i < D; i++) {
+      double s = 0.0;
+      for (int64_t t = 0; t < T; t++) s += dlog[t * E + e] * elem(x, fmt, t * D + i);
+      dwr[e * D + i] = s;
+    }
+    if (db) {
+      double s = 0.0;
+      for (int64_t t = 0; t < T; t++) s += dlog[t * E + e];
+      db[e] = s;
+    }
+  }
+done:
+  free(logits); free(probs); free(ids); free(gates); free(slots); free(drop); free(load);
+  free(kept); free(eo); free(m); free(dense); free(y); free(f); free(dxa); free(dlog);
+  return rc;
 }

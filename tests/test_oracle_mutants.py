@@ -39,6 +39,19 @@ MUTANTS = {
     "dense_mlp_dropped": (" + dense[t * D + o];", ";"),
     "zloss_not_squared": ("acc += lz * lz;", "acc += lz;"),
     "quant_round_toward_zero": ("nearbyint(r[i] / s)", "trunc(r[i] / s)"),
+    # backward
+    "bwd_gelu_grad_missing_term": (
+        "return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * inv_sqrt_2pi * exp(-0.5 * z * z);",
+        "return 0.5 * (1.0 + erf(z / sqrt(2.0)));"),
+    "bwd_renorm_without_correction": ("renorm ? (dg[j] - sdg) / S : dg[j]",
+                                      "renorm ? dg[j] / S : dg[j]"),
+    "bwd_dropped_get_gradient": ("if (ids[q] != e || slots[q] < 0) continue;",
+                                 "if (ids[q] != e) continue;"),
+    "bwd_aux_gradient_dropped": (
+        "dp[e] = g_aux * alpha * (double)E * f[e] / (double)T;", "dp[e] = 0.0;"),
+    "bwd_softmax_jacobian_sign": ("p[e] * (dp[e] - pdp)", "p[e] * (dp[e] + pdp)"),
+    "bwd_zloss_grad_halved": ("g_z * 2.0 / (double)T", "g_z * 1.0 / (double)T"),
+    "bwd_dw2_uses_preactivation": ("const double hf = gelu(a[f]);", "const double hf = a[f];"),
 }
 
 
@@ -55,6 +68,7 @@ def test_pins_kill_mutant(name, tmp_path):
     r = subprocess.run(
         [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-         os.path.join(ROOT, "tests", "test_oracle_bruteforce.py")],
+         os.path.join(ROOT, "tests", "test_oracle_bruteforce.py"),
+         os.path.join(ROOT, "tests", "test_oracle_backward.py")],
         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
