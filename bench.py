@@ -62,6 +62,8 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--drop-policy", default="token_order", choices=["token_order", "gate_priority"])
     p.add_argument("--z-loss", action="store_true", help="also compute the router z-loss")
+    p.add_argument("--backward", action="store_true",
+                   help="time the layer backward (after one forward) instead of the forward")
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
@@ -103,6 +105,23 @@ def kernel_work(wl, kept, cfg_C):
         out["dense_gemm2"] = dict(bytes=(T * F + d * F + T * d) * sa, flops=2.0 * T * d * F)
     out["router"] = dict(bytes=(wl.T * wl.d + wl.E * wl.d) * sa + wl.T * wl.k * 8,
                          flops=2.0 * wl.T * wl.d * wl.E)
+    # backward GEMMs (bwd_*): the expert products over the kept rows read the
+    # active experts' weights (dZ, dX) or write their gradients (dW1, dW2)
+    K = n_kept
+    out["bwd_expert_z"] = dict(bytes=wbytes + K * (wl.d + wl.d_ff) * sa,
+                               flops=2.0 * K * wl.d * wl.d_ff)
+    out["bwd_expert_dz"] = dict(bytes=wbytes + K * (wl.d + 2 * wl.d_ff) * sa,
+                                flops=2.0 * K * wl.d * wl.d_ff)
+    out["bwd_expert_dx"] = dict(bytes=wbytes + K * (wl.d_ff + wl.d) * sa,
+                                flops=2.0 * K * wl.d * wl.d_ff)
+    out["bwd_expert_dw"] = dict(bytes=wl.E * wl.d * wl.d_ff * sa + K * (wl.d + wl.d_ff) * sa,
+                                flops=2.0 * K * wl.d * wl.d_ff)
+    if wl.pr_moe:
+        T, d, F = wl.T, wl.d, wl.d_ff_dense
+        for c in ("bwd_dense_z", "bwd_dense_dz", "bwd_dense_dx", "bwd_dense_dw"):
+            out[c] = dict(bytes=(T * d + F * d + T * F) * sa, flops=2.0 * T * d * F)
+    out["bwd_router"] = dict(bytes=(wl.T * wl.d + wl.E * wl.d + wl.T * wl.E) * sa,
+                             flops=2.0 * wl.T * wl.d * wl.E)
     out["gather"] = dict(bytes=2.0 * n_kept * wl.d * sa, flops=0.0)
     out["combine"] = dict(bytes=(n_kept + wl.T * (1 + int(wl.add_skip) + int(wl.pr_moe)))
                           * wl.d * sa, flops=2.0 * n_kept * wl.d)
@@ -114,6 +133,11 @@ def classify(name: str) -> str | None:
     GEMMs, the kernel's own name otherwise)."""
     for prefix, cls in (("expert_ffn1", "expert_gemm1"), ("expert_ffn2", "expert_gemm2"),
                         ("dense_mlp1", "dense_gemm1"), ("dense_mlp2", "dense_gemm2"),
+                        ("bwd_expert_z", "bwd_expert_z"), ("bwd_expert_dz", "bwd_expert_dz"),
+                        ("bwd_expert_dx", "bwd_expert_dx"), ("bwd_expert_dw", "bwd_expert_dw"),
+                        ("bwd_dense_z", "bwd_dense_z"), ("bwd_dense_dz", "bwd_dense_dz"),
+                        ("bwd_dense_dx", "bwd_dense_dx"), ("bwd_dense_dw", "bwd_dense_dw"),
+                        ("bwd_router_", "bwd_router"),
                         ("router", "router"), ("gather", "gather"), ("combine", "combine")):
         if name.startswith(prefix):
             return cls
@@ -278,12 +302,23 @@ def main():
     inp = synth.make_inputs(wl, seed=args.seed, device=dev)
     cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy)
     C = binding.capacity(cfg)
-    out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss)
+    out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss, logits=args.backward,
+                                x_disp=args.backward, y_disp=args.backward)
     ws = binding.alloc_workspace(cfg, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
         binding.moe_layer_forward(cfg, inp["x"], inp, out, ws, stream)
+
+    if args.backward:
+        step()  # the forward whose outputs the backward reads
+        dy = synth.normal((wl.T, wl.d), 1.0, args.seed + 1, "dy", dev, torch.bfloat16)
+        grads = binding.alloc_grads(cfg, dev)
+        ws_b = binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD, device=dev)
+
+        def step():  # noqa: F811
+            binding.moe_layer_backward(cfg, inp["x"], inp, out, dy, grads, ws_b, g_aux=0.01,
+                                       g_z=0.001, stream=stream)
 
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * (1 << 30))
@@ -350,7 +385,8 @@ def main():
     roof["algorithmic_flops"] = wk["flops"]
 
     res = {
-        "metric": METRIC, "value": round(wl.T * args.steps / elapsed, 1), "unit": "tokens/s",
+        "metric": METRIC if not args.backward else "MoE-layer backward tokens/s",
+        "value": round(wl.T * args.steps / elapsed, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if wl.act == "bf16" else "f32",
@@ -361,6 +397,7 @@ def main():
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
                    "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
+                   "pass": "backward" if args.backward else "forward",
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
@@ -368,7 +405,7 @@ def main():
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.backward:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(res))

@@ -84,6 +84,7 @@ extern "C" {
 #define MOE_ENTRY_EXPERT_FFN 2
 #define MOE_ENTRY_COMBINE 3
 #define MOE_ENTRY_LAYER 4
+#define MOE_ENTRY_BACKWARD 5
 
 typedef struct moe_config {
   int64_t T;          /* tokens (>= 0) */
@@ -132,6 +133,16 @@ typedef struct moe_outputs {
   void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
   float *z_loss;       /* [1] router z-loss                     optional */
 } moe_outputs;
+
+typedef struct moe_grads {
+  void *dx;          /* [T, d] act                                  required */
+  void *dw_router;   /* [E, d] act                                  required */
+  float *db_router;  /* [E] fp32                                    optional */
+  void *dw1;         /* [E, d_ff, d] act                            required */
+  void *dw2;         /* [E, d, d_ff] act                            required */
+  void *dwm1;        /* [d_ff_dense, d] act                 pr_moe: required */
+  void *dwm2;        /* [d, d_ff_dense] act                 pr_moe: required */
+} moe_grads;
 
 /* Capacity C of the configuration, or a negative MOE_ERR_* code. */
 int64_t moe_capacity(const moe_config *cfg);
@@ -202,6 +213,26 @@ int moe_combine(const moe_config *cfg, const void *y_disp,
 int moe_layer_forward(const moe_config *cfg, const void *x,
                       const moe_weights *w, moe_outputs *out, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* Backward of moe_layer_forward: the gradients of
+ *   <dy, y> + g_aux * aux_loss + g_z * z_loss
+ * with respect to x and every weight, by the chain rule through the layer
+ * ("DeepSpeed MoE and Model Compression", section DeepSpeed-MoE; a token
+ * dropped by capacity skips the expert and gets no expert gradient,
+ * "DeepSpeed-MoE vs Switch Transformer", section "expert capacity overflow";
+ * the aux loss's f counts argmax decisions and is held constant; the top-k and
+ * capacity decisions are held as the forward made them).
+ * x, w: as given to the forward.  fwd: the forward's outputs for the same
+ * cfg, x and w; expert_ids, gates, slots, logits, x_disp and y_disp are
+ * required (so the forward must have been run with caller-owned logits,
+ * x_disp and y_disp).  dy [T, d] act.
+ * Out: grads (written, not accumulated); the weight gradients are in the
+ * activation type, accumulated in fp32.  bf16 activations and plain expert
+ * weights only (MOE_ERR_UNSUPPORTED otherwise).  Workspace:
+ * moe_workspace_bytes(cfg, MOE_ENTRY_BACKWARD). */
+int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *w,
+                       const moe_outputs *fwd, const void *dy, float g_aux, float g_z,
+                       moe_grads *grads, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *moe_status_string(int status);

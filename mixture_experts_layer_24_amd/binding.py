@@ -25,10 +25,12 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_W_PLAIN, MOE_W_INT8_G128 = 0, 1
 MOE_DROP_TOKEN_ORDER = 0
 MOE_DROP_GATE_PRIORITY = 1
-ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER = range(5)
+ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY_BACKWARD = \
+    range(6)
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_mlp", "moe_combine", "moe_layer_forward",
+            "moe_layer_backward",
             "moe_status_string", "moe_profile_enable", "moe_profile_reset",
             "moe_profile_read")
 
@@ -52,6 +54,11 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_router", "b_router", "w1", "w1_scale", "w2", "w2_scale", "wm1", "wm2")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "db_router", "dw1", "dw2", "dwm1", "dwm2")]
 
 
 class Outputs(ctypes.Structure):
@@ -93,6 +100,10 @@ def lib():
             L.moe_layer_forward.restype = i32
             L.moe_layer_forward.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
                                             ctypes.POINTER(Outputs), vp, sz, vp]
+            L.moe_layer_backward.restype = i32
+            L.moe_layer_backward.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
+                                             ctypes.POINTER(Outputs), vp, ctypes.c_float,
+                                             ctypes.c_float, ctypes.POINTER(Grads), vp, sz, vp]
             L.moe_status_string.restype = ctypes.c_char_p
             L.moe_status_string.argtypes = [i32]
             L.moe_profile_enable.restype = i32
@@ -302,6 +313,56 @@ def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
 
 def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):
     """weights: dict with w_router, b_router, w1, w1_scale, w2, w2_scale, wm1, wm2."""
+    W, O = _weights_struct(cfg, weights), _outputs_struct(cfg, out)
+    wsp, wsn = _ws(ws)
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        ctypes.byref(cfg), _ptr(x, (cfg.T, cfg.d), _act_dtype(cfg), "x"), ctypes.byref(W),
+        ctypes.byref(O), wsp, wsn, _stream(stream)))
+
+
+@dataclasses.dataclass
+class LayerGrads:
+    dx: torch.Tensor
+    dw_router: torch.Tensor
+    dw1: torch.Tensor
+    dw2: torch.Tensor
+    db_router: torch.Tensor | None = None
+    dwm1: torch.Tensor | None = None
+    dwm2: torch.Tensor | None = None
+
+
+def alloc_grads(cfg: Config, device="cuda", *, db_router=True) -> LayerGrads:
+    T, d, E, F, Fd = cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.d_ff_dense
+    a = _act_dtype(cfg)
+    e = lambda *s, dt=a: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+    pr = bool(cfg.pr_moe)
+    return LayerGrads(dx=e(T, d), dw_router=e(E, d), dw1=e(E, F, d), dw2=e(E, d, F),
+                      db_router=e(E, dt=torch.float32) if db_router else None,
+                      dwm1=e(Fd, d) if pr else None, dwm2=e(d, Fd) if pr else None)
+
+
+def moe_layer_backward(cfg, x, weights: dict, fwd: LayerOutputs, dy, grads: LayerGrads, ws,
+                       g_aux: float = 0.0, g_z: float = 0.0, stream=None):
+    """Backward of moe_layer_forward (fwd: its outputs, with logits, x_disp and
+    y_disp allocated)."""
+    T, d, E, F, Fd = cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.d_ff_dense
+    a = _act_dtype(cfg)
+    pr = bool(cfg.pr_moe)
+    W, O = _weights_struct(cfg, weights), _outputs_struct(cfg, fwd)
+    G = Grads(dx=_ptr(grads.dx, (T, d), a, "dx"),
+              dw_router=_ptr(grads.dw_router, (E, d), a, "dw_router"),
+              db_router=_ptr(grads.db_router, (E,), torch.float32, "db_router", True),
+              dw1=_ptr(grads.dw1, (E, F, d), a, "dw1"), dw2=_ptr(grads.dw2, (E, d, F), a, "dw2"),
+              dwm1=_ptr(grads.dwm1, (Fd, d), a, "dwm1", not pr),
+              dwm2=_ptr(grads.dwm2, (d, Fd), a, "dwm2", not pr))
+    wsp, wsn = _ws(ws)
+    _check("moe_layer_backward", lib().moe_layer_backward(
+        ctypes.byref(cfg), _ptr(x, (T, d), a, "x"), ctypes.byref(W), ctypes.byref(O),
+        _ptr(dy, (T, d), a, "dy"), float(g_aux), float(g_z), ctypes.byref(G), wsp, wsn,
+        _stream(stream)))
+
+
+def _weights_struct(cfg, weights: dict) -> Weights:
     T, d, E, k, F, Fd = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff, cfg.d_ff_dense
     C = capacity(cfg)
     a, wd = _act_dtype(cfg), _wdtype(cfg)
@@ -318,7 +379,14 @@ def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None)
                       not q8),
         wm1=_ptr(weights.get("wm1"), (Fd, d), a, "wm1", not pr),
         wm2=_ptr(weights.get("wm2"), (d, Fd), a, "wm2", not pr))
-    O = Outputs(
+    return W
+
+
+def _outputs_struct(cfg, out: LayerOutputs) -> Outputs:
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    C = capacity(cfg)
+    a = _act_dtype(cfg)
+    return Outputs(
         y=_ptr(out.y, (T, d), a, "y"),
         expert_ids=_ptr(out.expert_ids, (T, k), torch.int32, "expert_ids"),
         gates=_ptr(out.gates, (T, k), torch.float32, "gates"),
@@ -332,10 +400,6 @@ def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None)
         y_disp=_ptr(out.y_disp, (E, C, d), a, "y_disp", True),
         dense_out=_ptr(out.dense_out, (T, d), a, "dense_out", True),
         z_loss=_ptr(out.z_loss, (1,), torch.float32, "z_loss", True))
-    wsp, wsn = _ws(ws)
-    _check("moe_layer_forward", lib().moe_layer_forward(
-        ctypes.byref(cfg), _ptr(x, (T, d), a, "x"), ctypes.byref(W), ctypes.byref(O),
-        wsp, wsn, _stream(stream)))
 
 
 # ------------------------------------------------------------------ profiling

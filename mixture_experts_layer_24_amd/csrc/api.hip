@@ -76,7 +76,11 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 struct Layout {
   size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
       total;
+  // backward
+  size_t dg, fcnt, ecount, dlog, dlog16, dY, Z, H, dZ, dX, dxr, Zd, Hd, dZd, dxd;
 };
+
+int64_t padded_experts(const moe_config *c) { return (c->E + 7) / 8 * 8; }
 
 Layout layout(const moe_config *c, int entry) {
   Layout L{};
@@ -124,6 +128,28 @@ Layout layout(const moe_config *c, int entry) {
       if (c->pr_moe) {
         L.hidden_dense = take((size_t)c->T * c->d_ff_dense * as);
         L.dense = take((size_t)c->T * c->d * as);
+      }
+      break;
+    }
+    case MOE_ENTRY_BACKWARD: {
+      const size_t TB = (size_t)c->T, ECd = (size_t)c->E * C * c->d * as;
+      const size_t ECF = (size_t)c->E * C * c->d_ff * as;
+      L.dg = take(TB * c->k * 4);
+      L.fcnt = take((size_t)c->E * 4);
+      L.ecount = take(4);
+      L.dlog = take(TB * c->E * 4);
+      L.dlog16 = take(TB * padded_experts(c) * as);
+      L.dY = take(ECd);
+      L.Z = take(ECF);
+      L.H = take(ECF);
+      L.dZ = take(ECF);
+      L.dX = take(ECd);
+      L.dxr = take(TB * c->d * as);
+      if (c->pr_moe) {
+        L.Zd = take(TB * c->d_ff_dense * as);
+        L.Hd = take(TB * c->d_ff_dense * as);
+        L.dZd = take(TB * c->d_ff_dense * as);
+        L.dxd = take(TB * c->d * as);
       }
       break;
     }
@@ -266,7 +292,7 @@ int64_t moe_capacity(const moe_config *cfg) {
 
 size_t moe_workspace_bytes(const moe_config *cfg, int entry) {
   if (check_config(cfg) != MOE_OK) return 0;
-  if (entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_LAYER) return 0;
+  if (entry < MOE_ENTRY_ROUTE || entry > MOE_ENTRY_BACKWARD) return 0;
   return layout(cfg, entry).total;
 }
 
@@ -472,6 +498,149 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
                                  cfg->add_skip ? x : nullptr, dense, out->y, T, (int)cfg->d,
                                  (int)cfg->k, capacity_of(cfg), (int)cfg->E,
                                  cfg->act_dtype == MOE_BF16, s);
+  return hip_status(e);
+}
+
+int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *w,
+                       const moe_outputs *fwd, const void *dy, float g_aux, float g_z,
+                       moe_grads *gr, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!w || !fwd || !gr) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_BF16 || cfg->expert_wfmt != MOE_W_PLAIN) return MOE_ERR_UNSUPPORTED;
+  const int64_t T = cfg->T, Tk = T * cfg->k, E = cfg->E, C = capacity_of(cfg);
+  const int64_t d = cfg->d, F = cfg->d_ff, Fd = cfg->d_ff_dense;
+  const bool pr = cfg->pr_moe != 0;
+  if (!need(x, T, 16) || !need(w->w_router, 1, 16) || !need(w->w1, 1, 16) ||
+      !need(w->w2, 1, 16) || (pr && (!need(w->wm1, 1, 16) || !need(w->wm2, 1, 16))))
+    return MOE_ERR_INVALID_ARG;
+  if (!need(fwd->expert_ids, Tk, 4) || !need(fwd->gates, Tk, 4) || !need(fwd->slots, Tk, 4) ||
+      !need(fwd->logits, T, 4) || !need(fwd->x_disp, E * C, 16) || !need(fwd->y_disp, E * C, 16) ||
+      !need(dy, T, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (!need(gr->dx, T, 16) || !need(gr->dw_router, 1, 16) || !opt(gr->db_router, 4) ||
+      !need(gr->dw1, 1, 16) || !need(gr->dw2, 1, 16) ||
+      (pr && (!need(gr->dwm1, 1, 16) || !need(gr->dwm2, 1, 16))))
+    return MOE_ERR_INVALID_ARG;
+  rc = check_ws(cfg, MOE_ENTRY_BACKWARD, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_BACKWARD);
+  hipStream_t s = (hipStream_t)stream;
+  using moe::bf16;
+  using moe::GenArgs;
+  const int Ep = (int)padded_experts(cfg);
+  float *dg = (float *)at(ws, L.dg), *dlog = (float *)at(ws, L.dlog);
+  int32_t *fcnt = (int32_t *)at(ws, L.fcnt), *ecount = (int32_t *)at(ws, L.ecount);
+  bf16 *dlog16 = (bf16 *)at(ws, L.dlog16), *dY = (bf16 *)at(ws, L.dY), *Z = (bf16 *)at(ws, L.Z);
+  bf16 *H = (bf16 *)at(ws, L.H), *dZ = (bf16 *)at(ws, L.dZ), *dX = (bf16 *)at(ws, L.dX);
+  bf16 *dxr = (bf16 *)at(ws, L.dxr);
+  const bf16 *xb = (const bf16 *)x, *dyb = (const bf16 *)dy;
+  const int32_t *ids = fwd->expert_ids, *slots = fwd->slots, *kept = fwd->kept;
+  const bf16 *xd = (const bf16 *)fwd->x_disp;
+
+  hipError_t e = moe_host::launch_bwd_gate(dyb, (const bf16 *)fwd->y_disp, ids, slots, fwd->gates,
+                                           T, (int)cfg->k, (int)d, C, (int)E, dg, dY, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_bwd_router(fwd->logits, ids, fwd->gates, dg, fcnt, T, (int)E, Ep,
+                                    (int)cfg->k, cfg->normalize_topk, cfg->aux_alpha, g_aux, g_z,
+                                    dlog, dlog16, gr->db_router, s);
+  if (e == hipSuccess) e = moe_host::launch_fill_i32(ecount, 1, (int)E, s);
+  // router: dx_r = dlogits W_r, dW_r = dlogits^T x
+  if (e == hipSuccess) {
+    GenArgs a{};
+    a.A = dlog16; a.a_m = Ep; a.a_k = 1;
+    a.B = (const bf16 *)w->w_router; a.b_n = 1; a.b_k = d; a.b_kmax = E;
+    a.C = dxr; a.c_m = d; a.M = T; a.K = Ep; a.N = (int)d; a.G = 1;
+    e = moe_host::launch_gemm_gen(a, false, true, false, "bwd_router_dx", s);
+  }
+  if (e == hipSuccess) {
+    GenArgs a{};
+    a.A = dlog16; a.a_m = 1; a.a_k = Ep; a.a_kmax = T;
+    a.B = xb; a.b_n = 1; a.b_k = d; a.b_kmax = T;
+    a.C = (bf16 *)gr->dw_router; a.c_m = d; a.mrows = ecount; a.M = Ep; a.K = T;
+    a.N = (int)d; a.G = 1;
+    e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_router_dw", s);
+  }
+  // experts
+  if (e == hipSuccess && C > 0) {
+    GemmArgs z{xd, w->w1, nullptr, Z, kept, C, (int)F, (int)d, (int)E};
+    e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_expert_z", s);
+  }
+  if (e == hipSuccess) e = moe_host::launch_gelu_map(Z, H, E * C * F, s);
+  if (e == hipSuccess && C > 0) {  // dZ = (dY W2) * GELU'(Z)
+    GenArgs a{};
+    a.A = dY; a.a_g = C * d; a.a_m = d; a.a_k = 1;
+    a.B = (const bf16 *)w->w2; a.b_g = d * F; a.b_n = 1; a.b_k = F; a.b_kmax = d;
+    a.C = dZ; a.c_g = C * F; a.c_m = F; a.Z = Z; a.mrows = kept; a.M = C; a.K = d;
+    a.N = (int)F; a.G = (int)E;
+    e = moe_host::launch_gemm_gen(a, false, true, true, "bwd_expert_dz", s);
+  }
+  if (e == hipSuccess && C > 0) {  // dX = dZ W1
+    GenArgs a{};
+    a.A = dZ; a.a_g = C * F; a.a_m = F; a.a_k = 1;
+    a.B = (const bf16 *)w->w1; a.b_g = F * d; a.b_n = 1; a.b_k = d; a.b_kmax = F;
+    a.C = dX; a.c_g = C * d; a.c_m = d; a.mrows = kept; a.M = C; a.K = F; a.N = (int)d;
+    a.G = (int)E;
+    e = moe_host::launch_gemm_gen(a, false, true, false, "bwd_expert_dx", s);
+  }
+  if (e == hipSuccess) {  // dW2 = dY^T H  (K = kept rows of the expert)
+    GenArgs a{};
+    a.A = dY; a.a_g = C * d; a.a_m = 1; a.a_k = d; a.a_kmax = C;
+    a.B = H; a.b_g = C * F; a.b_n = 1; a.b_k = F; a.b_kmax = C;
+    a.C = (bf16 *)gr->dw2; a.c_g = d * F; a.c_m = F; a.M = d; a.krows = kept; a.K = C;
+    a.N = (int)F; a.G = (int)E;
+    e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_expert_dw2", s);
+  }
+  if (e == hipSuccess) {  // dW1 = dZ^T X
+    GenArgs a{};
+    a.A = dZ; a.a_g = C * F; a.a_m = 1; a.a_k = F; a.a_kmax = C;
+    a.B = xd; a.b_g = C * d; a.b_n = 1; a.b_k = d; a.b_kmax = C;
+    a.C = (bf16 *)gr->dw1; a.c_g = F * d; a.c_m = d; a.M = F; a.krows = kept; a.K = C;
+    a.N = (int)d; a.G = (int)E;
+    e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_expert_dw1", s);
+  }
+  // PR-MoE dense MLP
+  bf16 *dxd = nullptr;
+  if (pr && e == hipSuccess) {
+    bf16 *Zd = (bf16 *)at(ws, L.Zd), *Hd = (bf16 *)at(ws, L.Hd), *dZd = (bf16 *)at(ws, L.dZd);
+    dxd = (bf16 *)at(ws, L.dxd);
+    if (T > 0) {
+      GemmArgs z{x, w->wm1, nullptr, Zd, nullptr, T, (int)Fd, (int)d, 1};
+      e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_dense_z", s);
+    }
+    if (e == hipSuccess) e = moe_host::launch_gelu_map(Zd, Hd, T * Fd, s);
+    if (e == hipSuccess && T > 0) {
+      GenArgs a{};
+      a.A = dyb; a.a_m = d; a.a_k = 1;
+      a.B = (const bf16 *)w->wm2; a.b_n = 1; a.b_k = Fd; a.b_kmax = d;
+      a.C = dZd; a.c_m = Fd; a.Z = Zd; a.M = T; a.K = d; a.N = (int)Fd; a.G = 1;
+      e = moe_host::launch_gemm_gen(a, false, true, true, "bwd_dense_dz", s);
+    }
+    if (e == hipSuccess && T > 0) {
+      GenArgs a{};
+      a.A = dZd; a.a_m = Fd; a.a_k = 1;
+      a.B = (const bf16 *)w->wm1; a.b_n = 1; a.b_k = d; a.b_kmax = Fd;
+      a.C = dxd; a.c_m = d; a.M = T; a.K = Fd; a.N = (int)d; a.G = 1;
+      e = moe_host::launch_gemm_gen(a, false, true, false, "bwd_dense_dx", s);
+    }
+    if (e == hipSuccess) {
+      GenArgs a{};
+      a.A = dyb; a.a_m = 1; a.a_k = d; a.a_kmax = T;
+      a.B = Hd; a.b_n = 1; a.b_k = Fd; a.b_kmax = T;
+      a.C = (bf16 *)gr->dwm2; a.c_m = Fd; a.M = d; a.K = T; a.N = (int)Fd; a.G = 1;
+      e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_dense_dw2", s);
+    }
+    if (e == hipSuccess) {
+      GenArgs a{};
+      a.A = dZd; a.a_m = 1; a.a_k = Fd; a.a_kmax = T;
+      a.B = xb; a.b_n = 1; a.b_k = d; a.b_kmax = T;
+      a.C = (bf16 *)gr->dwm1; a.c_m = d; a.M = Fd; a.K = T; a.N = (int)d; a.G = 1;
+      e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_dense_dw1", s);
+    }
+  }
+  if (e == hipSuccess)
+    e = moe_host::launch_bwd_dx(cfg->add_skip ? dyb : nullptr, dxd, dxr, dX, ids, slots, T,
+                                (int)cfg->k, (int)d, C, (int)E, (bf16 *)gr->dx, s);
   return hip_status(e);
 }
 

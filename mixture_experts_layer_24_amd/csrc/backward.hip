@@ -1,0 +1,445 @@
+// backward.hip -- backward of the MoE layer on gfx950.
+//
+// Gradients of <dy, y> + g_aux * aux + g_z * z with respect to x and every
+// weight, by the chain rule through the forward stages (the method's layer:
+// "DeepSpeed MoE and Model Compression", section DeepSpeed-MoE; capacity
+// overflow: "DeepSpeed-MoE vs Switch Transformer", where a dropped token skips
+// the expert and so gets no expert gradient; gates renormalised over the
+// top-k: survey notes sec. 1.1.1.1; Switch load-balance loss: survey notes
+// sec. 1.1.4.1; router z-loss: "DeepSpeed-MoE vs Switch Transformer", section
+// Router Z-loss).  Per kept assignment (t, j) of expert e at slot s:
+//   dg[t,j] = <dy[t], y_disp[e,s]>,   dY[e,s] = g[t,j] dy[t]
+// expert FFN (a = W1 x, h = GELU(a), out = W2 h), all as grouped GEMMs:
+//   dZ = (dY W2) * GELU'(Z),  dX = dZ W1,  dW2 = dY^T H,  dW1 = dZ^T X
+// router: dp from dg (through the renormalisation) and from the aux loss
+// (f_e is piecewise constant), softmax Jacobian, plus the z-loss term
+// (2/T) lse p; then dx += dlogits W_r, dW_r = dlogits^T x, db = sum dlogits.
+// The PR-MoE dense MLP is the same FFN backward with d(out) = dy.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  // Phi(z) + z phi(z)
+  const float cdf = 0.5f * (1.0f + erf_as(z * 0.70710678118654752440f));
+  return cdf + z * 0.39894228040143267794f * __expf(-0.5f * z * z);
+}
+
+// ---------------------------------------------------------------------------
+// General grouped GEMM for the backward products:
+//   C(g, m, n) = epi( sum_k A(g, m, k) B(g, n, k) ),  m < rows of group g
+// A(g, m, k) = A[g a_g + m a_m + k a_k] with either a_k == 1 (K contiguous)
+// or a_m == 1 (K-major, the layout the forward's weights and activations have
+// for the products that contract over their other index); the same for B.
+// Tiles: 128 x BN x 32, four waves of 64 x BN/2, 32x32x16 bf16 MFMA, fp32
+// accumulators.  Operands go through registers into LDS as [row][k] (rows of
+// 40 elements: 80-byte stride, conflict-free 16-byte operand reads); a
+// K-major operand is loaded 8 rows wide at one k and written transposed.
+// Reduction steps past the group's valid K read as zero; rows past the
+// group's valid M are clamped on load and not stored.
+
+template <int BN, bool AKM, bool BKM, bool DGELU>
+__global__ __launch_bounds__(256) void gemm_gen_kernel(GenArgs a) {
+  constexpr int BM = 128, BK = 32, LDK = BK + 8;
+  constexpr int WTN = BN / 2, TM = 2, TN = WTN / 32;
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 2, wn = wave % 2;
+  const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = a.N / BN;
+  const int tile = blockIdx.x;
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  int64_t mvalid = a.M;
+  if (a.mrows) mvalid = a.mrows[g] < mvalid ? a.mrows[g] : mvalid;
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= mvalid) return;
+  const int n0 = tn * BN;
+  int64_t kvalid = a.K;
+  if (a.krows) kvalid = a.krows[g] < kvalid ? a.krows[g] : kvalid;
+  const int ksteps = (int)((kvalid + BK - 1) / BK);
+  const bf16 *Ag = a.A + (int64_t)g * a.a_g;
+  const bf16 *Bg = a.B + (int64_t)g * a.b_g;
+
+  // per thread: two 16-byte chunks of each operand per K step
+  u32x4 ra[2], rb[2];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int c = tid + 256 * p;
+      if constexpr (!AKM) {  // 128 rows x 4 chunks along k
+        const int r = c >> 2, kc = (c & 3) * 8;
+        int64_t m = m0 + r;
+        if (m >= mvalid) m = mvalid - 1;
+        ra[p] = (k0 + kc < kvalid) ? *(const u32x4 *)(Ag + m * a.a_m + (k0 + kc)) : zero;
+      } else {  // 32 k rows x 16 chunks along m
+        const int k = c >> 4, rc = (c & 15) * 8;
+        const int64_t kk = k0 + k;
+        const bool ok = kk < kvalid && kk < a.a_kmax && m0 + rc < a.M;
+        ra[p] = ok ? *(const u32x4 *)(Ag + kk * a.a_k + m0 + rc) : zero;
+      }
+      if constexpr (!BKM) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        if (r < BN)
+          rb[p] = (k0 + kc < kvalid) ? *(const u32x4 *)(Bg + (int64_t)(n0 + r) * a.b_n + (k0 + kc))
+                                     : zero;
+      } else {
+        const int k = c >> 4, rc = (c & 15) * 8;
+        const int64_t kk = k0 + k;
+        if (rc < BN) {
+          const bool ok = kk < kvalid && kk < a.b_kmax;
+          rb[p] = ok ? *(const u32x4 *)(Bg + kk * a.b_k + n0 + rc) : zero;
+        }
+      }
+    }
+  };
+  auto store = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int c = tid + 256 * p;
+      if constexpr (!AKM) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        *(u32x4 *)(&As[st][r * LDK + kc]) = ra[p];
+      } else {
+        const int k = c >> 4, rc = (c & 15) * 8;
+        const bf16 *v = (const bf16 *)&ra[p];
+#pragma unroll
+        for (int i = 0; i < 8; i++) As[st][(rc + i) * LDK + k] = v[i];
+      }
+      if constexpr (!BKM) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        if (r < BN) *(u32x4 *)(&Bs[st][r * LDK + kc]) = rb[p];
+      } else {
+        const int k = c >> 4, rc = (c & 15) * 8;
+        if (rc < BN) {
+          const bf16 *v = (const bf16 *)&rb[p];
+#pragma unroll
+          for (int i = 0; i < 8; i++) Bs[st][(rc + i) * LDK + k] = v[i];
+        }
+      }
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  if (ksteps > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; kt++) {
+    const int st = kt & 1;
+    if (kt + 1 < ksteps) load((kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < BK / 16; s++) {
+      const int col = 16 * s + 8 * (lane >> 5);
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+        af[i] = *(const bf16x8 *)(&As[st][(wm * 64 + i * 32 + (lane & 31)) * LDK + col]);
+#pragma unroll
+      for (int j = 0; j < TN; j++)
+        bfr[j] = *(const bf16x8 *)(&Bs[st][(wn * WTN + j * 32 + (lane & 31)) * LDK + col]);
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < ksteps) store(st ^ 1);
+    __syncthreads();
+  }
+
+  // 32x32 MFMA layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4,
+  // column l%32
+  bf16 *Cg = a.C + (int64_t)g * a.c_g;
+  const bf16 *Zg = DGELU ? a.Z + (int64_t)g * a.c_g : nullptr;
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int n = n0 + wn * WTN + j * 32 + (lane & 31);
+        if (m < mvalid) {
+          float v = acc[i][j][r];
+          if (DGELU) v *= gelu_grad_f((float)Zg[m * a.c_m + n]);
+          Cg[m * a.c_m + n] = (bf16)v;
+        }
+      }
+}
+
+// H = GELU(Z), elementwise (bf16)
+__global__ __launch_bounds__(256) void gelu_map_kernel(const bf16 *z, bf16 *h, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    h[i] = (bf16)gelu_f((float)z[i]);
+}
+
+// one wave per assignment: dg = <dy[t], y_disp[e,s]>, dY[e,s] = g dy[t]
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const bf16 *dy, const bf16 *y_disp,
+                                                       const int32_t *ids, const int32_t *slots,
+                                                       const float *gates, int64_t n_assign,
+                                                       int k, int d, int64_t C, int E, float *dg,
+                                                       bf16 *dY) {
+  const int lane = lane_id();
+  const int64_t a = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (a >= n_assign) return;
+  const int s = __builtin_amdgcn_readfirstlane(slots[a]);
+  const int e = __builtin_amdgcn_readfirstlane(ids[a]);
+  if (s < 0 || s >= C || e < 0 || e >= E) {
+    if (lane == 0) dg[a] = 0.f;
+    return;
+  }
+  const float g = gates[a];
+  const bf16 *dyt = dy + (a / k) * (int64_t)d;
+  const bf16 *yr = y_disp + ((int64_t)e * C + s) * d;
+  bf16 *dr = dY + ((int64_t)e * C + s) * d;
+  float acc = 0.f;
+  for (int o = lane * 8; o < d; o += kWave * 8) {
+    const bf16x8 u = *(const bf16x8 *)(dyt + o), v = *(const bf16x8 *)(yr + o);
+    bf16x8 w;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      acc += (float)u[i] * (float)v[i];
+      w[i] = (bf16)(g * (float)u[i]);
+    }
+    *(bf16x8 *)(dr + o) = w;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) dg[a] = acc;
+}
+
+__global__ __launch_bounds__(256) void first_choice_kernel(const int32_t *ids, int64_t T, int k,
+                                                           int E, int32_t *cnt) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < T;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int e = ids[t * k];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// one wave per token: dlogits from the gate gradients, the aux loss and the
+// z-loss; fp32 [T, E] and bf16 [T, Ep] (zero past E) copies
+__global__ __launch_bounds__(256) void bwd_router_kernel(
+    const float *logits, const int32_t *ids, const float *gates, const float *dg,
+    const int32_t *fcnt, int64_t T, int E, int Ep, int k, int normalize, float alpha,
+    float g_aux, float g_z, float *dlog, bf16 *dlog16) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  float l[4], p[4], dp[4];
+  float m = neg_inf();
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    l[i] = e < E ? logits[t * E + e] : neg_inf();
+    m = fmaxf(m, l[i]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    p[i] = e < E ? __expf(l[i] - m) : 0.f;
+    s += p[i];
+  }
+  s = wave_sum(s);
+  const float lse = m + logf(s);
+  const float aux_scale = g_aux * alpha * (float)E / (float)T / (float)T;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    p[i] = p[i] / s;
+    dp[i] = e < E ? aux_scale * (float)fcnt[e] : 0.f;
+  }
+  // gate gradients (the same values in every lane)
+  float S = 0.f, sdg = 0.f;
+  for (int j = 0; j < k; j++) {
+    const int ej = ids[t * k + j];
+    // p[ej] lives in lane ej % 64, register ej / 64
+    float pv = p[0];
+    if ((ej >> 6) == 1) pv = p[1];
+    if ((ej >> 6) == 2) pv = p[2];
+    if ((ej >> 6) == 3) pv = p[3];
+    S += __shfl(pv, ej & 63, kWave);
+    sdg += dg[t * k + j] * gates[t * k + j];
+  }
+  const bool renorm = k >= 2 && normalize;
+  for (int j = 0; j < k; j++) {
+    const int ej = ids[t * k + j];
+    const float v = renorm ? (dg[t * k + j] - sdg) / S : dg[t * k + j];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (lane + kWave * i == ej) dp[i] += v;
+  }
+  float pdp = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) pdp += p[i] * dp[i];
+  pdp = wave_sum(pdp);
+  const float zc = g_z * 2.0f / (float)T * lse;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = lane + kWave * i;
+    const float v = p[i] * (dp[i] - pdp) + zc * p[i];
+    if (e < E) dlog[t * E + e] = v;
+    if (e < Ep) dlog16[t * Ep + e] = (bf16)(e < E ? v : 0.f);
+  }
+}
+
+// db[e] = sum over tokens of dlog[t, e], fixed order (chunks, then a tree)
+__global__ __launch_bounds__(256) void colsum_kernel(const float *dlog, int64_t T, int E,
+                                                     float *db) {
+  __shared__ double red[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int64_t chunk = (T + 255) / 256;
+  const int64_t t0 = tid * chunk, t1 = t0 + chunk < T ? t0 + chunk : T;
+  double v = 0.0;
+  for (int64_t t = t0; t < t1; t++) v += (double)dlog[t * E + e];
+  red[tid] = v;
+  __syncthreads();
+  for (int st = 128; st >= 1; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) db[e] = (float)red[0];
+}
+
+// one wave per token: dx = [dy] + [dx_dense] + dx_router + sum over kept j of
+// dX[e_j, s_j], accumulated in fp32 in that order
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const bf16 *dy, const bf16 *dxd,
+                                                     const bf16 *dxr, const bf16 *dX,
+                                                     const int32_t *ids, const int32_t *slots,
+                                                     int64_t T, int k, int d, int64_t C, int E,
+                                                     bf16 *dx) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  for (int o = lane * 8; o < d; o += kWave * 8) {
+    float acc[8];
+    const bf16x8 r = *(const bf16x8 *)(dxr + t * d + o);
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = (float)r[i];
+    if (dy) {
+      const bf16x8 u = *(const bf16x8 *)(dy + t * d + o);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += (float)u[i];
+    }
+    if (dxd) {
+      const bf16x8 u = *(const bf16x8 *)(dxd + t * d + o);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += (float)u[i];
+    }
+    for (int j = 0; j < k; j++) {
+      const int s = slots[t * k + j], e = ids[t * k + j];
+      if (s < 0 || s >= C || e < 0 || e >= E) continue;
+      const bf16x8 u = *(const bf16x8 *)(dX + ((int64_t)e * C + s) * d + o);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += (float)u[i];
+    }
+    bf16x8 w;
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = (bf16)acc[i];
+    *(bf16x8 *)(dx + t * d + o) = w;
+  }
+}
+
+}  // namespace moe
+
+namespace moe_host {
+using namespace moe;
+
+template <int BN, bool AKM, bool BKM, bool DG>
+static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s) {
+  const int tiles = a.G * (int)((a.M + 127) / 128) * (a.N / BN);
+  if (tiles <= 0) return hipGetLastError();
+  const char *name = intern_name(role, BN == 128 ? "gen128" : "gen64");
+  MOE_LAUNCH(name, (gemm_gen_kernel<BN, AKM, BKM, DG>), dim3(tiles), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// a_kmajor / b_kmajor: which operand layouts; dgelu: epilogue
+hipError_t launch_gemm_gen(const GenArgs &a, bool a_kmajor, bool b_kmajor, bool dgelu,
+                           const char *role, hipStream_t s) {
+  const bool n128 = a.N % 128 == 0;
+#define MOE_GEN(BN_)                                                                     \
+  do {                                                                                   \
+    if (!a_kmajor && b_kmajor && dgelu) return launch_gen_t<BN_, false, true, true>(a, role, s); \
+    if (!a_kmajor && b_kmajor) return launch_gen_t<BN_, false, true, false>(a, role, s); \
+    if (a_kmajor && b_kmajor) return launch_gen_t<BN_, true, true, false>(a, role, s);   \
+  } while (0)
+  if (n128)
+    MOE_GEN(128);
+  else
+    MOE_GEN(64);
+#undef MOE_GEN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gelu_map(const bf16 *z, bf16 *h, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipGetLastError();
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  MOE_LAUNCH("gelu_map", gelu_map_kernel, dim3((unsigned)blocks), dim3(256), 0, s, z, h, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gate(const bf16 *dy, const bf16 *y_disp, const int32_t *ids,
+                           const int32_t *slots, const float *gates, int64_t T, int k, int d,
+                           int64_t C, int E, float *dg, bf16 *dY, hipStream_t s) {
+  const int64_t n = T * k;
+  if (n <= 0) return hipGetLastError();
+  MOE_LAUNCH("bwd_gate", bwd_gate_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, dy,
+             y_disp, ids, slots, gates, n, k, d, C, E, dg, dY);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_router(const float *logits, const int32_t *ids, const float *gates,
+                             const float *dg, int32_t *fcnt, int64_t T, int E, int Ep, int k,
+                             int normalize, float alpha, float g_aux, float g_z, float *dlog,
+                             bf16 *dlog16, float *db, hipStream_t s) {
+  MOE_LAUNCH("fill_i32", fill_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, s, fcnt, E, 0);
+  if (T > 0) {
+    int64_t blocks = (T + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    MOE_LAUNCH("first_choice", first_choice_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ids,
+               T, k, E, fcnt);
+    MOE_LAUNCH("bwd_router", bwd_router_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+               logits, ids, gates, dg, fcnt, T, E, Ep, k, normalize, alpha, g_aux, g_z, dlog,
+               dlog16);
+  }
+  if (db) MOE_LAUNCH("colsum", colsum_kernel, dim3(E), dim3(256), 0, s, dlog, T, E, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s) {
+  if (n > 0) MOE_LAUNCH("fill_i32", fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx(const bf16 *dy, const bf16 *dxd, const bf16 *dxr, const bf16 *dX,
+                         const int32_t *ids, const int32_t *slots, int64_t T, int k, int d,
+                         int64_t C, int E, bf16 *dx, hipStream_t s) {
+  if (T <= 0) return hipGetLastError();
+  MOE_LAUNCH("bwd_dx", bwd_dx_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, dy, dxd,
+             dxr, dX, ids, slots, T, k, d, C, E, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe_host

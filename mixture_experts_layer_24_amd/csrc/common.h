@@ -21,6 +21,7 @@ constexpr int kWave = 64;
 
 // ------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

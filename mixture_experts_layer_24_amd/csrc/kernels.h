@@ -33,6 +33,22 @@ struct GemmArgs {
   int N, K, G;
 };
 
+// general grouped GEMM of the backward (backward.hip)
+struct GenArgs {
+  const bf16 *A;
+  int64_t a_g, a_m, a_k, a_kmax;  // a_kmax: k rows that exist in memory (K-major)
+  const bf16 *B;
+  int64_t b_g, b_n, b_k, b_kmax;
+  bf16 *C;
+  int64_t c_g, c_m;
+  const bf16 *Z;         // DGELU epilogue: C = acc * GELU'(Z), Z laid out as C
+  const int32_t *mrows;  // [G] valid rows (clamped to M) or null
+  int64_t M;
+  const int32_t *krows;  // [G] valid reduction length (clamped to K) or null
+  int64_t K;
+  int N, G;
+};
+
 }  // namespace moe
 
 namespace moe_host {
@@ -40,6 +56,20 @@ namespace moe_host {
 int router_blocks(int64_t T);
 hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
 hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s);
+hipError_t launch_gemm_gen(const moe::GenArgs &a, bool a_kmajor, bool b_kmajor, bool dgelu,
+                           const char *role, hipStream_t s);
+hipError_t launch_gelu_map(const moe::bf16 *z, moe::bf16 *h, int64_t n, hipStream_t s);
+hipError_t launch_bwd_gate(const moe::bf16 *dy, const moe::bf16 *y_disp, const int32_t *ids,
+                           const int32_t *slots, const float *gates, int64_t T, int k, int d,
+                           int64_t C, int E, float *dg, moe::bf16 *dY, hipStream_t s);
+hipError_t launch_bwd_router(const float *logits, const int32_t *ids, const float *gates,
+                             const float *dg, int32_t *fcnt, int64_t T, int E, int Ep, int k,
+                             int normalize, float alpha, float g_aux, float g_z, float *dlog,
+                             moe::bf16 *dlog16, float *db, hipStream_t s);
+hipError_t launch_bwd_dx(const moe::bf16 *dy, const moe::bf16 *dxd, const moe::bf16 *dxr,
+                         const moe::bf16 *dX, const int32_t *ids, const int32_t *slots, int64_t T,
+                         int k, int d, int64_t C, int E, moe::bf16 *dx, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int n, int v, hipStream_t s);
 hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, hipStream_t s);
 
 // dispatch (token blocks of the same size as the router's)

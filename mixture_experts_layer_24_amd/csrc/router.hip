@@ -24,7 +24,6 @@ namespace moe {
 
 constexpr int RBM = 64;  // tokens per block
 
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // L: LDS logits tile [RBM][ldl] fp32 (bias not yet added).
 template <int MAXK>

@@ -1,0 +1,112 @@
+"""GPU parity of the layer backward against the oracle's fp64 backward.
+
+The oracle's backward is pinned separately (finite differences of the pinned
+forward, torch autograd on the one-expert case).  Here the GPU gradients of
+<dy, y> + g_aux * aux + g_z * z_loss, taken from the GPU forward's saved
+routing, are compared with the oracle's on the same bf16 inputs, after
+checking that both forwards made the same discrete decisions (top-k and
+capacity), which the backward holds fixed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_24_amd import binding, synth, workloads
+from parity_util import TAU, check_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+W = workloads.Workload
+
+CASES = [
+    W("bwd_top2_pr", T=300, d=256, E=8, k=2, d_ff=256, capacity_factor=1.0, d_ff_dense=256,
+      pr_moe=True, add_skip=True),
+    W("bwd_top1_drops", T=200, d=128, E=4, k=1, d_ff=384, capacity_factor=0.5),
+    W("bwd_top3_bn64", T=130, d=192, E=6, k=3, d_ff=128, capacity_factor=2.0, zipf_s=0.8),
+    W("bwd_idle_experts", T=40, d=128, E=16, k=1, d_ff=256, capacity_factor=1.0, zipf_s=2.0,
+      pr_moe=True, d_ff_dense=128, add_skip=False),
+    W("bwd_prmoe_shape", T=520, d=512, E=16, k=1, d_ff=1024, capacity_factor=1.0,
+      d_ff_dense=1024, pr_moe=True, add_skip=False),
+]
+
+
+@pytest.mark.parametrize("policy", ["token_order", "gate_priority"])
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_backward_matches_oracle(wl, policy):
+    print(f"[backward] {wl.name} {policy}", flush=True)
+    g_aux, g_z = 0.3, 0.2
+    inp = synth.make_inputs(wl, seed=3)
+    dinp = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    cfg = binding.config_of(wl, drop_policy=policy)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True)
+    binding.moe_layer_forward(cfg, dinp["x"], dinp, out, binding.alloc_workspace(cfg))
+    dy = synth.normal((wl.T, wl.d), 1.0, 9, "dy", "cpu", torch.bfloat16)
+    grads = binding.alloc_grads(cfg, DEV)
+    binding.moe_layer_backward(cfg, dinp["x"], dinp, out, dy.to(DEV), grads,
+                               binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD),
+                               g_aux=g_aux, g_z=g_z)
+    torch.cuda.synchronize()
+    pol = oracle.DROP_GATE_PRIORITY if policy == "gate_priority" else oracle.DROP_TOKEN_ORDER
+    fw = oracle.layer_forward(inp["x"], inp["w_router"], inp["w1"], inp["w2"], k=wl.k,
+                              capacity_factor=wl.capacity_factor, bias=inp["b_router"],
+                              wm1=inp["wm1"], wm2=inp["wm2"], normalize=wl.normalize_topk,
+                              pr_moe=wl.pr_moe, add_skip=wl.add_skip, policy=pol,
+                              alpha=wl.aux_alpha)
+    # the backward holds the forward's discrete decisions: both sides must agree
+    assert np.array_equal(to_np(out.expert_ids), fw["ids"])
+    assert np.array_equal(to_np(out.slots), fw["slots"])
+    ref = oracle.layer_backward(inp["x"], inp["w_router"], inp["w1"], inp["w2"],
+                                dy.double().numpy(), k=wl.k, capacity_factor=wl.capacity_factor,
+                                bias=inp["b_router"], wm1=inp["wm1"], wm2=inp["wm2"],
+                                normalize=wl.normalize_topk, pr_moe=wl.pr_moe,
+                                add_skip=wl.add_skip, policy=pol, alpha=wl.aux_alpha,
+                                g_aux=g_aux, g_z=g_z)
+    tau = TAU["bf16"]
+    errs = {n: check_close(n, getattr(grads, n), ref[n], tau)
+            for n in ("dx", "dw_router", "db_router", "dw1", "dw2")}
+    print("  relative errors " + ", ".join(f"{n} {v:.2e}" for n, v in errs.items()), flush=True)
+    kept = to_np(out.kept)
+    for e in np.nonzero(kept == 0)[0]:  # an expert without rows gets zero gradient
+        assert not grads.dw1[e].any() and not grads.dw2[e].any()
+    if wl.pr_moe:
+        check_close("dwm1", grads.dwm1, ref["dwm1"], tau)
+        check_close("dwm2", grads.dwm2, ref["dwm2"], tau)
+
+
+def test_backward_is_deterministic():
+    wl = CASES[0]
+    inp = synth.make_inputs(wl, seed=4)
+    dinp = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    cfg = binding.config_of(wl)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True)
+    binding.moe_layer_forward(cfg, dinp["x"], dinp, out, binding.alloc_workspace(cfg))
+    dy = synth.normal((wl.T, wl.d), 1.0, 2, "dy", DEV, torch.bfloat16)
+    ws = binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD)
+    runs = []
+    for _ in range(2):
+        g = binding.alloc_grads(cfg, DEV)
+        binding.moe_layer_backward(cfg, dinp["x"], dinp, out, dy, g, ws, g_aux=0.5, g_z=0.1)
+        torch.cuda.synchronize()
+        runs.append(g)
+    for name in ("dx", "dw_router", "db_router", "dw1", "dw2", "dwm1", "dwm2"):
+        assert torch.equal(getattr(runs[0], name), getattr(runs[1], name)), name
+
+
+def test_backward_rejects_unsupported_and_missing_outputs():
+    wl = W("q", T=64, d=128, E=4, k=1, d_ff=128, capacity_factor=1.0, wfmt="int8")
+    cfg = binding.config_of(wl)
+    inp = {k: (None if v is None else v.to(DEV)) for k, v in synth.make_inputs(wl).items()}
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True)
+    g = binding.alloc_grads(cfg, DEV)
+    dy = torch.zeros(64, 128, dtype=torch.bfloat16, device=DEV)
+    ws = binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD)
+    with pytest.raises(binding.MoeError, match="unsupported"):
+        binding.moe_layer_backward(cfg, inp["x"], inp, out, dy, g, ws)
+    wl2 = wl.replace(wfmt="plain")
+    cfg2 = binding.config_of(wl2)
+    inp2 = {k: (None if v is None else v.to(DEV)) for k, v in synth.make_inputs(wl2).items()}
+    out2 = binding.alloc_outputs(cfg2, DEV)  # no logits / x_disp / y_disp saved
+    with pytest.raises(binding.MoeError, match="invalid"):
+        binding.moe_layer_backward(cfg2, inp2["x"], inp2, out2, dy, binding.alloc_grads(cfg2, DEV),
+                                   binding.alloc_workspace(cfg2, binding.ENTRY_BACKWARD))
