@@ -16,6 +16,7 @@
 // (2/T) lse p; then dx += dlogits W_r, dW_r = dlogits^T x, db = sum dlogits.
 // The PR-MoE dense MLP is the same FFN backward with d(out) = dy.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace moe {
@@ -172,6 +173,198 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(GenArgs a) {
       for (int r = 0; r < 16; r++) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int n = n0 + wn * WTN + j * 32 + (lane & 31);
+        if (m < mvalid) {
+          float v = acc[i][j][r];
+          if (DGELU) v *= gelu_grad_f((float)Zg[m * a.c_m + n]);
+          Cg[m * a.c_m + n] = (bf16)v;
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
+// The same products on the LDS-DMA pipeline, for the large shapes (M and N
+// multiples of 128, K a multiple of 32; reduction rows past the group's
+// valid K are zeroed in LDS before use).  Tiles 128 x 128 x 32, four waves of
+// 64 x 64, NS stages in flight.  A K-contiguous operand is staged as in the
+// forward GEMM ([row][k], 64-byte rows, slot c ^ ((R >> 2) & 3)).  A K-major
+// operand is staged as it lies in memory, [k][row] with 256-byte rows, chunk
+// c of row k in slot c ^ 4 (k & 3), and its MFMA fragments are read with
+// gfx950's transposing LDS read ds_read_b64_tr_b16: within each 16-lane group
+// lane i receives element i % 4 of the 4-element pieces addressed by lanes
+// i/4, 4 + i/4, 8 + i/4, 12 + i/4 (measured on MI355X), so lane r of a group
+// addressing row k0 + r/4, elements e0 + 4 (r % 4) hands lane i the values of
+// element e0 + i at k0 .. k0 + 3 -- the 32x32x16 operand layout.  The swizzle
+// spreads a half-wave's 32 eight-byte reads over all 64 banks.
+typedef __bf16 bf16x4v __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+__device__ __forceinline__ int swz_km(int k) { return 4 * (k & 3); }
+
+// 8 consecutive k (kbase + 8 (lane / 32) ...) of row row0 + lane % 32 from a
+// K-major tile of 128-element rows at LDS byte address `tile`
+__device__ __forceinline__ bf16x8 frag_kmajor(uint32_t tile, int row0, int kbase, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int e = row0 + 16 * (g & 1) + 4 * (r & 3);
+  bf16x8 out;
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const int k = kbase + 8 * (g >> 1) + 4 * p + (r >> 2);
+    const uint32_t off = tile + k * 256 + ((((e >> 3) ^ swz_km(k)) << 4) | ((e & 7) << 1));
+    const bf16x4v v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4v *)(uintptr_t)off);
+#pragma unroll
+    for (int j = 0; j < 4; j++) out[4 * p + j] = v[j];
+  }
+  return out;
+}
+
+template <bool AKM, bool BKM, bool DGELU, int NS>
+__global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
+  constexpr int BM = 128, BN = 128, BK = 32, TILE = 8192;  // bytes per operand tile
+  constexpr int STAGE = 2 * TILE;
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 2, wn = wave % 2;
+  const int tiles_m = (int)(a.M / BM), tiles_n = a.N / BN;
+  const int tile = blockIdx.x;
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  int64_t mvalid = a.M;
+  if (a.mrows) mvalid = a.mrows[g] < mvalid ? a.mrows[g] : mvalid;
+  const int64_t m0 = (int64_t)tm * BM;
+  if (m0 >= mvalid) return;
+  const int n0 = tn * BN;
+  int64_t kvalid = a.K;
+  if (a.krows) kvalid = a.krows[g] < kvalid ? a.krows[g] : kvalid;
+  const int ksteps = (int)((kvalid + BK - 1) / BK);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+
+  // per-tile operand bases (bytes) and this lane's offsets for its chunks:
+  // every wave moves 2 chunks (1 KB each) of A and 2 of B per stage
+  const char *abase, *bbase;
+  int64_t astep, bstep;  // bytes per K step
+  uint32_t voa[2], vob[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int q = 2 * wave + i;
+    if constexpr (!AKM) {  // rows of 64 bytes: 16 rows per chunk
+      const int R = 16 * q + lane / 4, slot = lane % 4;
+      int64_t m = m0 + R;
+      if (m >= mvalid) m = mvalid - 1;
+      voa[i] = (uint32_t)((m - m0) * a.a_m * 2 + ((slot ^ swz_slot<32>(R)) << 4));
+    } else {  // k rows of 256 bytes: 4 rows per chunk
+      const int k = 4 * q + lane / 16, slot = lane % 16;
+      voa[i] = (uint32_t)(k * a.a_k * 2 + ((slot ^ swz_km(k)) << 4));
+    }
+    if constexpr (!BKM) {
+      const int R = 16 * q + lane / 4, slot = lane % 4;
+      vob[i] = (uint32_t)(R * a.b_n * 2 + ((slot ^ swz_slot<32>(R)) << 4));
+    } else {
+      const int k = 4 * q + lane / 16, slot = lane % 16;
+      vob[i] = (uint32_t)(k * a.b_k * 2 + ((slot ^ swz_km(k)) << 4));
+    }
+  }
+  if constexpr (!AKM) {
+    abase = (const char *)(a.A + (int64_t)g * a.a_g + m0 * a.a_m);
+    astep = BK * 2;
+  } else {
+    abase = (const char *)(a.A + (int64_t)g * a.a_g + m0);
+    astep = (int64_t)BK * a.a_k * 2;
+  }
+  if constexpr (!BKM) {
+    bbase = (const char *)(a.B + (int64_t)g * a.b_g + (int64_t)n0 * a.b_n);
+    bstep = BK * 2;
+  } else {
+    bbase = (const char *)(a.B + (int64_t)g * a.b_g + n0);
+    bstep = (int64_t)BK * a.b_k * 2;
+  }
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+    const char *ga = abase + (int64_t)kt * astep, *gb = bbase + (int64_t)kt * bstep;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+      dma16<false>(ga, voa[i],
+                   __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (2 * wave + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+      dma16<false>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILE +
+                                                              (2 * wave + i) * 1024));
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; p++)
+    if (p < ksteps) issue(p, p);
+  for (int kt = 0; kt < ksteps; kt++) {
+    if (kt + NS - 2 < ksteps)
+      wait_vmcnt<(NS - 2) * 4>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    const int st = kt % NS;
+    const int kleft = (int)(kvalid - (int64_t)kt * BK);
+    if (kleft < BK) {  // ragged last step: zero the k rows past the valid ones
+      // (only K-major operands reach here: the host keeps K-contiguous K whole)
+      for (int idx = tid; idx < (BK - kleft) * 16; idx += 256) {
+        const int k = kleft + idx / 16, c = idx % 16;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        if (AKM) *(u32x4 *)(smem + st * STAGE + k * 256 + c * 16) = z;
+        if (BKM) *(u32x4 *)(smem + st * STAGE + TILE + k * 256 + c * 16) = z;
+      }
+      __syncthreads();
+    }
+    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
+    const uint32_t ta = lds0 + st * STAGE, tb = ta + TILE;
+#pragma unroll
+    for (int s = 0; s < BK / 16; s++) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int row0 = wm * 64 + i * 32;
+        if constexpr (AKM) {
+          af[i] = frag_kmajor(ta, row0, 16 * s, lane);
+        } else {
+          const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
+          af[i] = *(const bf16x8 *)(smem + st * STAGE + R * 64 + ((c ^ swz_slot<32>(R)) << 4));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int row0 = wn * 64 + j * 32;
+        if constexpr (BKM) {
+          bfr[j] = frag_kmajor(tb, row0, 16 * s, lane);
+        } else {
+          const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
+          bfr[j] =
+              *(const bf16x8 *)(smem + st * STAGE + TILE + R * 64 + ((c ^ swz_slot<32>(R)) << 4));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  bf16 *Cg = a.C + (int64_t)g * a.c_g;
+  const bf16 *Zg = DGELU ? a.Z + (int64_t)g * a.c_g : nullptr;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
         if (m < mvalid) {
           float v = acc[i][j][r];
           if (DGELU) v *= gelu_grad_f((float)Zg[m * a.c_m + n]);
@@ -374,9 +567,38 @@ static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s
   return hipGetLastError();
 }
 
+template <bool AKM, bool BKM, bool DG>
+static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t s) {
+  const int tiles = a.G * (int)(a.M / 128) * (a.N / 128);
+  if (tiles <= 0) return hipGetLastError();
+  MOE_LAUNCH(intern_name(role, "dma128x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4>), dim3(tiles),
+             dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// the DMA kernel needs 128-multiples for M and N, K a multiple of 32, a
+// whole K for K-contiguous operands, K-major extents that cover the rounded-up
+// K, 16-byte aligned rows, and per-lane offsets below 2^32
+static bool dmag_ok(const GenArgs &a, bool akm, bool bkm) {
+  if (a.M % 128 || a.N % 128 || a.K % 32 || a.K <= 0) return false;
+  if ((!akm || !bkm) && a.krows) return false;
+  if (akm && (a.a_kmax < a.K || a.a_k % 8)) return false;
+  if (bkm && (a.b_kmax < a.K || a.b_k % 8)) return false;
+  if (!akm && (a.a_m % 8 || a.a_m * 2 * 128 >= (int64_t(1) << 31))) return false;
+  if (!bkm && (a.b_n % 8 || a.b_n * 2 * 128 >= (int64_t(1) << 31))) return false;
+  if (akm && a.a_k * 2 * 32 >= (int64_t(1) << 31)) return false;
+  if (bkm && a.b_k * 2 * 32 >= (int64_t(1) << 31)) return false;
+  return true;
+}
+
 // a_kmajor / b_kmajor: which operand layouts; dgelu: epilogue
 hipError_t launch_gemm_gen(const GenArgs &a, bool a_kmajor, bool b_kmajor, bool dgelu,
                            const char *role, hipStream_t s) {
+  if (dmag_ok(a, a_kmajor, b_kmajor)) {
+    if (!a_kmajor && b_kmajor && dgelu) return launch_dmag_t<false, true, true>(a, role, s);
+    if (!a_kmajor && b_kmajor) return launch_dmag_t<false, true, false>(a, role, s);
+    if (a_kmajor && b_kmajor) return launch_dmag_t<true, true, false>(a, role, s);
+  }
   const bool n128 = a.N % 128 == 0;
 #define MOE_GEN(BN_)                                                                     \
   do {                                                                                   \

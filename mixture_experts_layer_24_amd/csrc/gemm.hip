@@ -27,6 +27,7 @@
 // expert's tiles back to back so they share its L2 for their A rows;
 // otherwise each XCD takes a contiguous range of tiles.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -234,51 +235,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 // results); their completion is awaited with explicit vmcnt waits before the
 // barrier that publishes a stage, because the compiler would otherwise wait
 // for every outstanding load before each LDS read.
-template <int BK>
-__device__ __forceinline__ int swz_slot(int R) {
-  if constexpr (BK == 64)
-    return (R & 7) ^ ((R >> 3) & 1);
-  else
-    return (R >> 2) & 3;
-}
-
-// NT: non-temporal (streamed once, e.g. expert weights: ~7.0 vs ~6.2 TB/s
-// for plain streaming reads on MI355X).  The compiler treats m0 as reserved
-// and ignores the clobber; that is safe here because compiler-generated code
-// in these kernels never uses m0 (tests/test_isa_cpu.py checks the ISA).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-template <bool NT>
-__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// 32-row fragments of a wave's TM-fragment row band holding at least one
-// valid row, given `left` = valid rows from the band's first row (uniform).
-template <int TM>
-__device__ __forceinline__ int live_frags(int64_t left) {
-  if (left <= 0) return 0;
-  const int64_t f = (left + 31) / 32;
-  return f < TM ? (int)f : TM;
-}
-
-// s_waitcnt vmcnt(N) with the other counters left open (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
 // NTB: load the weight operand non-temporally (read once)
 template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, bool GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {

@@ -28,6 +28,11 @@ CASES = [
       pr_moe=True, d_ff_dense=128, add_skip=False),
     W("bwd_prmoe_shape", T=520, d=512, E=16, k=1, d_ff=1024, capacity_factor=1.0,
       d_ff_dense=1024, pr_moe=True, add_skip=False),
+    # 128-multiples: the LDS-DMA kernels with transposing operand reads
+    # (capacity 128 with ragged kept rows, T = 1024 for the dense products)
+    W("bwd_dma_top1_pr", T=1024, d=256, E=8, k=1, d_ff=512, capacity_factor=1.0,
+      d_ff_dense=256, pr_moe=True, add_skip=True),
+    W("bwd_dma_top2", T=512, d=384, E=8, k=2, d_ff=256, capacity_factor=1.0, zipf_s=0.5),
 ]
 
 
