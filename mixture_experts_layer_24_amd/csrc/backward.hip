@@ -355,22 +355,49 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
     }
   }
 
+  // epilogue through LDS, one 64-row band (the two waves with wm == band) at
+  // a time, in fp32 (rows of 132 floats): coalesced 16-byte stores, and the
+  // GELU' factor applied before the single rounding to bf16
   bf16 *Cg = a.C + (int64_t)g * a.c_g;
   const bf16 *Zg = DGELU ? a.Z + (int64_t)g * a.c_g : nullptr;
+  constexpr int CROW = 132;
+  static_assert(64 * CROW * 4 <= NS * STAGE, "band fits the stages");
+  float *cs = (float *)smem;
+  for (int band = 0; band < 2; band++) {
+    __syncthreads();  // stages (or the previous band) no longer read
+    if (wm == band) {
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+      for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (m < mvalid) {
-          float v = acc[i][j][r];
-          if (DGELU) v *= gelu_grad_f((float)Zg[m * a.c_m + n]);
-          Cg[m * a.c_m + n] = (bf16)v;
-        }
+          for (int r = 0; r < 16; r++) {
+            const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int Cc = wn * 64 + j * 32 + (lane & 31);
+            cs[R * CROW + Cc] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    const int64_t r0 = m0 + band * 64;
+    for (int idx = tid; idx < 64 * 16; idx += 256) {
+      const int R = idx >> 4, ch = idx & 15;
+      const int64_t m = r0 + R;
+      if (m >= mvalid) continue;
+      const float *src = cs + R * CROW + ch * 8;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) v[q] = src[q];
+      if (DGELU) {
+        const bf16x8 z = *(const bf16x8 *)(Zg + m * a.c_m + n0 + ch * 8);
+#pragma unroll
+        for (int q = 0; q < 8; q++) v[q] *= gelu_grad_f((float)z[q]);
       }
+      bf16x8 o;
+#pragma unroll
+      for (int q = 0; q < 8; q++) o[q] = (bf16)v[q];
+      *(bf16x8 *)(Cg + m * a.c_m + n0 + ch * 8) = o;
+    }
+  }
 }
 
 // H = GELU(Z), elementwise (bf16)
