@@ -79,6 +79,10 @@ def _load(path: str | None = None):
         lib.oracle_layer_backward.argtypes = (
             [i64] * 5 + [i64, dbl, i64] + [i32] * 4 + [dbl, vp, i32] + [vp] * 6 +
             [vp, dbl, dbl] + [vp] * 7)
+        lib.oracle_backward_sampled.restype = i32
+        lib.oracle_backward_sampled.argtypes = (
+            [i64] * 6 + [i32] * 3 + [dbl, vp, i32] + [vp] * 6 + [vp, vp, vp, dbl, dbl] +
+            [vp, i64, vp, vp, i64, vp, vp, i64, vp])
         lib.oracle_z_loss.restype = dbl
         lib.oracle_z_loss.argtypes = [i64, i64, vp]
         lib.oracle_quantize_sym_int8.restype = i32
@@ -319,3 +323,42 @@ def layer_backward(x, w_router, w1, w2, dy, *, k: int, capacity_factor: float,
     if not pr_moe:
         out["dwm1"] = out["dwm2"] = None
     return out
+
+
+def backward_sampled(x, w_router, w1, w2, ids, slots, dy, rows, *, k: int, bias=None,
+                     wm1=None, wm2=None, normalize: bool = True, pr_moe: bool = False,
+                     add_skip: bool = True, alpha: float = 1.0, g_aux: float = 0.0,
+                     g_z: float = 0.0, dw1_idx=(), dw2_idx=()):
+    """dx rows of the tokens `rows` and dW1 / dW2 entries (triples (e, f, i) /
+    (e, o, f)) of the layer backward under the given routing decisions
+    ids / slots (T x k); dy: T x D upstream gradient."""
+    xa, xf = _np(x)
+    wra, _ = _np(w_router)
+    w1a, _ = _np(w1)
+    w2a, _ = _np(w2)
+    T, D = xa.shape
+    E, F = w1a.shape[0], w1a.shape[1]
+    Fd = 0
+    m1 = m2 = None
+    if pr_moe:
+        m1, _ = _np(wm1)
+        m2, _ = _np(wm2)
+        Fd = m1.shape[0]
+    b = None if bias is None else np.ascontiguousarray(_np(bias)[0], dtype=np.float32)
+    ids = np.ascontiguousarray(ids, np.int32)
+    slots = np.ascontiguousarray(slots, np.int32)
+    rows = np.ascontiguousarray(rows, np.int64)
+    dyf = np.ascontiguousarray(np.asarray(dy, np.float64).reshape(T, D))
+    i1 = np.ascontiguousarray(np.asarray(dw1_idx, np.int64).reshape(-1, 3))
+    i2 = np.ascontiguousarray(np.asarray(dw2_idx, np.int64).reshape(-1, 3))
+    dx = np.zeros((len(rows), D))
+    v1, v2 = np.zeros(len(i1)), np.zeros(len(i2))
+    rc = _load().oracle_backward_sampled(
+        T, D, E, k, F, Fd, int(normalize), int(pr_moe), int(add_skip), float(alpha),
+        xa.ctypes.data, xf, wra.ctypes.data, _p(b), w1a.ctypes.data, w2a.ctypes.data,
+        _p(m1), _p(m2), ids.ctypes.data, slots.ctypes.data, dyf.ctypes.data, float(g_aux),
+        float(g_z), rows.ctypes.data, len(rows), dx.ctypes.data, i1.ctypes.data, len(i1),
+        v1.ctypes.data, i2.ctypes.data, len(i2), v2.ctypes.data)
+    if rc:
+        raise ValueError("oracle_backward_sampled rejected its arguments")
+    return dict(dx=dx, dw1=v1, dw2=v2)

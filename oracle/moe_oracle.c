@@ -490,12 +490,35 @@ static void ffn_row_backward(int64_t D, int64_t F, const void *x, int fmt, int64
     for (int64_t f = 0; f < F; f++) s += elem(w1, fmt, f * D + i) * dh[f];
     dx_row[i] += s;
   }
+  if (!dw1 || !dw2) return; /* dx only */
   for (int64_t f = 0; f < F; f++) {
     const double hf = gelu(a[f]);
     for (int64_t o = 0; o < D; o++) dw2[o * F + f] += dout[o] * hf;
   }
   for (int64_t f = 0; f < F; f++)
     for (int64_t i = 0; i < D; i++) dw1[f * D + i] += dh[f] * elem(x, fmt, row * D + i);
+}
+
+/* dL/dlogits of one token from its gate gradients dg_j = <dy_t, expert output>
+ * (zero for a dropped assignment), its chosen experts ids_t, gates g, softmax
+ * probabilities p, log-sum-exp lse and the argmax fractions f; dp is scratch
+ * [E], the result goes to dl [E] (the bullets above, in order). */
+static void router_token_grad(int64_t E, int64_t k, int64_t T, int normalize, double alpha,
+                              double g_aux, double g_z, const double *f, const double *p,
+                              double lse, const int32_t *ids_t, const double *g,
+                              const double *dg, double *dp, double *dl) {
+  for (int64_t e = 0; e < E; e++) dp[e] = g_aux * alpha * (double)E * f[e] / (double)T;
+  double S = 0.0, sdg = 0.0;
+  for (int64_t j = 0; j < k; j++) {
+    S += p[ids_t[j]];
+    sdg += dg[j] * g[j];
+  }
+  for (int64_t j = 0; j < k; j++)
+    dp[ids_t[j]] += (k >= 2 && normalize) ? (dg[j] - sdg) / S : dg[j];
+  double pdp = 0.0;
+  for (int64_t e = 0; e < E; e++) pdp += p[e] * dp[e];
+  for (int64_t e = 0; e < E; e++)
+    dl[e] = p[e] * (dp[e] - pdp) + g_z * 2.0 / (double)T * lse * p[e];
 }
 
 int oracle_layer_backward(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
@@ -580,30 +603,21 @@ int oracle_layer_backward(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
 #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; t++) {
       const double *p = probs + t * E, *l = logits + t * E;
-      for (int64_t e = 0; e < E; e++) dp[e] = g_aux * alpha * (double)E * f[e] / (double)T;
-      double dg[64], S = 0.0, sdg = 0.0;
+      double dg[64];
       for (int64_t j = 0; j < k; j++) {
         const int64_t q = t * k + j;
         double v = 0.0;
         if (slots[q] >= 0)
           for (int64_t o = 0; o < D; o++) v += dy[t * D + o] * eo[q * D + o];
         dg[j] = v;
-        S += p[ids[q]];
-        sdg += v * gates[q];
       }
-      const int renorm = k >= 2 && normalize;
-      for (int64_t j = 0; j < k; j++)
-        dp[ids[t * k + j]] += renorm ? (dg[j] - sdg) / S : dg[j];
-      double pdp = 0.0;
-      for (int64_t e = 0; e < E; e++) pdp += p[e] * dp[e];
       double mx = l[0];
       for (int64_t e = 1; e < E; e++)
         if (l[e] > mx) mx = l[e];
       double se = 0.0;
       for (int64_t e = 0; e < E; e++) se += exp(l[e] - mx);
-      const double lse = mx + log(se);
-      for (int64_t e = 0; e < E; e++)
-        dlog[t * E + e] = p[e] * (dp[e] - pdp) + g_z * 2.0 / (double)T * lse * p[e];
+      router_token_grad(E, k, T, normalize, alpha, g_aux, g_z, f, p, mx + log(se), ids + t * k,
+                        gates + t * k, dg, dp, dlog + t * E);
     }
     free(dp);
   }
@@ -631,5 +645,130 @@ int oracle_layer_backward(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
 done:
   free(logits); free(probs); free(ids); free(gates); free(slots); free(drop); free(load);
   free(kept); free(eo); free(m); free(dense); free(y); free(f); free(dxa); free(dlog);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Selected entries of the layer backward, for checks at sizes where the
+ * whole backward is too slow: the chain rule of oracle_layer_backward
+ * restricted to
+ *   the dx rows of the tokens in `rows`, and
+ *   dW1[e][f][i] and dW2[e][o][f] entries listed as (e, ., .) triples,
+ * given the forward's discrete decisions ids and slots (for example another
+ * implementation's), with every continuous value (logits, probabilities,
+ * gates, expert activations and outputs) recomputed in fp64 from x and the
+ * weights; f (argmax fractions of the aux loss) from ids[t, 0].
+ * Plain weights only.  dy: T x D (every token's, the dW sums read them
+ * all); dx_rows: n_rows x D; dw1_vals, dw2_vals: one per triple.
+ * ---------------------------------------------------------------------- */
+/* probabilities, log-sum-exp and gates of token t under the given ids */
+static void token_gates(int64_t D, int64_t E, int64_t k, int normalize, const void *x, int fmt,
+                        const void *wr, const float *bias, const int32_t *ids, int64_t t,
+                        double *p, double *lse, double *g) {
+  double mx = -INFINITY;
+  for (int64_t e = 0; e < E; e++) {
+    double s = 0.0;
+    for (int64_t i = 0; i < D; i++) s += elem(x, fmt, t * D + i) * elem(wr, fmt, e * D + i);
+    if (bias) s += (double)bias[e];
+    p[e] = s;
+    if (s > mx) mx = s;
+  }
+  double z = 0.0;
+  for (int64_t e = 0; e < E; e++) z += exp(p[e] - mx);
+  *lse = mx + log(z);
+  for (int64_t e = 0; e < E; e++) p[e] = exp(p[e] - *lse);
+  double S = 0.0;
+  for (int64_t j = 0; j < k; j++) S += p[ids[t * k + j]];
+  for (int64_t j = 0; j < k; j++)
+    g[j] = (k >= 2 && normalize) ? p[ids[t * k + j]] / S : p[ids[t * k + j]];
+}
+
+int oracle_backward_sampled(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int64_t Fd,
+                            int normalize, int pr_moe, int add_skip, double alpha,
+                            const void *x, int fmt, const void *wr, const float *bias,
+                            const void *w1, const void *w2, const void *wm1, const void *wm2,
+                            const int32_t *ids, const int32_t *slots, const double *dy,
+                            double g_aux, double g_z, const int64_t *rows, int64_t n_rows,
+                            double *dx_rows, const int64_t *w1_idx, int64_t n_w1,
+                            double *dw1_vals, const int64_t *w2_idx, int64_t n_w2,
+                            double *dw2_vals) {
+  if (fmt == OR_I8 || k > 64) return -1;
+  const size_t es = fmt == OR_F64 ? 8 : (fmt == OR_F32 ? 4 : 2);
+  double *f = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+  for (int64_t t = 0; t < T; t++) f[ids[t * k]] += 1.0 / (double)T;
+  const int64_t Fm = F > Fd ? F : Fd;
+  int rc = 0;
+
+  /* dx rows */
+#pragma omp parallel
+  {
+    double *p = (double *)malloc((size_t)E * sizeof(double));
+    double *dp = (double *)malloc((size_t)E * sizeof(double));
+    double *dl = (double *)malloc((size_t)E * sizeof(double));
+    double *a = (double *)malloc((size_t)(Fm > 0 ? Fm : 1) * sizeof(double));
+    double *dh = (double *)malloc((size_t)(Fm > 0 ? Fm : 1) * sizeof(double));
+    double *o = (double *)malloc((size_t)D * sizeof(double));
+    double *dout = (double *)malloc((size_t)D * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_rows; n++) {
+      const int64_t t = rows[n];
+      double *dx = dx_rows + n * D;
+      const double *dyt = dy + t * D;
+      double lse, g[64], dg[64];
+      token_gates(D, E, k, normalize, x, fmt, wr, bias, ids, t, p, &lse, g);
+      for (int64_t i = 0; i < D; i++) dx[i] = add_skip ? dyt[i] : 0.0;
+      if (pr_moe) ffn_row_backward(D, Fd, x, fmt, t, wm1, wm2, dyt, a, dh, dx, NULL, NULL);
+      for (int64_t j = 0; j < k; j++) {
+        const int64_t q = t * k + j, e = ids[q];
+        dg[j] = 0.0;
+        if (slots[q] < 0) continue;
+        const void *w1e = (const char *)w1 + (size_t)(e * F * D) * es;
+        const void *w2e = (const char *)w2 + (size_t)(e * D * F) * es;
+        ffn_one_row(D, F, x, fmt, t, w1e, w2e, fmt, NULL, NULL, a, o);
+        for (int64_t i = 0; i < D; i++) dg[j] += dyt[i] * o[i];
+        for (int64_t i = 0; i < D; i++) dout[i] = g[j] * dyt[i];
+        ffn_row_backward(D, F, x, fmt, t, w1e, w2e, dout, a, dh, dx, NULL, NULL);
+      }
+      router_token_grad(E, k, T, normalize, alpha, g_aux, g_z, f, p, lse, ids + t * k, g, dg, dp,
+                        dl);
+      for (int64_t e = 0; e < E; e++)
+        for (int64_t i = 0; i < D; i++) dx[i] += dl[e] * elem(wr, fmt, e * D + i);
+    }
+    free(p); free(dp); free(dl); free(a); free(dh); free(o); free(dout);
+  }
+
+  /* expert weight-gradient entries: sums over the expert's kept assignments */
+#pragma omp parallel
+  {
+    double *p = (double *)malloc((size_t)E * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_w1 + n_w2; n++) {
+      const int is1 = n < n_w1;
+      const int64_t *ix = is1 ? w1_idx + 3 * n : w2_idx + 3 * (n - n_w1);
+      const int64_t e = ix[0];
+      const int64_t fi = is1 ? ix[1] : ix[2]; /* hidden unit */
+      const void *w1e = (const char *)w1 + (size_t)(e * F * D) * es;
+      const void *w2e = (const char *)w2 + (size_t)(e * D * F) * es;
+      double acc = 0.0, lse, g[64];
+      for (int64_t q = 0; q < T * k; q++) {
+        if (slots[q] < 0 || ids[q] != e) continue; /* kept rows of e */
+        const int64_t t = q / k, j = q % k;
+        token_gates(D, E, k, normalize, x, fmt, wr, bias, ids, t, p, &lse, g);
+        double av = 0.0;
+        for (int64_t i = 0; i < D; i++) av += elem(w1e, fmt, fi * D + i) * elem(x, fmt, t * D + i);
+        if (is1) { /* dW1[e][f][i] = sum da_f x_i, da_f = GELU'(a_f) sum_o W2[o][f] g dy[o] */
+          double s = 0.0;
+          for (int64_t o2 = 0; o2 < D; o2++) s += elem(w2e, fmt, o2 * F + fi) * g[j] * dy[t * D + o2];
+          acc += s * gelu_grad(av) * elem(x, fmt, t * D + ix[2]);
+        } else { /* dW2[e][o][f] = sum g dy[o] GELU(a_f) */
+          acc += g[j] * dy[t * D + ix[1]] * gelu(av);
+        }
+      }
+      if (is1) dw1_vals[n] = acc;
+      else dw2_vals[n - n_w1] = acc;
+    }
+    free(p);
+  }
+  free(f);
   return rc;
 }

@@ -120,3 +120,27 @@ def test_single_expert_reduces_to_torch_autograd():
     for ana, ref in ((g["dx"], tx.grad), (g["dw_router"], twr.grad), (g["dw1"][0], tw1.grad),
                      (g["dw2"][0], tw2.grad)):
         np.testing.assert_allclose(ana, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_sampled_entries_equal_the_full_backward(case):
+    # the restricted chain rule (used at full size) against the whole backward
+    T, D, E, F, Fd = 9, 6, 4, 5, 3
+    rng = np.random.default_rng(11)
+    p = _params(rng, T, D, E, F, Fd, case["pr"])
+    dy = rng.standard_normal((T, D))
+    kw = dict(k=case["k"], bias=p["b"], wm1=p.get("wm1"), wm2=p.get("wm2"),
+              normalize=case["normalize"], pr_moe=case["pr"], add_skip=case["skip"],
+              alpha=0.7, g_aux=0.3, g_z=0.2)
+    fw = oracle.layer_forward(p["x"], p["wr"], p["w1"], p["w2"], capacity_factor=1.0,
+                              capacity_override=case["C"], policy=case["policy"],
+                              **{k: v for k, v in kw.items() if k not in ("g_aux", "g_z")})
+    full = oracle.layer_backward(p["x"], p["wr"], p["w1"], p["w2"], dy, capacity_factor=1.0,
+                                 capacity_override=case["C"], policy=case["policy"], **kw)
+    i1 = [(e, f, i) for e in range(E) for f in range(F) for i in range(D)]
+    i2 = [(e, o, f) for e in range(E) for o in range(D) for f in range(F)]
+    s = oracle.backward_sampled(p["x"], p["wr"], p["w1"], p["w2"], fw["ids"], fw["slots"], dy,
+                                np.arange(T), dw1_idx=i1, dw2_idx=i2, **kw)
+    np.testing.assert_allclose(s["dx"], full["dx"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s["dw1"], full["dw1"].ravel(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s["dw2"], full["dw2"].ravel(), rtol=1e-11, atol=1e-12)

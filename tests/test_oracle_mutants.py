@@ -21,7 +21,7 @@ MUTANTS = {
                             "if (best < 0 || l[e] >= l[best]) best = e;"),
     "softmax_sign": ("p[e] = exp(l[e] - m);", "p[e] = exp(m - l[e]);"),
     "softmax_unnormalised": ("for (int64_t e = 0; e < E; e++) p[e] /= z;", ""),
-    "topk_not_renormalised": ("(k >= 2 && normalize) ?", "(0) ?"),
+    "topk_not_renormalised": ("g[j] = (k >= 2 && normalize) ? p[sel[j]]", "g[j] = (0) ? p[sel[j]]"),
     "aux_uses_last_choice": ("f[ids[t * k]] += 1.0;", "f[ids[t * k + k - 1]] += 1.0;"),
     "aux_missing_N": ("loss *= alpha * (double)E;", "loss *= alpha;"),
     "capacity_floor": ("c = (int64_t)ceil(", "c = (int64_t)floor("),
@@ -43,8 +43,8 @@ MUTANTS = {
     "bwd_gelu_grad_missing_term": (
         "return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * inv_sqrt_2pi * exp(-0.5 * z * z);",
         "return 0.5 * (1.0 + erf(z / sqrt(2.0)));"),
-    "bwd_renorm_without_correction": ("renorm ? (dg[j] - sdg) / S : dg[j]",
-                                      "renorm ? dg[j] / S : dg[j]"),
+    "bwd_renorm_without_correction": ("normalize) ? (dg[j] - sdg) / S : dg[j]",
+                                      "normalize) ? dg[j] / S : dg[j]"),
     "bwd_dropped_get_gradient": ("if (ids[q] != e || slots[q] < 0) continue;",
                                  "if (ids[q] != e) continue;"),
     "bwd_aux_gradient_dropped": (
