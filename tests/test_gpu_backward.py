@@ -115,3 +115,49 @@ def test_backward_rejects_unsupported_and_missing_outputs():
     with pytest.raises(binding.MoeError, match="invalid"):
         binding.moe_layer_backward(cfg2, inp2["x"], inp2, out2, dy, binding.alloc_grads(cfg2, DEV),
                                    binding.alloc_workspace(cfg2, binding.ENTRY_BACKWARD))
+
+
+@pytest.mark.parametrize("name", ["prmoe128_1p3b", "moe128_350m"])
+def test_full_size_backward_sampled(name):
+    # the workload at full size, in bench.py's launch configuration; the oracle
+    # recomputes sampled dx rows and expert weight-gradient entries under the
+    # GPU forward's routing decisions
+    wl = workloads.WORKLOADS[name]
+    print(f"[full_size_backward] {name}", flush=True)
+    g_aux, g_z = 0.01, 0.001
+    inp = synth.make_inputs(wl, seed=0, device=DEV)
+    cfg = binding.config_of(wl)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True)
+    binding.moe_layer_forward(cfg, inp["x"], inp, out, binding.alloc_workspace(cfg))
+    dy = synth.normal((wl.T, wl.d), 1.0, 5, "dy", DEV, torch.bfloat16)
+    grads = binding.alloc_grads(cfg, DEV)
+    binding.moe_layer_backward(cfg, inp["x"], inp, out, dy, grads,
+                               binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD),
+                               g_aux=g_aux, g_z=g_z)
+    torch.cuda.synchronize()
+    ids, slots, kept = to_np(out.expert_ids), to_np(out.slots), to_np(out.kept)
+    rng = np.random.default_rng(0)
+    dropped = np.nonzero((slots < 0).any(axis=1))[0]
+    rows = sorted(set(rng.choice(wl.T, size=6, replace=False).tolist()) |
+                  set(dropped[:2].tolist()))
+    experts = rng.choice(np.nonzero(kept > 0)[0], size=2, replace=False)
+    i1 = [(int(e), int(rng.integers(wl.d_ff)), int(rng.integers(wl.d))) for e in experts
+          for _ in range(6)]
+    i2 = [(int(e), int(rng.integers(wl.d)), int(rng.integers(wl.d_ff))) for e in experts
+          for _ in range(6)]
+    cpu = {k: (None if v is None else v.cpu()) for k, v in inp.items()}
+    s = oracle.backward_sampled(cpu["x"], cpu["w_router"], cpu["w1"], cpu["w2"], ids, slots,
+                                dy.double().cpu().numpy(), rows, k=wl.k, bias=cpu["b_router"],
+                                wm1=cpu["wm1"], wm2=cpu["wm2"], normalize=wl.normalize_topk,
+                                pr_moe=wl.pr_moe, add_skip=wl.add_skip, alpha=wl.aux_alpha,
+                                g_aux=g_aux, g_z=g_z, dw1_idx=i1, dw2_idx=i2)
+    tau = TAU["bf16"]
+    check_close("dx rows", grads.dx[rows], s["dx"], tau)
+    for name_w, idx, vals in (("dw1", i1, s["dw1"]), ("dw2", i2, s["dw2"])):
+        g = getattr(grads, name_w)
+        for (e, a, b), ref in zip(idx, vals):
+            scale = float(g[e].abs().max())
+            got = float(g[e, a, b])
+            assert abs(got - ref) <= tau * scale, f"{name_w}[{e},{a},{b}]: {got} vs {ref}"
+    del inp, cpu, grads, out
+    torch.cuda.empty_cache()
