@@ -400,6 +400,160 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradients of the experts, whose reduction runs over the expert's
+// kept rows only (K <= KR <= 128):  C(g, m, n) = sum_{k < kvalid} A(g, m, k)
+// B(g, n, k), both operands K-major.  A workgroup owns a 128-row panel of C
+// and one of nsplit equal ranges of its 128-column tiles: it loads the
+// panel's A slab (KR rows of 128 elements, as stored) once, keeps its MFMA
+// fragments in registers, and streams the B slabs of its tiles through two
+// LDS stages by DMA, one tile ahead.  The MFMA runs with the operands' roles
+// exchanged (B slab rows as the first operand), so each lane ends with four
+// consecutive columns of one row of C; every wave stages its 64 x 64 block
+// in a private LDS patch and stores it as whole 128-byte row segments.  The
+// stores drain while the next tile computes: the one barrier per tile orders
+// LDS only, and the wait for a B slab lets this wave's eight stores of the
+// previous tile stay in flight (a wave's vector memory operations complete
+// in issue order).  Panels start their sweeps at different tiles (panel tm
+// at tile tm of its range), so the workgroups running at once read
+// different B slabs and write different column ranges instead of all
+// hitting the same few L2 channels.  Reduction rows past kvalid: B rows are
+// loaded from row kvalid - 1 (finite values) and the matching A rows are
+// zeroed in LDS, so they add exactly zero.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int swz_patch(int m) { return (m >> 1) & 7; }
+
+template <int KR>
+__global__ __launch_bounds__(256) void gemm_dwk_kernel(GenArgs a) {
+  constexpr int BM = 128, BN = 128;
+  constexpr int SLAB = KR * 256;  // bytes of a K-major slab of 128 columns
+  constexpr int CH = KR / 16;     // 1-KB DMA chunks per wave per slab
+  constexpr int PATCH = 64 * 128;
+  constexpr int STORES = PATCH / (kWave * 16);  // 16-byte stores per lane per tile
+  constexpr int KS = KR / 16;                   // MFMA reduction steps
+  static_assert(3 * SLAB + 4 * PATCH <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[3 * SLAB + 4 * PATCH];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 2, wn = wave % 2;
+  const int tiles_m = (int)(a.M / BM), S = a.nsplit;
+  const int tiles_n = a.N / BN / S;  // tiles of this workgroup's range
+  const int per_group = tiles_m * S;
+  const int blk = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, per_group)
+                                 : xcd_remap(blockIdx.x, a.G * per_group);
+  const int g = blk / per_group, rr = blk - g * per_group;
+  const int tm = rr / S, t0 = (rr - tm * S) * tiles_n;  // panel, first tile of the range
+  const int64_t m0 = (int64_t)tm * BM;
+  int kvalid = (int)a.K;
+  if (a.krows && a.krows[g] < kvalid) kvalid = a.krows[g];
+  bf16 *Cg = a.C + (int64_t)g * a.c_g + m0 * a.c_m + (int64_t)t0 * BN;
+  if (kvalid <= 0) {  // no kept rows: the gradient is zero
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int per_row = tiles_n * BN / 8;
+    for (int r = 0; r < BM; r++)
+      for (int c = tid; c < per_row; c += 256) *(u32x4 *)(Cg + (int64_t)r * a.c_m + 8 * c) = z;
+    return;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  const uint32_t lds_a = lds0, lds_b = lds0 + SLAB;
+  char *patch = smem + 3 * SLAB + wave * PATCH;
+
+  // chunk q = CH * wave + i holds k rows 4q .. 4q + 3; lane: row 4q + lane / 16,
+  // slot lane % 16, which holds the row's 16-byte chunk slot ^ swz_km(k)
+  uint32_t voa[CH], vob[CH];
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int k = 4 * (CH * wave + i) + lane / 16, slot = lane % 16;
+    const int kk = k < kvalid ? k : kvalid - 1;
+    const uint32_t c16 = (uint32_t)((slot ^ swz_km(k)) << 4);
+    voa[i] = (uint32_t)(kk * a.a_k * 2) + c16;
+    vob[i] = (uint32_t)(kk * a.b_k * 2) + c16;
+  }
+  const char *abase = (const char *)(a.A + (int64_t)g * a.a_g + m0);
+  const char *bbase = (const char *)(a.B + (int64_t)g * a.b_g + (int64_t)t0 * BN);
+  // the i-th tile of the sweep (staggered start) and its B slab into stage i & 1
+  auto tile_of = [&](int i) { return (i + tm) % tiles_n; };
+  auto issue_b = [&](int i) __attribute__((always_inline)) {
+    const char *gb = bbase + (int64_t)tile_of(i) * BN * 2;
+    const uint32_t st = lds_b + (i & 1) * SLAB;
+#pragma unroll
+    for (int c = 0; c < CH; c++)
+      dma16<false>(gb, vob[c], __builtin_amdgcn_readfirstlane(st + (CH * wave + c) * 1024));
+  };
+#pragma unroll
+  for (int i = 0; i < CH; i++)
+    dma16<false>(abase, voa[i], __builtin_amdgcn_readfirstlane(lds_a + (CH * wave + i) * 1024));
+  issue_b(0);
+  wait_vmcnt<0>();
+  lds_barrier();  // every wave's part has landed
+  // A rows kvalid .. KR - 1 (loaded from row kvalid - 1) become zero
+  for (int idx = tid; idx < (KR - kvalid) * 16; idx += 256) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *(u32x4 *)(smem + (kvalid + idx / 16) * 256 + (idx % 16) * 16) = z;
+  }
+  lds_barrier();
+  bf16x8 af[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; s++)
+#pragma unroll
+    for (int i = 0; i < 2; i++) af[s][i] = frag_kmajor(lds_a, wm * 64 + i * 32, 16 * s, lane);
+
+  for (int it = 0; it < tiles_n; it++) {
+    if (it > 0) {
+      wait_vmcnt<STORES>();  // newer than slab it's DMA: this wave's stores of tile it - 1
+      lds_barrier();         // every wave's part of slab it; stage (it + 1) & 1 free
+    }
+    if (it + 1 < tiles_n) issue_b(it + 1);
+    const uint32_t tb = lds_b + (it & 1) * SLAB;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      bf16x8 bfr[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++) bfr[j] = frag_kmajor(tb, wn * 64 + j * 32, 16 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)  // D[n][m]: rows from the B slab
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[s][i], acc[i][j], 0, 0, 0);
+    }
+    // lane: row m = 32 i + lane % 32 of the wave's block, columns
+    // 32 j + 8 q + 4 (lane / 32) + 0..3 from registers 4 q .. 4 q + 3
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int m = 32 * i + (lane & 31), c = 4 * j + q;
+          bf16x4v v;
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = (bf16)acc[i][j][4 * q + e];
+          *(bf16x4v *)(patch + m * 128 + ((c ^ swz_patch(m)) << 4) + 8 * (lane >> 5)) = v;
+        }
+    asm volatile("" ::: "memory");  // the wave's LDS operations run in order
+    bf16 *Ct = Cg + (int64_t)(wm * 64) * a.c_m + tile_of(it) * BN + wn * 64;
+#pragma unroll
+    for (int p = 0; p < STORES; p++) {
+      const int R = 8 * p + lane / 8, c = lane % 8;
+      const u32x4 v = *(const u32x4 *)(patch + R * 128 + ((c ^ swz_patch(R)) << 4));
+      __builtin_nontemporal_store(v, (u32x4 *)(Ct + (int64_t)R * a.c_m + 8 * c));
+    }
+    asm volatile("" ::: "memory");  // the stores stay ahead of the next wait
+  }
+}
+
 // H = GELU(Z), elementwise (bf16)
 __global__ __launch_bounds__(256) void gelu_map_kernel(const bf16 *z, bf16 *h, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -603,6 +757,35 @@ static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t 
   return hipGetLastError();
 }
 
+// N splits: about eight tiles per workgroup and at most ~128 workgroups per
+// group (measured on MI355X: fewer, longer sweeps lose the group's operands
+// from L2; shorter ones pay the A slab again per few tiles)
+template <int KR>
+static hipError_t launch_dwk_t(const GenArgs &a0, const char *role, hipStream_t s) {
+  GenArgs a = a0;
+  const int tiles_m = (int)(a.M / 128), tiles_n = a.N / 128;
+  a.nsplit = 1;
+  while (tiles_n % (2 * a.nsplit) == 0 && tiles_n / (2 * a.nsplit) >= 8 &&
+         tiles_m * 2 * a.nsplit <= 128)
+    a.nsplit *= 2;
+  const int64_t blocks = (int64_t)a.G * tiles_m * a.nsplit;
+  if (blocks <= 0 || a.N <= 0) return hipGetLastError();
+  MOE_LAUNCH(intern_name(role, KR == 128 ? "dwk128" : (KR == 64 ? "dwk64" : "dwk32")),
+             gemm_dwk_kernel<KR>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// the short-reduction weight-gradient kernel: both operands K-major with
+// 16-byte aligned rows, M and N multiples of 128, K <= 128 rows in memory,
+// 16-byte aligned output rows
+static bool dwk_ok(const GenArgs &a, bool akm, bool bkm, bool dgelu) {
+  if (!akm || !bkm || dgelu || a.K <= 0 || a.K > 128) return false;
+  if (a.M % 128 || a.N % 128 || a.a_kmax < a.K || a.b_kmax < a.K) return false;
+  if (a.a_k % 8 || a.b_k % 8 || a.c_m % 8 || a.a_g % 8 || a.b_g % 8 || a.c_g % 8) return false;
+  if (a.a_k * 2 * 128 >= (int64_t(1) << 31) || a.b_k * 2 * 128 >= (int64_t(1) << 31)) return false;
+  return a.G * (a.M / 128) * (a.N / 128) < (int64_t(1) << 31);
+}
+
 // the DMA kernel needs 128-multiples for M and N, K a multiple of 32, a
 // whole K for K-contiguous operands, K-major extents that cover the rounded-up
 // K, 16-byte aligned rows, and per-lane offsets below 2^32
@@ -621,6 +804,11 @@ static bool dmag_ok(const GenArgs &a, bool akm, bool bkm) {
 // a_kmajor / b_kmajor: which operand layouts; dgelu: epilogue
 hipError_t launch_gemm_gen(const GenArgs &a, bool a_kmajor, bool b_kmajor, bool dgelu,
                            const char *role, hipStream_t s) {
+  if (dwk_ok(a, a_kmajor, b_kmajor, dgelu)) {
+    if (a.K <= 32) return launch_dwk_t<32>(a, role, s);
+    if (a.K <= 64) return launch_dwk_t<64>(a, role, s);
+    return launch_dwk_t<128>(a, role, s);
+  }
   if (dmag_ok(a, a_kmajor, b_kmajor)) {
     if (!a_kmajor && b_kmajor && dgelu) return launch_dmag_t<false, true, true>(a, role, s);
     if (!a_kmajor && b_kmajor) return launch_dmag_t<false, true, false>(a, role, s);

@@ -47,6 +47,7 @@ struct GenArgs {
   const int32_t *krows;  // [G] valid reduction length (clamped to K) or null
   int64_t K;
   int N, G;
+  int nsplit;  // short-reduction weight-gradient kernel: N sweeps per row panel (set by the launcher)
 };
 
 }  // namespace moe

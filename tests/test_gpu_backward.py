@@ -33,6 +33,8 @@ CASES = [
     W("bwd_dma_top1_pr", T=1024, d=256, E=8, k=1, d_ff=512, capacity_factor=1.0,
       d_ff_dense=256, pr_moe=True, add_skip=True),
     W("bwd_dma_top2", T=512, d=384, E=8, k=2, d_ff=256, capacity_factor=1.0, zipf_s=0.5),
+    # d_ff = 2048: the expert dW2 sweep over 16 column tiles is split in two
+    W("bwd_split_sweep", T=512, d=256, E=8, k=2, d_ff=2048, capacity_factor=1.0, zipf_s=0.3),
 ]
 
 
