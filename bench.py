@@ -2,12 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--copy-calibration GIB]
+                    [--backward | --train] [--recompute]
     python bench.py --pmc-summary FETCH.csv WRITE.csv --label L --symbol RE
                     --workload NAME --copy-gib G --command "..."   (no GPU)
 
 A step is one moe_layer_forward (router + softmax/top-k + aux loss, dispatch,
 PR-MoE dense MLP, expert FFNs, combine) over one batch of seeded synthetic
-tokens already resident in HBM.  The default workload is the 1.3B+PR-MoE-128
+tokens already resident in HBM (--backward: one moe_layer_backward of that
+forward; --train: forward keeping the FFN activations, then the backward).
+The default workload is the 1.3B+PR-MoE-128
 layer (T=16384, d=2048, E=128 top-1 experts with d_ff=8192 plus a dense MLP
 with d_ff=8192, bf16); the other workloads are parity cases and can be timed
 with --workload.  One JSON line is printed:
@@ -64,6 +67,11 @@ def parse():
     p.add_argument("--z-loss", action="store_true", help="also compute the router z-loss")
     p.add_argument("--backward", action="store_true",
                    help="time the layer backward (after one forward) instead of the forward")
+    p.add_argument("--train", action="store_true",
+                   help="time forward (keeping the FFN activations) + backward as one step")
+    p.add_argument("--recompute", action="store_true",
+                   help="backward / train: do not keep the FFN activations in the forward; "
+                        "the backward recomputes them")
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
@@ -302,23 +310,31 @@ def main():
     inp = synth.make_inputs(wl, seed=args.seed, device=dev)
     cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy)
     C = binding.capacity(cfg)
-    out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss, logits=args.backward,
-                                x_disp=args.backward, y_disp=args.backward)
+    bwd = args.backward or args.train
+    out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss, logits=bwd, x_disp=bwd,
+                                y_disp=bwd, saved_activations=bwd and not args.recompute)
     ws = binding.alloc_workspace(cfg, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def forward():
         binding.moe_layer_forward(cfg, inp["x"], inp, out, ws, stream)
 
-    if args.backward:
-        step()  # the forward whose outputs the backward reads
+    step = forward
+    if bwd:
+        forward()  # the forward whose outputs the backward reads
         dy = synth.normal((wl.T, wl.d), 1.0, args.seed + 1, "dy", dev, torch.bfloat16)
         grads = binding.alloc_grads(cfg, dev)
         ws_b = binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD, device=dev)
 
-        def step():  # noqa: F811
+        def backward():
             binding.moe_layer_backward(cfg, inp["x"], inp, out, dy, grads, ws_b, g_aux=0.01,
                                        g_z=0.001, stream=stream)
+
+        def train_step():
+            forward()
+            backward()
+
+        step = train_step if args.train else backward
 
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * (1 << 30))
@@ -385,7 +401,8 @@ def main():
     roof["algorithmic_flops"] = wk["flops"]
 
     res = {
-        "metric": METRIC if not args.backward else "MoE-layer backward tokens/s",
+        "metric": ("MoE-layer training (forward + backward) tokens/s" if args.train else
+                   "MoE-layer backward tokens/s" if args.backward else METRIC),
         "value": round(wl.T * args.steps / elapsed, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -397,7 +414,9 @@ def main():
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
                    "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
-                   "pass": "backward" if args.backward else "forward",
+                   "pass": "train" if args.train else "backward" if args.backward else "forward",
+                   **({"ffn_activations": "recomputed" if args.recompute else "saved"}
+                      if bwd else {}),
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
@@ -405,7 +424,7 @@ def main():
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not args.backward:
+    if not args.no_cpu_baseline and not bwd:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(res))

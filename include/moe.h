@@ -132,6 +132,12 @@ typedef struct moe_outputs {
   void *y_disp;        /* [E, C, d] act; NULL = in the workspace */
   void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
   float *z_loss;       /* [1] router z-loss                     optional */
+  /* Activations a training forward keeps for moe_layer_backward (each
+   * optional; the rows past an expert's kept count are not written):   */
+  void *h_disp;        /* [E, C, d_ff] act GELU(W1 x) of the kept rows; NULL = workspace */
+  void *z_disp;        /* [E, C, d_ff] act W1 x, the pre-activation; NULL = not kept */
+  void *h_dense;       /* [T, d_ff_dense] act GELU(Wm1 x) (pr_moe); NULL = workspace */
+  void *z_dense;       /* [T, d_ff_dense] act Wm1 x (pr_moe); NULL = not kept */
 } moe_outputs;
 
 typedef struct moe_grads {
@@ -225,7 +231,9 @@ int moe_layer_forward(const moe_config *cfg, const void *x,
  * x, w: as given to the forward.  fwd: the forward's outputs for the same
  * cfg, x and w; expert_ids, gates, slots, logits, x_disp and y_disp are
  * required (so the forward must have been run with caller-owned logits,
- * x_disp and y_disp).  dy [T, d] act.
+ * x_disp and y_disp).  When the forward also kept z_disp and h_disp (and
+ * z_dense and h_dense for PR-MoE), the backward reads them instead of
+ * recomputing W1 x and GELU(W1 x).  dy [T, d] act.
  * Out: grads (written, not accumulated); the weight gradients are in the
  * activation type, accumulated in fp32.  bf16 activations and plain expert
  * weights only (MOE_ERR_UNSUPPORTED otherwise).  Workspace:

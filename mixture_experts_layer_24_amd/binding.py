@@ -64,7 +64,8 @@ class Grads(ctypes.Structure):
 class Outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("y", "expert_ids", "gates", "slots", "load", "kept", "aux_loss", "drop_mask",
-                 "logits", "x_disp", "y_disp", "dense_out", "z_loss")]
+                 "logits", "x_disp", "y_disp", "dense_out", "z_loss", "h_disp", "z_disp",
+                 "h_dense", "z_dense")]
 
 
 _lock = threading.Lock()
@@ -292,10 +293,17 @@ class LayerOutputs:
     y_disp: torch.Tensor | None = None
     dense_out: torch.Tensor | None = None
     z_loss: torch.Tensor | None = None
+    h_disp: torch.Tensor | None = None   # [E, C, d_ff] GELU(W1 x), kept rows
+    z_disp: torch.Tensor | None = None   # [E, C, d_ff] W1 x
+    h_dense: torch.Tensor | None = None  # [T, d_ff_dense] (pr_moe)
+    z_dense: torch.Tensor | None = None
 
 
 def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
-                  x_disp=False, y_disp=False, dense_out=False, z_loss=False) -> LayerOutputs:
+                  x_disp=False, y_disp=False, dense_out=False, z_loss=False,
+                  saved_activations=False) -> LayerOutputs:
+    """saved_activations: also keep the FFN hidden activations and their
+    pre-activations, which the backward then reads instead of recomputing."""
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     C = capacity(cfg)
     a = _act_dtype(cfg)
@@ -308,7 +316,11 @@ def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
         logits=e(T, E, dt=torch.float32) if logits else None,
         x_disp=e(E, C, d) if x_disp else None, y_disp=e(E, C, d) if y_disp else None,
         dense_out=e(T, d) if (dense_out and cfg.pr_moe) else None,
-        z_loss=e(1, dt=torch.float32) if z_loss else None)
+        z_loss=e(1, dt=torch.float32) if z_loss else None,
+        h_disp=e(E, C, cfg.d_ff) if saved_activations else None,
+        z_disp=e(E, C, cfg.d_ff) if saved_activations else None,
+        h_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None,
+        z_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None)
 
 
 def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):
@@ -399,7 +411,11 @@ def _outputs_struct(cfg, out: LayerOutputs) -> Outputs:
         x_disp=_ptr(out.x_disp, (E, C, d), a, "x_disp", True),
         y_disp=_ptr(out.y_disp, (E, C, d), a, "y_disp", True),
         dense_out=_ptr(out.dense_out, (T, d), a, "dense_out", True),
-        z_loss=_ptr(out.z_loss, (1,), torch.float32, "z_loss", True))
+        z_loss=_ptr(out.z_loss, (1,), torch.float32, "z_loss", True),
+        h_disp=_ptr(out.h_disp, (E, C, cfg.d_ff), a, "h_disp", True),
+        z_disp=_ptr(out.z_disp, (E, C, cfg.d_ff), a, "z_disp", True),
+        h_dense=_ptr(out.h_dense, (T, cfg.d_ff_dense), a, "h_dense", True),
+        z_dense=_ptr(out.z_dense, (T, cfg.d_ff_dense), a, "z_dense", True))
 
 
 # ------------------------------------------------------------------ profiling

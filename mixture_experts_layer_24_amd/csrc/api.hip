@@ -216,13 +216,14 @@ hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *id
                                  c->d * (int64_t)act_size(c), x_disp, s);
 }
 
+// hidden: GELU(W1 x) of the kept rows; zpre: W1 x itself, or null (not kept)
 hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t *kept,
                          const void *w1, const void *s1, const void *w2, const void *s2,
-                         void *y_disp, void *hidden, hipStream_t s) {
+                         void *y_disp, void *hidden, hipStream_t s, void *zpre = nullptr) {
   const int64_t C = capacity_of(c);
   if (C == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
-  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E};
+  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre};
   hipError_t e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
   if (e != hipSuccess) return e;
   GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E};
@@ -230,10 +231,10 @@ hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t 
 }
 
 hipError_t do_dense(const moe_config *c, const void *x, const void *wm1, const void *wm2,
-                    void *out, void *hidden, hipStream_t s) {
+                    void *out, void *hidden, hipStream_t s, void *zpre = nullptr) {
   if (c->T == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16;
-  GemmArgs g1{x, wm1, nullptr, hidden, nullptr, c->T, (int)c->d_ff_dense, (int)c->d, 1};
+  GemmArgs g1{x, wm1, nullptr, hidden, nullptr, c->T, (int)c->d_ff_dense, (int)c->d, 1, zpre};
   hipError_t e = moe_host::launch_gemm(g1, bf, 0, 1, "dense_mlp1", s);
   if (e != hipSuccess) return e;
   GemmArgs g2{hidden, wm2, nullptr, out, nullptr, c->T, (int)c->d, (int)c->d_ff_dense, 1};
@@ -445,7 +446,8 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
       !need(out->slots, Tk, 4) || !need(out->load, 1, 4) || !need(out->kept, 1, 4) ||
       !need(out->aux_loss, 1, 4) || !opt(out->drop_mask, 1) || !opt(out->logits, 4) ||
       !opt(out->x_disp, 16) || !opt(out->y_disp, 16) || !opt(out->dense_out, 16) ||
-      !opt(out->z_loss, 4))
+      !opt(out->z_loss, 4) || !opt(out->h_disp, 16) || !opt(out->z_disp, 16) ||
+      !opt(out->h_dense, 16) || !opt(out->z_dense, 16))
     return MOE_ERR_INVALID_ARG;
   (void)rowsE;
   rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
@@ -457,9 +459,13 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   int32_t *offs = (int32_t *)at(ws, L.offs);
   void *x_disp = out->x_disp ? out->x_disp : at(ws, L.x_disp);
   void *y_disp = out->y_disp ? out->y_disp : at(ws, L.y_disp);
-  void *hidden = at(ws, L.hidden);
-  void *dense = nullptr;
-  if (cfg->pr_moe) dense = out->dense_out ? out->dense_out : at(ws, L.dense);
+  void *hidden = out->h_disp ? out->h_disp : at(ws, L.hidden);
+  void *dense = nullptr, *hidden_dense = nullptr;
+  if (cfg->pr_moe) {
+    dense = out->dense_out ? out->dense_out : at(ws, L.dense);
+    hidden_dense = out->h_dense ? out->h_dense : at(ws, L.hidden_dense);
+  }
+  void *zd = cfg->pr_moe ? out->z_dense : nullptr;
 
   hipError_t e = hipSuccess;
   // fork: the dense MLP on the side stream
@@ -471,10 +477,10 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
     if (e == hipSuccess) e = hipEventRecord(side->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     if (e == hipSuccess)
-      e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), side->s);
+      e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden_dense, side->s, zd);
     if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
   } else if (cfg->pr_moe) {
-    e = do_dense(cfg, x, w->wm1, w->wm2, dense, at(ws, L.hidden_dense), s);
+    e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden_dense, s, zd);
   }
   double *term = (double *)at(ws, L.term);
   if (e == hipSuccess)
@@ -490,7 +496,7 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
                         out->slots, out->drop_mask, term, out->aux_loss, x_disp, s);
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
-                      hidden, s);
+                      hidden, s, out->z_disp);
   // join: the combine reads D(x)
   if (e == hipSuccess && side) e = hipStreamWaitEvent(s, side->join, 0);
   if (e == hipSuccess)
@@ -516,7 +522,8 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
     return MOE_ERR_INVALID_ARG;
   if (!need(fwd->expert_ids, Tk, 4) || !need(fwd->gates, Tk, 4) || !need(fwd->slots, Tk, 4) ||
       !need(fwd->logits, T, 4) || !need(fwd->x_disp, E * C, 16) || !need(fwd->y_disp, E * C, 16) ||
-      !need(dy, T, 16))
+      !need(dy, T, 16) || !opt(fwd->z_disp, 16) || !opt(fwd->h_disp, 16) ||
+      !opt(fwd->z_dense, 16) || !opt(fwd->h_dense, 16))
     return MOE_ERR_INVALID_ARG;
   if (!need(gr->dx, T, 16) || !need(gr->dw_router, 1, 16) || !opt(gr->db_router, 4) ||
       !need(gr->dw1, 1, 16) || !need(gr->dw2, 1, 16) ||
@@ -561,12 +568,17 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
     a.N = (int)d; a.G = 1;
     e = moe_host::launch_gemm_gen(a, true, true, false, "bwd_router_dw", s);
   }
-  // experts
-  if (e == hipSuccess && C > 0) {
-    GemmArgs z{xd, w->w1, nullptr, Z, kept, C, (int)F, (int)d, (int)E};
-    e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_expert_z", s);
+  // experts: the forward's saved W1 x and GELU(W1 x), else recomputed
+  if (fwd->z_disp && fwd->h_disp) {
+    Z = (bf16 *)fwd->z_disp;
+    H = (bf16 *)fwd->h_disp;
+  } else {
+    if (e == hipSuccess && C > 0) {
+      GemmArgs z{xd, w->w1, nullptr, Z, kept, C, (int)F, (int)d, (int)E};
+      e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_expert_z", s);
+    }
+    if (e == hipSuccess) e = moe_host::launch_gelu_map(Z, H, E * C * F, s);
   }
-  if (e == hipSuccess) e = moe_host::launch_gelu_map(Z, H, E * C * F, s);
   if (e == hipSuccess && C > 0) {  // dZ = (dY W2) * GELU'(Z)
     GenArgs a{};
     a.A = dY; a.a_g = C * d; a.a_m = d; a.a_k = 1;
@@ -604,11 +616,16 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
   if (pr && e == hipSuccess) {
     bf16 *Zd = (bf16 *)at(ws, L.Zd), *Hd = (bf16 *)at(ws, L.Hd), *dZd = (bf16 *)at(ws, L.dZd);
     dxd = (bf16 *)at(ws, L.dxd);
-    if (T > 0) {
-      GemmArgs z{x, w->wm1, nullptr, Zd, nullptr, T, (int)Fd, (int)d, 1};
-      e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_dense_z", s);
+    if (fwd->z_dense && fwd->h_dense) {
+      Zd = (bf16 *)fwd->z_dense;
+      Hd = (bf16 *)fwd->h_dense;
+    } else {
+      if (T > 0) {
+        GemmArgs z{x, w->wm1, nullptr, Zd, nullptr, T, (int)Fd, (int)d, 1};
+        e = moe_host::launch_gemm(z, 1, 0, 0, "bwd_dense_z", s);
+      }
+      if (e == hipSuccess) e = moe_host::launch_gelu_map(Zd, Hd, T * Fd, s);
     }
-    if (e == hipSuccess) e = moe_host::launch_gelu_map(Zd, Hd, T * Fd, s);
     if (e == hipSuccess && T > 0) {
       GenArgs a{};
       a.A = dyb; a.a_m = d; a.a_k = 1;

@@ -34,7 +34,7 @@
 
 namespace moe {
 
-template <int BM, int BN, int WM, int WN, int MF, bool BINT8, bool GELU>
+template <int BM, int BN, int WM, int WN, int MF, bool BINT8, int GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = 64 * WM * WN;
   constexpr int BK = 64;
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
   const int8_t *Bq = (const int8_t *)a.B + (int64_t)g * N * K;
   const _Float16 *Sg = (const _Float16 *)a.Bscale + (int64_t)g * N * (K / 128);
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+  bf16 *Zg = GELU == 2 ? (bf16 *)a.Zpre + (int64_t)g * a.M_cap * N : nullptr;
 
   u32x4 ra[A_PT], rb[B_PT];
   float rs[BINT8 ? B_PT : 1];
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
         const int64_t m = m0 + wm * WTM + i * MF + mr;
         const int n = n0 + wn * WTN + j * MF + nc;
         float v = acc[i][j][r];
+        if (GELU == 2 && m < rows) Zg[m * N + n] = (bf16)v;
         if (GELU) v = gelu_f(v);
         if (m < rows) Cg[m * N + n] = (bf16)v;
       }
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 // barrier that publishes a stage, because the compiler would otherwise wait
 // for every outstanding load before each LDS read.
 // NTB: load the weight operand non-temporally (read once)
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, bool GELU>
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, int GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   static_assert(BK == 64 || BK == 32, "K step");
   constexpr int W = WM * WN;
@@ -278,6 +280,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   const char *Abase = (const char *)a.A + ((int64_t)g * a.M_cap + m0) * K * 2;
   const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K * 2;
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+  bf16 *Zg = GELU == 2 ? (bf16 *)a.Zpre + (int64_t)g * a.M_cap * N : nullptr;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
   // Every wave moves A_PW chunks of the activation tile and B_PW chunks of
@@ -364,6 +367,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
+  // pass 0 writes C; with the pre-activation output (GELU == 2), pass 1 writes Zpre
+  for (int pass = 0; pass < (GELU == 2 ? 2 : 1); pass++)
   for (int band = 0; band < WM; band++) {
     __syncthreads();  // stage buffers (or the previous band) no longer read
     if (wm == band) {
@@ -376,17 +381,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
             const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int Cc = wn * WTN + j * 32 + (lane & 31);
             float v = acc[i][j][r];
-            if (GELU) v = gelu_f(v);
+            if (GELU && pass == 0) v = gelu_f(v);
             *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
           }
     }
     __syncthreads();
+    bf16 *Og = pass ? Zg : Cg;
     const int64_t r0 = m0 + band * WTM;
     const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
     for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
       const int R = idx / OCPR, ch = idx - R * OCPR;
       if (R < mrows)
-        *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+        *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
     }
   }
 }
@@ -422,7 +428,7 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, f
   return r;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool GELU>
+template <int BM, int BN, int WM, int WN, int NS, int GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int W = WM * WN;
@@ -467,6 +473,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K;
   const char *Sbase = (const char *)a.Bscale + ((int64_t)g * N + n0) * (int64_t)KG * 2;
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
+  bf16 *Zg = GELU == 2 ? (bf16 *)a.Zpre + (int64_t)g * a.M_cap * N : nullptr;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
   const uint32_t lds_sc = lds0 + NS * STAGE;
 
@@ -574,6 +581,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   constexpr int CROW = BN * 2 + 16;
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;
+  // pass 0 writes C; with the pre-activation output (GELU == 2), pass 1 writes Zpre
+  for (int pass = 0; pass < (GELU == 2 ? 2 : 1); pass++)
   for (int band = 0; band < WM; band++) {
     __syncthreads();
     if (wm == band) {
@@ -586,24 +595,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
             const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int Cc = wn * WTN + j * 32 + (lane & 31);
             float v = acc[i][j][r];
-            if (GELU) v = gelu_f(v);
+            if (GELU && pass == 0) v = gelu_f(v);
             *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
           }
     }
     __syncthreads();
+    bf16 *Og = pass ? Zg : Cg;
     const int64_t r0 = m0 + band * WTM;
     const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
     for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
       const int R = idx / OCPR, ch = idx - R * OCPR;
       if (R < mrows)
-        *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+        *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
     }
   }
 }
 
 // fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
 // any shape (bounds-checked); the correctness path for fp32 layers.
-template <bool GELU>
+template <int GELU>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int T = 64, BKF = 16;
   __shared__ float As[BKF][T + 1], Bs[BKF][T + 1];
@@ -625,6 +635,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   const float *Ag = (const float *)a.A + (int64_t)g * a.M_cap * K;
   const float *Bg = (const float *)a.B + (int64_t)g * N * K;
   float *Cg = (float *)a.C + (int64_t)g * a.M_cap * N;
+  float *Zg = GELU == 2 ? (float *)a.Zpre + (int64_t)g * a.M_cap * N : nullptr;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += BKF) {
@@ -650,7 +661,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     for (int j = 0; j < 4; j++) {
       const int64_t m = m0 + ty * 4 + i;
       const int n = n0 + tx * 4 + j;
-      if (m < rows && n < N) Cg[m * N + n] = GELU ? gelu_f(acc[i][j]) : acc[i][j];
+      if (m < rows && n < N) {
+        Cg[m * N + n] = GELU ? gelu_f(acc[i][j]) : acc[i][j];
+        if (GELU == 2) Zg[m * N + n] = acc[i][j];
+      }
     }
 }
 
@@ -659,6 +673,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 namespace moe_host {
 using namespace moe;
 
+// epilogue variant: 0 none, 1 GELU, 2 GELU and the pre-activation kept in Zpre
+static int epi_of(const GemmArgs &a, int gelu) { return gelu ? (a.Zpre ? 2 : 1) : 0; }
+
+template <int BM, int BN, int WM, int WN, int MF, bool I8>
+static hipError_t launch_cfg_t(const GemmArgs &a, int epi, dim3 grid, dim3 block, const char *name,
+                               hipStream_t s) {
+  if (epi == 2)
+    MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, I8, 2>), grid, block, 0, s, a);
+  else if (epi == 1)
+    MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, I8, 1>), grid, block, 0, s, a);
+  else
+    MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, I8, 0>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int MF>
 static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_t s,
                              const char *role, const char *tile) {
@@ -666,17 +695,19 @@ static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
   const char *name = intern_name(role, tile);
-  if (b_int8) {
-    if (gelu)
-      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, true, true>), grid, block, 0, s, a);
-    else
-      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, true, false>), grid, block, 0, s, a);
-  } else {
-    if (gelu)
-      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, false, true>), grid, block, 0, s, a);
-    else
-      MOE_LAUNCH(name, (gemm_bf16_kernel<BM, BN, WM, WN, MF, false, false>), grid, block, 0, s, a);
-  }
+  if (b_int8) return launch_cfg_t<BM, BN, WM, WN, MF, true>(a, epi_of(a, gelu), grid, block, name, s);
+  return launch_cfg_t<BM, BN, WM, WN, MF, false>(a, epi_of(a, gelu), grid, block, name, s);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool NT>
+static hipError_t launch_dma_t(const GemmArgs &a, int epi, dim3 grid, dim3 block, const char *name,
+                               hipStream_t s) {
+  if (epi == 2)
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 2>), grid, block, 0, s, a);
+  else if (epi == 1)
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 1>), grid, block, 0, s, a);
+  else
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 0>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -687,18 +718,9 @@ static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t 
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
   const char *name = intern_name(role, tile);
-  if (nt_b) {
-    if (gelu)
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, true>), grid, block, 0, s, a);
-    else
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, false>), grid, block, 0, s, a);
-  } else {
-    if (gelu)
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, true>), grid, block, 0, s, a);
-    else
-      MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  if (nt_b)
+    return launch_dma_t<BM, BN, WM, WN, BK, NS, true>(a, epi_of(a, gelu), grid, block, name, s);
+  return launch_dma_t<BM, BN, WM, WN, BK, NS, false>(a, epi_of(a, gelu), grid, block, name, s);
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
@@ -708,10 +730,13 @@ static hipError_t launch_dma_i8(const GemmArgs &a, int gelu, hipStream_t s, cons
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
   const char *name = intern_name(role, tile);
-  if (gelu)
-    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, true>), grid, block, 0, s, a);
+  const int epi = epi_of(a, gelu);
+  if (epi == 2)
+    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, s, a);
+  else if (epi == 1)
+    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, s, a);
   else
-    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, false>), grid, block, 0, s, a);
+    MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -724,10 +749,13 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
   if (!act_bf16) {
     const int tiles = a.G * (int)((a.M_cap + 63) / 64) * ((a.N + 63) / 64);
     const char *name = intern_name(role, "f32");
-    if (gelu)
-      MOE_LAUNCH(name, gemm_f32_kernel<true>, dim3(tiles), dim3(256), 0, s, a);
+    const int epi = epi_of(a, gelu);
+    if (epi == 2)
+      MOE_LAUNCH(name, gemm_f32_kernel<2>, dim3(tiles), dim3(256), 0, s, a);
+    else if (epi == 1)
+      MOE_LAUNCH(name, gemm_f32_kernel<1>, dim3(tiles), dim3(256), 0, s, a);
     else
-      MOE_LAUNCH(name, gemm_f32_kernel<false>, dim3(tiles), dim3(256), 0, s, a);
+      MOE_LAUNCH(name, gemm_f32_kernel<0>, dim3(tiles), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   const int nt = a.rows != nullptr;  // grouped expert GEMM: weights read once

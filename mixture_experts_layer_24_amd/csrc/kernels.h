@@ -23,6 +23,7 @@ struct RouterArgs {
 
 // Grouped "NT" GEMM: for each group g < G and row m < rows[g] (or M_cap):
 //   C[g][m][n] = epi( sum_k A[g][m][k] * B[g][n][k] )
+// (with the GELU epilogue and Zpre set, Zpre[g][m][n] = the sum itself)
 struct GemmArgs {
   const void *A;        // act, [G][M_cap][K] (row stride K)
   const void *B;        // act or int8, [G][N][K]
@@ -31,6 +32,7 @@ struct GemmArgs {
   const int32_t *rows;  // [G] valid rows per group (device) or null = M_cap
   int64_t M_cap;
   int N, K, G;
+  void *Zpre;  // GELU epilogue only: also store the pre-activation here (as C), or null
 };
 
 // general grouped GEMM of the backward (backward.hip)

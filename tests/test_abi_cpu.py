@@ -169,3 +169,17 @@ def test_binding_refuses_cpu_tensors(L):
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         binding.moe_route(cfg, x, x[:2], None, None, None, None, None, None)
+
+
+def _header_fields(struct):
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), src, re.S).group(1)
+    return [m.group(1) for m in re.finditer(r"\b(\w+)\s*;", body)]
+
+
+@pytest.mark.parametrize("struct,cls", [("moe_config", "Config"), ("moe_weights", "Weights"),
+                                        ("moe_outputs", "Outputs"), ("moe_grads", "Grads")])
+def test_binding_structs_follow_the_header(struct, cls):
+    # same members in the same order: the ctypes layout is the C layout
+    assert [f[0] for f in getattr(binding, cls)._fields_] == _header_fields(struct)

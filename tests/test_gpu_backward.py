@@ -163,3 +163,56 @@ def test_full_size_backward_sampled(name):
             assert abs(got - ref) <= tau * scale, f"{name_w}[{e},{a},{b}]: {got} vs {ref}"
     del inp, cpu, grads, out
     torch.cuda.empty_cache()
+
+
+SAVED_CASES = [CASES[0], CASES[5], CASES[7]]
+
+
+@pytest.mark.parametrize("wl", SAVED_CASES, ids=[w.name for w in SAVED_CASES])
+def test_backward_from_saved_activations(wl):
+    # a forward that keeps W1 x and GELU(W1 x) (expert and dense) gives the
+    # same y; what it kept is the pre-activation and its GELU; the backward
+    # that reads them instead of recomputing matches the oracle
+    print(f"[saved] {wl.name}", flush=True)
+    from scipy.special import erf
+    g_aux, g_z = 0.3, 0.2
+    inp = synth.make_inputs(wl, seed=6)
+    dinp = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    cfg = binding.config_of(wl)
+    ws = binding.alloc_workspace(cfg)
+    plain = binding.alloc_outputs(cfg, DEV)
+    binding.moe_layer_forward(cfg, dinp["x"], dinp, plain, ws)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True,
+                                saved_activations=True)
+    binding.moe_layer_forward(cfg, dinp["x"], dinp, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.y, plain.y)
+    kept = to_np(out.kept)
+    def gelu(v):
+        return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+    xd = out.x_disp.double().cpu().numpy()
+    w1 = inp["w1"].double().numpy()
+    for e in range(wl.E):
+        if kept[e] == 0:
+            continue
+        z_ref = xd[e, :kept[e]] @ w1[e].T
+        check_close(f"z_disp[{e}]", out.z_disp[e, :kept[e]], z_ref, TAU["bf16"])
+        check_close(f"h_disp[{e}]", out.h_disp[e, :kept[e]], gelu(z_ref), TAU["bf16"])
+    if wl.pr_moe:
+        zd_ref = inp["x"].double().numpy() @ inp["wm1"].double().numpy().T
+        check_close("z_dense", out.z_dense, zd_ref, TAU["bf16"])
+        check_close("h_dense", out.h_dense, gelu(zd_ref), TAU["bf16"])
+    dy = synth.normal((wl.T, wl.d), 1.0, 9, "dy", "cpu", torch.bfloat16)
+    grads = binding.alloc_grads(cfg, DEV)
+    binding.moe_layer_backward(cfg, dinp["x"], dinp, out, dy.to(DEV), grads,
+                               binding.alloc_workspace(cfg, binding.ENTRY_BACKWARD),
+                               g_aux=g_aux, g_z=g_z)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(inp["x"], inp["w_router"], inp["w1"], inp["w2"],
+                                dy.double().numpy(), k=wl.k, capacity_factor=wl.capacity_factor,
+                                bias=inp["b_router"], wm1=inp["wm1"], wm2=inp["wm2"],
+                                normalize=wl.normalize_topk, pr_moe=wl.pr_moe,
+                                add_skip=wl.add_skip, alpha=wl.aux_alpha, g_aux=g_aux, g_z=g_z)
+    tau = TAU["bf16"]
+    for n in ("dx", "dw_router", "db_router", "dw1", "dw2") + (("dwm1", "dwm2") if wl.pr_moe else ()):
+        check_close(n, getattr(grads, n), ref[n], tau)
