@@ -37,6 +37,7 @@ _lib = None
 
 F32, BF16, I8, F64 = 0, 1, 2, 3
 DROP_TOKEN_ORDER, DROP_GATE_PRIORITY = 0, 1
+ROUTER_TOPK, ROUTER_TOP_P, ROUTER_COSINE, ROUTER_NOISY = 0, 1, 2, 3
 
 
 def build(out: str = _LIB, src: str = _SRC, extra: tuple = ()) -> str:
@@ -85,6 +86,16 @@ def _load(path: str | None = None):
             [vp, i64, vp, vp, i64, vp, vp, i64, vp])
         lib.oracle_z_loss.restype = dbl
         lib.oracle_z_loss.argtypes = [i64, i64, vp]
+        lib.oracle_route_variant.restype = i32
+        lib.oracle_route_variant.argtypes = ([i64] * 4 + [i32, i32, dbl, dbl, i64, vp, i32, vp,
+                                              vp, vp, vp, vp] + [vp] * 5)
+        lib.oracle_importance_load.restype = None
+        lib.oracle_importance_load.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_cov2.restype = dbl
+        lib.oracle_cov2.argtypes = [i64, vp]
+        lib.oracle_layer_forward_v.restype = i32
+        lib.oracle_layer_forward_v.argtypes = (
+            lib.oracle_layer_forward.argtypes + [i32, dbl, dbl, i64, vp, vp, vp, vp])
         lib.oracle_quantize_sym_int8.restype = i32
         lib.oracle_quantize_sym_int8.argtypes = [i64, i64, vp, vp, vp, vp]
         if path is None:
@@ -224,6 +235,70 @@ def z_loss(logits) -> float:
     return float(_load().oracle_z_loss(T, E, lg.ctypes.data))
 
 
+def _router_extras(router, x_fmt, w_noise, noise, emb, T, E, d):
+    wn = en = nz = None
+    de = 0
+    if router == ROUTER_NOISY:
+        wn, f = _np(w_noise)
+        assert f == x_fmt and wn.shape == (E, d)
+        nz = np.ascontiguousarray(_np(noise)[0], dtype=np.float32)
+        assert nz.shape == (T, E)
+    if router == ROUTER_COSINE:
+        en, f = _np(emb)
+        assert f == x_fmt and en.shape[0] == E
+        de = en.shape[1]
+    return wn, nz, en, de
+
+
+def route_variant(x, w_router, k: int, *, router: int = ROUTER_TOPK, bias=None,
+                  normalize: bool = True, top_p: float = 1.0, tau: float = 1.0,
+                  w_noise=None, noise=None, emb=None):
+    """Router variants (TopK, TopP, cosine with w_router = W_proj [de, d] and
+    emb [E, de], noisy TopK with w_noise [E, d] and noise [T, E] fp32):
+    logits, probs, ids (-1 = unused slot), gates, load_p (T x E), and the
+    per-expert importance and load sums."""
+    xa, xf = _np(x)
+    wa, wf = _np(w_router)
+    assert wf == xf
+    T, d = xa.shape
+    E = (_np(emb)[0].shape[0] if router == ROUTER_COSINE else wa.shape[0])
+    wn, nz, en, de = _router_extras(router, xf, w_noise, noise, emb, T, E, d)
+    if router == ROUTER_COSINE:
+        assert wa.shape == (de, d)
+    b = None if bias is None else np.ascontiguousarray(_np(bias)[0], dtype=np.float32)
+    logits = np.zeros((T, E)); probs = np.zeros((T, E)); load_p = np.zeros((T, E))
+    ids = np.zeros((T, k), np.int32); gates = np.zeros((T, k))
+    rc = _load().oracle_route_variant(T, d, E, k, int(router), int(normalize), float(top_p),
+                                      float(tau), de, xa.ctypes.data, xf, wa.ctypes.data, _p(b),
+                                      _p(wn), _p(nz), _p(en), logits.ctypes.data,
+                                      probs.ctypes.data, ids.ctypes.data, gates.ctypes.data,
+                                      load_p.ctypes.data)
+    if rc:
+        raise ValueError("oracle_route_variant rejected its arguments")
+    imp, load = importance_load(ids, gates, load_p)
+    return dict(logits=logits, probs=probs, ids=ids, gates=gates, load_p=load_p,
+                importance=imp, load=load)
+
+
+def importance_load(ids, gates, load_p):
+    """Per-expert Importance (sum of gates) and Load (sum of P(x, e))."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    gates = np.ascontiguousarray(gates, np.float64)
+    load_p = np.ascontiguousarray(load_p, np.float64)
+    T, k = ids.shape
+    E = load_p.shape[1]
+    imp = np.zeros(E); load = np.zeros(E)
+    _load().oracle_importance_load(T, E, k, ids.ctypes.data, gates.ctypes.data,
+                                   load_p.ctypes.data, imp.ctypes.data, load.ctypes.data)
+    return imp, load
+
+
+def cov2(v) -> float:
+    """Squared coefficient of variation (population variance / mean^2)."""
+    v = np.ascontiguousarray(v, np.float64)
+    return float(_load().oracle_cov2(v.size, v.ctypes.data))
+
+
 def quantize_sym_int8(w, scale=None):
     """(codes int8 [N, K], scales fp64 [N, K/128]) of an fp64 matrix."""
     w = np.ascontiguousarray(w, np.float64)
@@ -242,8 +317,11 @@ def layer_forward(x, w_router, w1, w2, *, k: int, capacity_factor: float,
                   capacity_override: int = 0, bias=None, s1=None, s2=None,
                   wm1=None, wm2=None, normalize: bool = True, pr_moe: bool = False,
                   add_skip: bool = True, policy: int = DROP_TOKEN_ORDER,
-                  alpha: float = 1.0):
-    """Whole layer; returns a dict of every intermediate the layer defines."""
+                  alpha: float = 1.0, router: int = ROUTER_TOPK, top_p: float = 1.0,
+                  tau: float = 1.0, w_noise=None, noise=None, emb=None):
+    """Whole layer; returns a dict of every intermediate the layer defines.
+    router / top_p / tau / w_noise / noise / emb: as route_variant (for the
+    cosine router w_router is W_proj)."""
     xa, xf = _np(x)
     wra, wrf = _np(w_router)
     assert wrf == xf, "router weights share the activation format"
@@ -253,6 +331,7 @@ def layer_forward(x, w_router, w1, w2, *, k: int, capacity_factor: float,
     T, D = xa.shape
     E, F = w1a.shape[0], w1a.shape[1]
     assert w1a.shape == (E, F, D) and w2a.shape == (E, D, F)
+    wn, nz, en, de = _router_extras(router, xf, w_noise, noise, emb, T, E, D)
     Fd = 0
     wm1a = wm2a = None
     if pr_moe:
@@ -269,15 +348,17 @@ def layer_forward(x, w_router, w1, w2, *, k: int, capacity_factor: float,
         slots=np.zeros((T, k), np.int32), drop=np.zeros((T, k), np.uint8),
         load=np.zeros(E, np.int32), kept=np.zeros(E, np.int32),
         expert_out=np.zeros((T, k, D)), m=np.zeros((T, D)), dense=np.zeros((T, D)),
-        y=np.zeros((T, D)), aux=np.zeros(1))
-    rc = _load().oracle_layer_forward(
+        y=np.zeros((T, D)), aux=np.zeros(1), load_p=np.zeros((T, E)))
+    rc = _load().oracle_layer_forward_v(
         T, D, E, k, F, Fd, float(capacity_factor), int(capacity_override),
         int(normalize), int(pr_moe), int(add_skip), int(policy), float(alpha),
         xa.ctypes.data, xf, wra.ctypes.data, _p(b), w1a.ctypes.data,
         w2a.ctypes.data, wf, _p(s1a), _p(s2a), _p(wm1a), _p(wm2a),
         *(out[n].ctypes.data for n in ("logits", "probs", "ids", "gates", "slots",
                                        "drop", "load", "kept", "expert_out", "m",
-                                       "dense", "y", "aux")))
+                                       "dense", "y", "aux")),
+        int(router), float(top_p), float(tau), de, _p(wn), _p(nz), _p(en),
+        out["load_p"].ctypes.data)
     if rc:
         raise ValueError("oracle_layer_forward rejected its arguments")
     out["aux"] = float(out["aux"][0])

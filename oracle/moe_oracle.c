@@ -25,6 +25,12 @@
  *         sec. 1.1.4.1 (Switch load-balance loss alpha*N*sum f_i Q_i),
  *         sec. 1.2.1 (bf16 is the top half of an fp32),
  *         sec. 1.2.2 (symmetric quantization: r_hat = s*q).
+ *  [SRV2] the same survey notes, sec. 1.1.1.1 (linear gating with TopK and a
+ *         noise term R_noise that encourages exploration), sec. 1.1.1.2
+ *         (cosine-similarity gating with a learnable projection, expert
+ *         embeddings and a temperature tau), sec. 1.1.4.1 (Importance and
+ *         Load losses: w * CoV(.)^2 of per-expert sums), sec. 1.1.4.2 (TopP
+ *         expert selection by accumulated score).
  *  [DSN]  "DeepSpeed-MoE: Advancing Mixture-of-Experts Inference and Training
  *         to Power Next-Generation AI Scale" (unpurerationalist.github.io
  *         notes), sec. 3.1 (Residual-MoE: fixed dense MLP plus one top-1
@@ -203,13 +209,20 @@ double oracle_aux_loss(int64_t T, int64_t E, int64_t k, const int32_t *ids,
  * assignments with the largest gate (ties to the earlier token); the slot is
  * the rank in that order.
  * Outputs: slots[t,j] (-1 when dropped), drop[t,j] (1 when dropped),
- * load[e] = assignments received, kept[e] = min(load[e], C).
+ * load[e] = assignments received, kept[e] = min(load[e], C).  Entries whose
+ * id is not an expert are no assignment (slot -1, drop 0).
  * ---------------------------------------------------------------------- */
 int oracle_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
                     const int32_t *ids, const double *gates, int policy,
                     int32_t *slots, uint8_t *drop, int32_t *load,
                     int32_t *kept) {
   if (policy == OR_DROP_GATE_PRIORITY && !gates) return -1;
+  /* an id outside 0..E-1 (a TopP token that chose fewer than k experts)
+   * is no assignment: slot -1, not dropped, counted nowhere */
+  for (int64_t a = 0; a < T * k; a++) {
+    slots[a] = -1;
+    drop[a] = 0;
+  }
   for (int64_t e = 0; e < E; e++) {
     int64_t n = 0;
     for (int64_t t = 0; t < T; t++)
@@ -326,19 +339,36 @@ int oracle_combine(int64_t T, int64_t D, int64_t k, const int32_t *slots,
  * expert_out T x k x D (per assignment; zero when dropped),
  * m T x D, dense T x D (zero when !pr_moe), y T x D, aux [1].
  * ---------------------------------------------------------------------- */
-int oracle_layer_forward(int64_t T, int64_t D, int64_t E, int64_t k,
-                         int64_t F, int64_t Fd, double cf, int64_t cap_override,
-                         int normalize, int pr_moe, int add_skip, int policy,
-                         double alpha, const void *x, int x_fmt,
-                         const void *wr, const float *bias, const void *w1,
-                         const void *w2, int w_fmt, const float *s1,
-                         const float *s2, const void *wm1, const void *wm2,
-                         double *logits, double *probs, int32_t *ids,
-                         double *gates, int32_t *slots, uint8_t *drop,
-                         int32_t *load, int32_t *kept, double *expert_out,
-                         double *m, double *dense, double *y, double *aux) {
-  int rc = oracle_route(T, D, E, k, normalize, x, x_fmt, wr, x_fmt, bias,
-                        logits, probs, ids, gates);
+/* the router variants of the section after oracle_z_loss */
+int oracle_route_variant(int64_t T, int64_t d, int64_t E, int64_t k, int variant, int normalize,
+                         double top_p, double tau, int64_t de, const void *x, int x_fmt,
+                         const void *wr, const float *bias, const void *w_noise,
+                         const float *noise, const void *emb, double *logits, double *probs,
+                         int32_t *ids, double *gates, double *load_p);
+
+/* The layer with a router variant (variant 0 = the softmax router of
+ * oracle_route; wr is then W_r, else as oracle_route_variant takes it). */
+int oracle_layer_forward_v(int64_t T, int64_t D, int64_t E, int64_t k,
+                           int64_t F, int64_t Fd, double cf, int64_t cap_override,
+                           int normalize, int pr_moe, int add_skip, int policy,
+                           double alpha, const void *x, int x_fmt,
+                           const void *wr, const float *bias, const void *w1,
+                           const void *w2, int w_fmt, const float *s1,
+                           const float *s2, const void *wm1, const void *wm2,
+                           double *logits, double *probs, int32_t *ids,
+                           double *gates, int32_t *slots, uint8_t *drop,
+                           int32_t *load, int32_t *kept, double *expert_out,
+                           double *m, double *dense, double *y, double *aux,
+                           int variant, double top_p, double tau, int64_t de,
+                           const void *w_noise, const float *noise, const void *emb,
+                           double *load_p) {
+  int rc;
+  if (variant == 0)
+    rc = oracle_route(T, D, E, k, normalize, x, x_fmt, wr, x_fmt, bias, logits, probs, ids,
+                      gates);
+  else
+    rc = oracle_route_variant(T, D, E, k, variant, normalize, top_p, tau, de, x, x_fmt, wr,
+                              bias, w_noise, noise, emb, logits, probs, ids, gates, load_p);
   if (rc) return rc;
   *aux = oracle_aux_loss(T, E, k, ids, probs, alpha, NULL, NULL);
   int64_t C = oracle_capacity(T, E, k, cf, cap_override);
@@ -379,6 +409,24 @@ int oracle_layer_forward(int64_t T, int64_t D, int64_t E, int64_t k,
   rc = oracle_combine(T, D, k, slots, gates, expert_out, base, y, m);
   free(base);
   return rc;
+}
+
+int oracle_layer_forward(int64_t T, int64_t D, int64_t E, int64_t k,
+                         int64_t F, int64_t Fd, double cf, int64_t cap_override,
+                         int normalize, int pr_moe, int add_skip, int policy,
+                         double alpha, const void *x, int x_fmt,
+                         const void *wr, const float *bias, const void *w1,
+                         const void *w2, int w_fmt, const float *s1,
+                         const float *s2, const void *wm1, const void *wm2,
+                         double *logits, double *probs, int32_t *ids,
+                         double *gates, int32_t *slots, uint8_t *drop,
+                         int32_t *load, int32_t *kept, double *expert_out,
+                         double *m, double *dense, double *y, double *aux) {
+  return oracle_layer_forward_v(T, D, E, k, F, Fd, cf, cap_override, normalize, pr_moe,
+                                add_skip, policy, alpha, x, x_fmt, wr, bias, w1, w2, w_fmt, s1,
+                                s2, wm1, wm2, logits, probs, ids, gates, slots, drop, load, kept,
+                                expert_out, m, dense, y, aux, 0, 0.0, 0.0, 0, NULL, NULL, NULL,
+                                NULL);
 }
 
 /* ------------------------------------------------------------------------
@@ -771,4 +819,207 @@ int oracle_backward_sampled(int64_t T, int64_t D, int64_t E, int64_t k, int64_t 
   }
   free(f);
   return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Router variants ([SRV2]), each followed by the same capacity dispatch,
+ * experts and combine as the softmax router.  variant:
+ *   OR_ROUTER_TOPK   logits = W_r x (+ b); TopK as oracle_route.
+ *   OR_ROUTER_TOP_P  logits = W_r x (+ b), p = softmax; experts are taken in
+ *                    descending p (ties to the lower index), accumulating
+ *                    their p, until the sum exceeds top_p ("until the
+ *                    cumulative value exceeds P, activate every accumulated
+ *                    expert", sec. 1.1.4.2); at most k are taken (the k slots
+ *                    per token); unused slots get id -1 and gate 0.  Gates:
+ *                    normalize -> p over the sum of the taken p (any count),
+ *                    else p.
+ *   OR_ROUTER_COSINE u = W_proj x (de values); logit_e = <emb_e, u> /
+ *                    (tau |u| |emb_e|) (+ b), 0 when a norm is 0 (sec.
+ *                    1.1.1.2: the token's projection against each expert's
+ *                    embedding, sharpened by 1/tau); softmax and TopK as the
+ *                    softmax router.
+ *   OR_ROUTER_NOISY  clean_e = W_g x (+ b), sigma_e = softplus(W_noise x),
+ *                    H_e = clean_e + eps_e sigma_e with eps the caller's
+ *                    standard-normal draws (sec. 1.1.1.1: g linear plus a
+ *                    noise term); the k largest H are kept and the gates are
+ *                    the softmax over the kept H (TopK before softmax); the
+ *                    logits reported are H.
+ * load_p[t,e] = P(x_t, e) of the Load loss (sec. 1.1.4.1: the probability
+ * that the gate of e is nonzero under a new draw of the noise): for the
+ * noisy router, with the other experts' H held, e is kept iff
+ * clean_e + eps' sigma_e exceeds the k-th largest H among the other
+ * experts, so P = Phi((clean_e - that value) / sigma_e) (1 when fewer than
+ * k other experts exist); for the noise-free routers P is 1 if e was taken
+ * and 0 otherwise.
+ * Formats: x, wr (W_r, W_g or W_proj [de, d]), w_noise [E, d] and emb
+ * [E, de] in x_fmt; noise [T, E] float32.
+ * ---------------------------------------------------------------------- */
+enum { OR_ROUTER_TOPK = 0, OR_ROUTER_TOP_P = 1, OR_ROUTER_COSINE = 2, OR_ROUTER_NOISY = 3 };
+
+static double softplus(double z) { return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z)); }
+static double std_normal_cdf(double z) { return 0.5 * erfc(-z / sqrt(2.0)); }
+
+int oracle_route_variant(int64_t T, int64_t d, int64_t E, int64_t k, int variant, int normalize,
+                         double top_p, double tau, int64_t de, const void *x, int x_fmt,
+                         const void *wr, const float *bias, const void *w_noise,
+                         const float *noise, const void *emb, double *logits, double *probs,
+                         int32_t *ids, double *gates, double *load_p) {
+  if (k < 1 || k > E || k > 64) return -1;
+  if (variant == OR_ROUTER_TOP_P && !(top_p > 0.0)) return -1;
+  if (variant == OR_ROUTER_COSINE && (!(tau > 0.0) || de < 1 || !emb)) return -1;
+  if (variant == OR_ROUTER_NOISY && (!w_noise || !noise)) return -1;
+  if (variant < OR_ROUTER_TOPK || variant > OR_ROUTER_NOISY) return -1;
+  int rc = 0;
+#pragma omp parallel
+  {
+    double *clean = (double *)malloc((size_t)E * sizeof(double));
+    double *sigma = (double *)malloc((size_t)E * sizeof(double));
+    double *u = (double *)malloc((size_t)(de > 0 ? de : 1) * sizeof(double));
+    double *other = (double *)malloc((size_t)E * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = 0; t < T; t++) {
+      double *l = logits + t * E, *p = probs + t * E;
+      /* logits */
+      if (variant == OR_ROUTER_COSINE) {
+        double nu = 0.0;
+        for (int64_t j = 0; j < de; j++) {
+          double v = 0.0;
+          for (int64_t i = 0; i < d; i++) v += elem(wr, x_fmt, j * d + i) * elem(x, x_fmt, t * d + i);
+          u[j] = v;
+          nu += v * v;
+        }
+        nu = sqrt(nu);
+        for (int64_t e = 0; e < E; e++) {
+          double ne = 0.0, dot = 0.0;
+          for (int64_t j = 0; j < de; j++) {
+            const double v = elem(emb, x_fmt, e * de + j);
+            ne += v * v;
+            dot += v * u[j];
+          }
+          ne = sqrt(ne);
+          l[e] = (nu > 0.0 && ne > 0.0) ? dot / (tau * nu * ne) : 0.0;
+          if (bias) l[e] += (double)bias[e];
+        }
+      } else {
+        for (int64_t e = 0; e < E; e++) {
+          double v = 0.0;
+          for (int64_t i = 0; i < d; i++) v += elem(x, x_fmt, t * d + i) * elem(wr, x_fmt, e * d + i);
+          if (bias) v += (double)bias[e];
+          clean[e] = v;
+          l[e] = v;
+        }
+        if (variant == OR_ROUTER_NOISY)
+          for (int64_t e = 0; e < E; e++) {
+            double z = 0.0;
+            for (int64_t i = 0; i < d; i++)
+              z += elem(x, x_fmt, t * d + i) * elem(w_noise, x_fmt, e * d + i);
+            sigma[e] = softplus(z);
+            l[e] = clean[e] + (double)noise[t * E + e] * sigma[e];
+          }
+      }
+      /* softmax, the largest logit shifted out */
+      double lmax = l[0];
+      for (int64_t e = 1; e < E; e++)
+        if (l[e] > lmax) lmax = l[e];
+      double zsum = 0.0;
+      for (int64_t e = 0; e < E; e++) zsum += exp(l[e] - lmax);
+      for (int64_t e = 0; e < E; e++) p[e] = exp(l[e] - lmax) / zsum;
+      /* selection in the order (larger logit, then smaller index) */
+      int32_t *sel = ids + t * k;
+      int64_t n = 0;
+      double cum = 0.0;
+      for (int64_t j = 0; j < k; j++) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; e++) {
+          int taken = 0;
+          for (int64_t q = 0; q < j; q++)
+            if (sel[q] == e) taken = 1;
+          if (!taken && (best < 0 || l[e] > l[best])) best = e;
+        }
+        sel[j] = (int32_t)best;
+        n = j + 1;
+        cum += p[best];
+        if (variant == OR_ROUTER_TOP_P && cum > top_p) break;
+      }
+      for (int64_t j = n; j < k; j++) sel[j] = -1;
+      double den = 0.0;
+      for (int64_t j = 0; j < n; j++) den += p[sel[j]];
+      double *g = gates + t * k;
+      for (int64_t j = 0; j < k; j++) {
+        if (j >= n) {
+          g[j] = 0.0;
+          continue;
+        }
+        int renorm;
+        if (variant == OR_ROUTER_NOISY) renorm = 1;
+        else if (variant == OR_ROUTER_TOP_P) renorm = normalize;
+        else renorm = k >= 2 && normalize;
+        g[j] = renorm ? p[sel[j]] / den : p[sel[j]];
+      }
+      /* P(x, e) */
+      if (load_p) {
+        double *lp = load_p + t * E;
+        for (int64_t e = 0; e < E; e++) {
+          int chosen = 0;
+          for (int64_t j = 0; j < n; j++)
+            if (sel[j] == e) chosen = 1;
+          if (variant != OR_ROUTER_NOISY) {
+            lp[e] = chosen ? 1.0 : 0.0;
+            continue;
+          }
+          /* k-th largest H among the other experts */
+          int64_t no = 0;
+          for (int64_t j = 0; j < E; j++)
+            if (j != e) other[no++] = l[j];
+          if (no < k) {
+            lp[e] = 1.0;
+            continue;
+          }
+          for (int64_t a = 0; a < k; a++) /* partial selection sort, descending */
+            for (int64_t b = a + 1; b < no; b++)
+              if (other[b] > other[a]) {
+                const double tmp = other[a];
+                other[a] = other[b];
+                other[b] = tmp;
+              }
+          lp[e] = std_normal_cdf((clean[e] - other[k - 1]) / sigma[e]);
+        }
+      }
+    }
+    free(clean); free(sigma); free(u); free(other);
+  }
+  return rc;
+}
+
+/* Importance_e = sum over tokens of the gate of e (0 when not chosen), and
+ * Load_e = sum over tokens of P(x, e) ([SRV2] 1.1.4.1). */
+void oracle_importance_load(int64_t T, int64_t E, int64_t k, const int32_t *ids,
+                            const double *gates, const double *load_p, double *importance,
+                            double *load) {
+  for (int64_t e = 0; e < E; e++) {
+    importance[e] = 0.0;
+    load[e] = 0.0;
+  }
+  for (int64_t t = 0; t < T; t++) {
+    for (int64_t j = 0; j < k; j++) {
+      const int32_t e = ids[t * k + j];
+      if (e >= 0 && e < E) importance[e] += gates[t * k + j];
+    }
+    for (int64_t e = 0; e < E; e++) load[e] += load_p[t * E + e];
+  }
+}
+
+/* CoV^2 = variance / mean^2 over the n values (population variance: the
+ * coefficient of variation of the experts' own values, sec. 1.1.4.1); 0 when
+ * the mean is 0. */
+double oracle_cov2(int64_t n, const double *v) {
+  if (n <= 0) return 0.0;
+  double mean = 0.0;
+  for (int64_t i = 0; i < n; i++) mean += v[i];
+  mean /= (double)n;
+  if (mean == 0.0) return 0.0;
+  double var = 0.0;
+  for (int64_t i = 0; i < n; i++) var += (v[i] - mean) * (v[i] - mean);
+  var /= (double)n;
+  return var / (mean * mean);
 }

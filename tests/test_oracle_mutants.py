@@ -52,6 +52,15 @@ MUTANTS = {
     "bwd_softmax_jacobian_sign": ("p[e] * (dp[e] - pdp)", "p[e] * (dp[e] + pdp)"),
     "bwd_zloss_grad_halved": ("g_z * 2.0 / (double)T", "g_z * 1.0 / (double)T"),
     "bwd_dw2_uses_preactivation": ("const double hf = gelu(a[f]);", "const double hf = a[f];"),
+    # router variants
+    "topp_never_stops": ("if (variant == OR_ROUTER_TOP_P && cum > top_p) break;", "if (0) break;"),
+    "cosine_without_tau": ("dot / (tau * nu * ne)", "dot / (nu * ne)"),
+    "noisy_scale_not_softplus": ("sigma[e] = softplus(z);", "sigma[e] = z;"),
+    "noisy_gates_not_renormalised": ("if (variant == OR_ROUTER_NOISY) renorm = 1;",
+                                     "if (variant == OR_ROUTER_NOISY) renorm = 0;"),
+    "load_p_threshold_counts_itself": ("if (j != e) other[no++] = l[j];", "other[no++] = l[j];"),
+    "cov2_sample_variance": ("var /= (double)n;", "var /= (double)(n - 1);"),
+    "unused_slot_marked_dropped": ("    slots[a] = -1;\n    drop[a] = 0;", "    slots[a] = -1;\n    drop[a] = 1;"),
 }
 
 
@@ -69,6 +78,7 @@ def test_pins_kill_mutant(name, tmp_path):
         [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
          os.path.join(ROOT, "tests", "test_oracle_bruteforce.py"),
-         os.path.join(ROOT, "tests", "test_oracle_backward.py")],
+         os.path.join(ROOT, "tests", "test_oracle_backward.py"),
+         os.path.join(ROOT, "tests", "test_oracle_router_variants.py")],
         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
