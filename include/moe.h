@@ -79,6 +79,28 @@ extern "C" {
                                     one dropped) */
 
 /* workspace query selectors */
+/* router (moe_config.router), the MoE survey notes' gating variants:
+ *  TOPK     p = softmax(W_r x + b), the k largest p (the default above)
+ *  TOP_P    p as TOPK; experts in descending p, accumulated until their sum
+ *           exceeds top_p, at most k of them (sec. 1.1.4.2); a token's unused
+ *           slots have expert id -1 and gate 0 and are no assignment; gates
+ *           renormalised over the taken experts when normalize_topk
+ *  COSINE   logit_e = <emb_e, W_proj x> / (cos_tau |W_proj x| |emb_e|) (+ b),
+ *           0 when a norm is 0 (sec. 1.1.1.2); then as TOPK
+ *  NOISY_TOPK  clean = W_r x + b, sigma = softplus(W_noise x), logit =
+ *           clean + noise * sigma with the caller's standard-normal draws; the
+ *           k largest logits kept, gates = softmax over them (sec. 1.1.1.1)
+ * Every router can also report the Importance and Load losses (sec. 1.1.4.1):
+ *   w_importance * CoV(sum_t gate_e)^2 and w_load * CoV(sum_t P(x_t, e))^2,
+ *   CoV^2 = population variance / mean^2 over the experts (0 for mean 0),
+ *   P(x, e) = Phi((clean_e - k-th largest logit among the other experts) /
+ *   sigma_e) for NOISY_TOPK (the probability that e keeps a nonzero gate
+ *   under a new draw of its noise), else 1 if e was chosen and 0 if not. */
+#define MOE_ROUTER_TOPK 0
+#define MOE_ROUTER_TOP_P 1
+#define MOE_ROUTER_COSINE 2
+#define MOE_ROUTER_NOISY_TOPK 3
+
 #define MOE_ENTRY_ROUTE 0
 #define MOE_ENTRY_DISPATCH 1
 #define MOE_ENTRY_EXPERT_FFN 2
@@ -105,6 +127,12 @@ typedef struct moe_config {
   int32_t overlap_dense;  /* pr_moe, moe_layer_forward: 1 = run the dense MLP on
                              the library's side stream, concurrently with the
                              expert path; 0 = everything in order on `stream` */
+  int32_t router;         /* MOE_ROUTER_* (0 = TOPK) */
+  float top_p;            /* TOP_P: threshold P > 0 */
+  float cos_tau;          /* COSINE: temperature > 0 */
+  int32_t cos_dim;        /* COSINE: projection width 1..256 */
+  float w_importance;     /* Importance-loss weight (0 = not computed) */
+  float w_load;           /* Load-loss weight (0 = not computed) */
 } moe_config;
 
 typedef struct moe_weights {
@@ -116,6 +144,12 @@ typedef struct moe_weights {
   const void *w2_scale;  /* [E, d, d_ff/128] fp16 (int8 only, else NULL) */
   const void *wm1;       /* [d_ff_dense, d] act (pr_moe only) */
   const void *wm2;       /* [d, d_ff_dense] act (pr_moe only) */
+  /* router variants (NULL unless the router needs them): */
+  const void *w_noise;   /* NOISY_TOPK: [E, d] act */
+  const void *w_proj;    /* COSINE: [cos_dim, d] act (w_router unused) */
+  const void *expert_emb;/* COSINE: [E, cos_dim] act */
+  const float *noise;    /* NOISY_TOPK: [T, E] fp32 standard-normal draws of this
+                            call (an input, not a weight) */
 } moe_weights;
 
 typedef struct moe_outputs {
@@ -138,6 +172,8 @@ typedef struct moe_outputs {
   void *z_disp;        /* [E, C, d_ff] act W1 x, the pre-activation; NULL = not kept */
   void *h_dense;       /* [T, d_ff_dense] act GELU(Wm1 x) (pr_moe); NULL = workspace */
   void *z_dense;       /* [T, d_ff_dense] act Wm1 x (pr_moe); NULL = not kept */
+  float *importance_loss; /* [1] (needs w_importance != 0)     optional */
+  float *load_loss;       /* [1] (needs w_load != 0)           optional */
 } moe_outputs;
 
 typedef struct moe_grads {
@@ -165,11 +201,23 @@ size_t moe_workspace_bytes(const moe_config *cfg, int entry);
  * ("DeepSpeed-MoE vs Switch Transformer", section "Router Z-loss"), the mean
  * over tokens of the squared log-sum-exp of the token's logits (+ bias).
  * Logits accumulate in fp32; the log-sum-exp is fp32 per token, the mean is
- * summed in fp64 in a fixed order. */
+ * summed in fp64 in a fixed order.  The softmax TopK router only
+ * (cfg->router == MOE_ROUTER_TOPK, else MOE_ERR_UNSUPPORTED; moe_route_ex
+ * runs every router). */
 int moe_route(const moe_config *cfg, const void *x, const void *w_router,
               const float *b_router, int32_t *expert_ids, float *gates,
               float *logits, float *aux_loss, float *z_loss, void *ws,
               size_t ws_bytes, void *stream);
+
+/* Any router of moe_config.router (see MOE_ROUTER_*): reads x and the
+ * router's members of w (w_router, b_router; w_noise and noise; w_proj and
+ * expert_emb); writes out->expert_ids, gates, aux_loss and, when given,
+ * logits (the logits the softmax saw: + bias, + noise), z_loss,
+ * importance_loss and load_loss (each loss needs its weight != 0).  The
+ * other members of out are not touched.  Workspace:
+ * moe_workspace_bytes(cfg, MOE_ENTRY_ROUTE). */
+int moe_route_ex(const moe_config *cfg, const void *x, const moe_weights *w,
+                 moe_outputs *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Capacity-limited dispatch and the layout transform into the expert-major
  * buffer ("DeepSpeed MoE and Model Compression", pack_by_expert;
@@ -177,6 +225,8 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router,
  * transformation).  x [T, d], expert_ids [T, k]; gates [T, k] fp32 (used by
  * MOE_DROP_GATE_PRIORITY, where it is required and must be finite; may be
  * NULL for MOE_DROP_TOKEN_ORDER).
+ * An expert id outside 0..E-1 (an unused TopP slot) is no assignment:
+ * slot -1, drop_mask 0, not counted in load.
  * Out: slots [T, k] (-1 = dropped), drop_mask [T, k] (NULL ok), load [E],
  * kept [E], x_disp [E, C, d]: row (e, s) = x[t] for the assignment with slot
  * s in expert e; rows s >= kept[e] are not written.  Token order: an
@@ -235,8 +285,9 @@ int moe_layer_forward(const moe_config *cfg, const void *x,
  * z_dense and h_dense for PR-MoE), the backward reads them instead of
  * recomputing W1 x and GELU(W1 x).  dy [T, d] act.
  * Out: grads (written, not accumulated); the weight gradients are in the
- * activation type, accumulated in fp32.  bf16 activations and plain expert
- * weights only (MOE_ERR_UNSUPPORTED otherwise).  Workspace:
+ * activation type, accumulated in fp32.  bf16 activations, plain expert
+ * weights and the softmax TopK router only (MOE_ERR_UNSUPPORTED otherwise).
+ * Workspace:
  * moe_workspace_bytes(cfg, MOE_ENTRY_BACKWARD). */
 int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *w,
                        const moe_outputs *fwd, const void *dy, float g_aux, float g_z,

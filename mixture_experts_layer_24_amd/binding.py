@@ -28,7 +28,7 @@ MOE_DROP_GATE_PRIORITY = 1
 ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY_BACKWARD = \
     range(6)
 
-EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch",
+EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_ex", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_mlp", "moe_combine", "moe_layer_forward",
             "moe_layer_backward",
             "moe_status_string", "moe_profile_enable", "moe_profile_reset",
@@ -48,12 +48,16 @@ class Config(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("expert_wfmt", ctypes.c_int32),
                 ("normalize_topk", ctypes.c_int32), ("pr_moe", ctypes.c_int32),
                 ("add_skip", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-                ("aux_alpha", ctypes.c_float), ("overlap_dense", ctypes.c_int32)]
+                ("aux_alpha", ctypes.c_float), ("overlap_dense", ctypes.c_int32),
+                ("router", ctypes.c_int32), ("top_p", ctypes.c_float), ("cos_tau", ctypes.c_float),
+                ("cos_dim", ctypes.c_int32), ("w_importance", ctypes.c_float),
+                ("w_load", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "b_router", "w1", "w1_scale", "w2", "w2_scale", "wm1", "wm2")]
+                ("w_router", "b_router", "w1", "w1_scale", "w2", "w2_scale", "wm1", "wm2",
+                 "w_noise", "w_proj", "expert_emb", "noise")]
 
 
 class Grads(ctypes.Structure):
@@ -65,7 +69,7 @@ class Outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("y", "expert_ids", "gates", "slots", "load", "kept", "aux_loss", "drop_mask",
                  "logits", "x_disp", "y_disp", "dense_out", "z_loss", "h_disp", "z_disp",
-                 "h_dense", "z_dense")]
+                 "h_dense", "z_dense", "importance_loss", "load_loss")]
 
 
 _lock = threading.Lock()
@@ -101,6 +105,9 @@ def lib():
             L.moe_layer_forward.restype = i32
             L.moe_layer_forward.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
                                             ctypes.POINTER(Outputs), vp, sz, vp]
+            L.moe_route_ex.restype = i32
+            L.moe_route_ex.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
+                                       ctypes.POINTER(Outputs), vp, sz, vp]
             L.moe_layer_backward.restype = i32
             L.moe_layer_backward.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
                                              ctypes.POINTER(Outputs), vp, ctypes.c_float,
@@ -128,12 +135,18 @@ def _check(fn: str, status: int):
 
 
 # ------------------------------------------------------------------ config
+ROUTERS = {"topk": 0, "top_p": 1, "cosine": 2, "noisy_topk": 3}
+
+
 def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16",
                 wfmt="plain", d_ff_dense=0, pr_moe=False, add_skip=True,
                 normalize_topk=True, aux_alpha=1.0, overlap_dense=True,
-                drop_policy="token_order") -> Config:
+                drop_policy="token_order", router="topk", top_p=0.0, cos_tau=0.0,
+                cos_dim=0, w_importance=0.0, w_load=0.0) -> Config:
     if drop_policy not in ("token_order", "gate_priority"):
         raise ValueError(f"drop_policy {drop_policy!r}")
+    if router not in ROUTERS:
+        raise ValueError(f"router {router!r}")
     return Config(T=T, d=d, E=E, k=k, d_ff=d_ff, d_ff_dense=d_ff_dense,
                   capacity_factor=capacity_factor, capacity=capacity,
                   act_dtype=MOE_F32 if act == "f32" else MOE_BF16,
@@ -142,7 +155,9 @@ def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16"
                   add_skip=int(add_skip),
                   drop_policy=(MOE_DROP_GATE_PRIORITY if drop_policy == "gate_priority"
                                else MOE_DROP_TOKEN_ORDER),
-                  aux_alpha=aux_alpha, overlap_dense=int(overlap_dense))
+                  aux_alpha=aux_alpha, overlap_dense=int(overlap_dense),
+                  router=ROUTERS[router], top_p=top_p, cos_tau=cos_tau, cos_dim=cos_dim,
+                  w_importance=w_importance, w_load=w_load)
 
 
 def config_of(wl: Workload, **override) -> Config:
@@ -297,11 +312,14 @@ class LayerOutputs:
     z_disp: torch.Tensor | None = None   # [E, C, d_ff] W1 x
     h_dense: torch.Tensor | None = None  # [T, d_ff_dense] (pr_moe)
     z_dense: torch.Tensor | None = None
+    importance_loss: torch.Tensor | None = None
+    load_loss: torch.Tensor | None = None
 
 
 def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
                   x_disp=False, y_disp=False, dense_out=False, z_loss=False,
-                  saved_activations=False) -> LayerOutputs:
+                  saved_activations=False, importance_loss=False,
+                  load_loss=False) -> LayerOutputs:
     """saved_activations: also keep the FFN hidden activations and their
     pre-activations, which the backward then reads instead of recomputing."""
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
@@ -320,7 +338,9 @@ def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
         h_disp=e(E, C, cfg.d_ff) if saved_activations else None,
         z_disp=e(E, C, cfg.d_ff) if saved_activations else None,
         h_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None,
-        z_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None)
+        z_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None,
+        importance_loss=e(1, dt=torch.float32) if importance_loss else None,
+        load_loss=e(1, dt=torch.float32) if load_loss else None)
 
 
 def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):
@@ -328,6 +348,17 @@ def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None)
     W, O = _weights_struct(cfg, weights), _outputs_struct(cfg, out)
     wsp, wsn = _ws(ws)
     _check("moe_layer_forward", lib().moe_layer_forward(
+        ctypes.byref(cfg), _ptr(x, (cfg.T, cfg.d), _act_dtype(cfg), "x"), ctypes.byref(W),
+        ctypes.byref(O), wsp, wsn, _stream(stream)))
+
+
+def moe_route_ex(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):
+    """Any router (cfg.router): writes out.expert_ids, gates, aux_loss and the
+    optional logits, z_loss, importance_loss and load_loss."""
+    W, O = _weights_struct(cfg, weights, router_only=True), _outputs_struct(cfg, out,
+                                                                             router_only=True)
+    wsp, wsn = _ws(ws)
+    _check("moe_route_ex", lib().moe_route_ex(
         ctypes.byref(cfg), _ptr(x, (cfg.T, cfg.d), _act_dtype(cfg), "x"), ctypes.byref(W),
         ctypes.byref(O), wsp, wsn, _stream(stream)))
 
@@ -374,37 +405,42 @@ def moe_layer_backward(cfg, x, weights: dict, fwd: LayerOutputs, dy, grads: Laye
         _stream(stream)))
 
 
-def _weights_struct(cfg, weights: dict) -> Weights:
+def _weights_struct(cfg, weights: dict, router_only: bool = False) -> Weights:
     T, d, E, k, F, Fd = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff, cfg.d_ff_dense
     C = capacity(cfg)
     a, wd = _act_dtype(cfg), _wdtype(cfg)
     q8 = cfg.expert_wfmt == MOE_W_INT8_G128
     pr = bool(cfg.pr_moe)
+    cos, noisy = cfg.router == ROUTERS["cosine"], cfg.router == ROUTERS["noisy_topk"]
     W = Weights(
-        w_router=_ptr(weights["w_router"], (E, d), a, "w_router"),
+        w_router=_ptr(weights.get("w_router"), (E, d), a, "w_router", cos),
         b_router=_ptr(weights.get("b_router"), (E,), torch.float32, "b_router", True),
-        w1=_ptr(weights["w1"], (E, F, d), wd, "w1"),
+        w1=_ptr(weights.get("w1"), (E, F, d), wd, "w1", router_only),
         w1_scale=_ptr(weights.get("w1_scale"), (E, F, d // 128), torch.float16, "w1_scale",
                       not q8),
-        w2=_ptr(weights["w2"], (E, d, F), wd, "w2"),
+        w2=_ptr(weights.get("w2"), (E, d, F), wd, "w2", router_only),
         w2_scale=_ptr(weights.get("w2_scale"), (E, d, F // 128), torch.float16, "w2_scale",
                       not q8),
         wm1=_ptr(weights.get("wm1"), (Fd, d), a, "wm1", not pr),
-        wm2=_ptr(weights.get("wm2"), (d, Fd), a, "wm2", not pr))
+        wm2=_ptr(weights.get("wm2"), (d, Fd), a, "wm2", not pr),
+        w_noise=_ptr(weights.get("w_noise"), (E, d), a, "w_noise", not noisy),
+        noise=_ptr(weights.get("noise"), (T, E), torch.float32, "noise", not noisy),
+        w_proj=_ptr(weights.get("w_proj"), (cfg.cos_dim, d), a, "w_proj", not cos),
+        expert_emb=_ptr(weights.get("expert_emb"), (E, cfg.cos_dim), a, "expert_emb", not cos))
     return W
 
 
-def _outputs_struct(cfg, out: LayerOutputs) -> Outputs:
+def _outputs_struct(cfg, out: LayerOutputs, router_only: bool = False) -> Outputs:
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     C = capacity(cfg)
     a = _act_dtype(cfg)
     return Outputs(
-        y=_ptr(out.y, (T, d), a, "y"),
+        y=_ptr(out.y, (T, d), a, "y", router_only),
         expert_ids=_ptr(out.expert_ids, (T, k), torch.int32, "expert_ids"),
         gates=_ptr(out.gates, (T, k), torch.float32, "gates"),
-        slots=_ptr(out.slots, (T, k), torch.int32, "slots"),
-        load=_ptr(out.load, (E,), torch.int32, "load"),
-        kept=_ptr(out.kept, (E,), torch.int32, "kept"),
+        slots=_ptr(out.slots, (T, k), torch.int32, "slots", router_only),
+        load=_ptr(out.load, (E,), torch.int32, "load", router_only),
+        kept=_ptr(out.kept, (E,), torch.int32, "kept", router_only),
         aux_loss=_ptr(out.aux_loss, (1,), torch.float32, "aux_loss"),
         drop_mask=_ptr(out.drop_mask, (T, k), torch.uint8, "drop_mask", True),
         logits=_ptr(out.logits, (T, E), torch.float32, "logits", True),
@@ -415,7 +451,9 @@ def _outputs_struct(cfg, out: LayerOutputs) -> Outputs:
         h_disp=_ptr(out.h_disp, (E, C, cfg.d_ff), a, "h_disp", True),
         z_disp=_ptr(out.z_disp, (E, C, cfg.d_ff), a, "z_disp", True),
         h_dense=_ptr(out.h_dense, (T, cfg.d_ff_dense), a, "h_dense", True),
-        z_dense=_ptr(out.z_dense, (T, cfg.d_ff_dense), a, "z_dense", True))
+        z_dense=_ptr(out.z_dense, (T, cfg.d_ff_dense), a, "z_dense", True),
+        importance_loss=_ptr(out.importance_loss, (1,), torch.float32, "importance_loss", True),
+        load_loss=_ptr(out.load_loss, (1,), torch.float32, "load_loss", True))
 
 
 # ------------------------------------------------------------------ profiling

@@ -38,6 +38,14 @@ int check_config(const moe_config *c) {
   if (!isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
   if (c->drop_policy != MOE_DROP_TOKEN_ORDER && c->drop_policy != MOE_DROP_GATE_PRIORITY)
     return MOE_ERR_INVALID_ARG;
+  if (c->router < MOE_ROUTER_TOPK || c->router > MOE_ROUTER_NOISY_TOPK) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(c->w_importance) || !isfinite(c->w_load)) return MOE_ERR_INVALID_ARG;
+  if (c->router == MOE_ROUTER_TOP_P && !(c->top_p > 0.f && isfinite(c->top_p)))
+    return MOE_ERR_INVALID_ARG;
+  if (c->router == MOE_ROUTER_COSINE &&
+      (!(c->cos_tau > 0.f && isfinite(c->cos_tau)) || c->cos_dim < 1 || c->cos_dim > 256))
+    return MOE_ERR_INVALID_ARG;
+  if (c->router == MOE_ROUTER_NOISY_TOPK && c->E > 128) return MOE_ERR_UNSUPPORTED;
   if (c->E > 256 || c->k > 8 || c->T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (c->T * c->k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;  // int32 slots/positions
   if (c->d > (1 << 20) || c->d_ff > (1 << 20) || c->d_ff_dense > (1 << 20))
@@ -76,11 +84,30 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 struct Layout {
   size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
       total;
+  // router variants
+  size_t scores, cosl, embn, imp, loadp;
   // backward
   size_t dg, fcnt, ecount, dlog, dlog16, dY, Z, H, dZ, dX, dxr, Zd, Hd, dZd, dxd;
 };
 
 int64_t padded_experts(const moe_config *c) { return (c->E + 7) / 8 * 8; }
+
+static_assert(MOE_ROUTER_TOPK == moe::RV_TOPK && MOE_ROUTER_TOP_P == moe::RV_TOP_P &&
+                  MOE_ROUTER_COSINE == moe::RV_COSINE && MOE_ROUTER_NOISY_TOPK == moe::RV_NOISY,
+              "router ids");
+
+// the router runs as raw products + a variant epilogue (router_var.hip)
+// instead of the fused softmax-TopK router
+bool variant_router(const moe_config *c) {
+  return c->router != MOE_ROUTER_TOPK || c->w_importance != 0.f || c->w_load != 0.f;
+}
+
+// columns of the raw product: E, 2E (gate and noise scale) or the projection
+int64_t score_cols(const moe_config *c) {
+  if (c->router == MOE_ROUTER_NOISY_TOPK) return 2 * c->E;
+  if (c->router == MOE_ROUTER_COSINE) return c->cos_dim;
+  return c->E;
+}
 
 Layout layout(const moe_config *c, int entry) {
   Layout L{};
@@ -97,12 +124,23 @@ Layout layout(const moe_config *c, int entry) {
   };
   const bool gp = c->drop_policy == MOE_DROP_GATE_PRIORITY;
   const size_t segB = (size_t)c->T * (size_t)c->k * 4;
+  auto take_variant = [&]() {
+    if (!variant_router(c)) return;
+    L.scores = take((size_t)c->T * score_cols(c) * 4);
+    if (c->router == MOE_ROUTER_COSINE) {
+      L.cosl = take((size_t)c->T * c->E * 4);
+      L.embn = take((size_t)c->E * c->cos_dim * 4);
+    }
+    L.imp = take(blkE);
+    L.loadp = take(blkE);
+  };
   switch (entry) {
     case MOE_ENTRY_ROUTE:
       L.qsum = take(blkE);
       L.fcount = take(blkE);
       L.term = take(termE);
       L.zpart = take((size_t)nblk * 4);
+      take_variant();
       break;
     case MOE_ENTRY_DISPATCH:
       L.hist = take(blkE);
@@ -121,6 +159,7 @@ Layout layout(const moe_config *c, int entry) {
       L.offs = take(blkE);
       L.term = take(termE);
       L.zpart = take((size_t)nblk * 4);
+      take_variant();
       if (gp) L.seg = take(segB);
       L.x_disp = take((size_t)c->E * C * c->d * as);
       L.y_disp = take((size_t)c->E * C * c->d * as);
@@ -195,6 +234,91 @@ hipError_t do_router(const moe_config *c, const void *x, const void *wr, const f
   if (e == hipSuccess && z_loss)
     e = moe_host::launch_zloss_sum(zpart, moe_host::router_blocks(c->T), c->T, z_loss, s);
   return e;
+}
+
+// any router: the fused softmax-TopK router, or raw products -> (cosine
+// logits) -> the variant epilogue; imp_loss / load_loss optional
+hipError_t do_router_v(const moe_config *c, const Layout &L, void *ws, const void *x,
+                       const moe_weights *w, int32_t *ids, float *gates, float *logits,
+                       float *qsum, int32_t *fcount, int32_t *hist, float *zpart, float *z_loss,
+                       float *imp_loss, float *load_loss, hipStream_t s) {
+  if (!variant_router(c))
+    return do_router(c, x, w->w_router, w->b_router, ids, gates, logits, qsum, fcount, hist,
+                     zpart, z_loss, s);
+  const int bf = c->act_dtype == MOE_BF16, E = (int)c->E;
+  const int nblk = moe_host::router_blocks(c->T);
+  float *scores = (float *)at(ws, L.scores);
+  RouterArgs ra{};
+  ra.x = x;
+  ra.T = c->T;
+  ra.d = (int)c->d;
+  ra.k = (int)c->k;
+  ra.logits = scores;
+  ra.E = (int)score_cols(c);
+  ra.nw1 = ra.E;
+  if (c->router == MOE_ROUTER_COSINE) {
+    ra.w = w->w_proj;
+  } else {
+    ra.w = w->w_router;
+    if (c->router == MOE_ROUTER_NOISY_TOPK) {
+      ra.w2 = w->w_noise;
+      ra.nw1 = E;
+    }
+  }
+  hipError_t e = moe_host::launch_router_scores(ra, bf, s);
+  const float *src = scores;
+  if (e == hipSuccess && c->router == MOE_ROUTER_COSINE) {
+    float *embn = (float *)at(ws, L.embn), *cosl = (float *)at(ws, L.cosl);
+    e = moe_host::launch_emb_normalize(w->expert_emb, bf, E, c->cos_dim, embn, s);
+    if (e == hipSuccess)
+      e = moe_host::launch_cosine_logits(scores, embn, c->T, E, c->cos_dim, 1.f / c->cos_tau,
+                                         cosl, s);
+    src = cosl;
+  }
+  RouteVarArgs va{};
+  va.src = src;
+  va.noise = w->noise;
+  va.bias = w->b_router;
+  va.ids = ids;
+  va.gates = gates;
+  va.logits = logits;
+  va.qsum = qsum;
+  va.fcount = fcount;
+  va.hist = hist;
+  va.zpart = z_loss ? zpart : nullptr;
+  va.imp = (float *)at(ws, L.imp);
+  va.loadp = (float *)at(ws, L.loadp);
+  va.T = c->T;
+  va.E = E;
+  va.k = (int)c->k;
+  va.normalize = c->normalize_topk;
+  va.variant = c->router;
+  va.top_p = c->top_p;
+  if (e == hipSuccess) e = moe_host::launch_route_logits(va, s);
+  if (e == hipSuccess && z_loss) e = moe_host::launch_zloss_sum(zpart, nblk, c->T, z_loss, s);
+  if (e == hipSuccess && (imp_loss || load_loss))  // T = 0: no blocks, both losses 0
+    e = moe_host::launch_cov_loss(va.imp, va.loadp, nblk, E, c->w_importance, c->w_load,
+                                  imp_loss, load_loss, s);
+  return e;
+}
+
+// the router's weights and inputs for cfg->router
+bool router_weights_ok(const moe_config *c, const moe_weights *w) {
+  if (!opt(w->b_router, 4)) return false;
+  if (c->router == MOE_ROUTER_COSINE)
+    return need(w->w_proj, 1, 16) && need(w->expert_emb, 1, 16);
+  if (!need(w->w_router, 1, 16)) return false;
+  if (c->router == MOE_ROUTER_NOISY_TOPK)
+    return need(w->w_noise, 1, 16) && need(w->noise, c->T * c->E, 4);
+  return true;
+}
+
+// loss outputs need their weights
+bool loss_outputs_ok(const moe_config *c, const moe_outputs *o) {
+  if (!opt(o->importance_loss, 4) || !opt(o->load_loss, 4)) return false;
+  if (o->importance_loss && c->w_importance == 0.f) return false;
+  if (o->load_loss && c->w_load == 0.f) return false;
+  return true;
 }
 
 // place slots (token order, or gate priority through the segment array
@@ -302,6 +426,7 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
               void *ws, size_t ws_bytes, void *stream) {
   int rc = check_config(cfg);
   if (rc != MOE_OK) return rc;
+  if (cfg->router != MOE_ROUTER_TOPK) return MOE_ERR_UNSUPPORTED;
   const int64_t T = cfg->T, Tk = T * cfg->k;
   if (!need(x, T, 16) || !need(w_router, 1, 16) || !opt(b_router, 4) ||
       !need(expert_ids, Tk, 4) || !need(gates, Tk, 4) || !opt(logits, 4) ||
@@ -320,6 +445,34 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
     e = moe_host::launch_scan_aux(nullptr, qsum, fcount, moe_host::router_blocks(T),
                                   (int)cfg->E, T, 0, nullptr, nullptr, nullptr, term, s);
   if (e == hipSuccess) e = moe_host::launch_aux_sum(term, (int)cfg->E, cfg->aux_alpha, aux_loss, s);
+  return hip_status(e);
+}
+
+int moe_route_ex(const moe_config *cfg, const void *x, const moe_weights *w, moe_outputs *out,
+                 void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  const int64_t T = cfg->T, Tk = T * cfg->k;
+  if (!need(x, T, 16) || !router_weights_ok(cfg, w) || !need(out->expert_ids, Tk, 4) ||
+      !need(out->gates, Tk, 4) || !opt(out->logits, 4) || !need(out->aux_loss, 1, 4) ||
+      !opt(out->z_loss, 4) || !loss_outputs_ok(cfg, out))
+    return MOE_ERR_INVALID_ARG;
+  rc = check_ws(cfg, MOE_ENTRY_ROUTE, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  const Layout L = layout(cfg, MOE_ENTRY_ROUTE);
+  hipStream_t s = (hipStream_t)stream;
+  float *qsum = (float *)at(ws, L.qsum);
+  int32_t *fcount = (int32_t *)at(ws, L.fcount);
+  double *term = (double *)at(ws, L.term);
+  hipError_t e = do_router_v(cfg, L, ws, x, w, out->expert_ids, out->gates, out->logits, qsum,
+                             fcount, nullptr, (float *)at(ws, L.zpart), out->z_loss,
+                             out->importance_loss, out->load_loss, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_scan_aux(nullptr, qsum, fcount, moe_host::router_blocks(T),
+                                  (int)cfg->E, T, 0, nullptr, nullptr, nullptr, term, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_aux_sum(term, (int)cfg->E, cfg->aux_alpha, out->aux_loss, s);
   return hip_status(e);
 }
 
@@ -435,8 +588,8 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   if (!w || !out) return MOE_ERR_INVALID_ARG;
   const int64_t T = cfg->T, Tk = T * cfg->k, rowsE = cfg->E * capacity_of(cfg);
   const bool q8 = cfg->expert_wfmt == MOE_W_INT8_G128;
-  if (!need(x, T, 16) || !need(w->w_router, 1, 16) || !opt(w->b_router, 4) ||
-      !need(w->w1, 1, 16) || !need(w->w2, 1, 16))
+  if (!need(x, T, 16) || !router_weights_ok(cfg, w) || !need(w->w1, 1, 16) ||
+      !need(w->w2, 1, 16))
     return MOE_ERR_INVALID_ARG;
   if (q8 ? (!need(w->w1_scale, 1, 2) || !need(w->w2_scale, 1, 2))
          : (w->w1_scale || w->w2_scale))
@@ -447,7 +600,7 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
       !need(out->aux_loss, 1, 4) || !opt(out->drop_mask, 1) || !opt(out->logits, 4) ||
       !opt(out->x_disp, 16) || !opt(out->y_disp, 16) || !opt(out->dense_out, 16) ||
       !opt(out->z_loss, 4) || !opt(out->h_disp, 16) || !opt(out->z_disp, 16) ||
-      !opt(out->h_dense, 16) || !opt(out->z_dense, 16))
+      !opt(out->h_dense, 16) || !opt(out->z_dense, 16) || !loss_outputs_ok(cfg, out))
     return MOE_ERR_INVALID_ARG;
   (void)rowsE;
   rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
@@ -484,8 +637,9 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   }
   double *term = (double *)at(ws, L.term);
   if (e == hipSuccess)
-    e = do_router(cfg, x, w->w_router, w->b_router, out->expert_ids, out->gates, out->logits,
-                  qsum, fcount, hist, (float *)at(ws, L.zpart), out->z_loss, s);
+    e = do_router_v(cfg, L, ws, x, w, out->expert_ids, out->gates, out->logits, qsum, fcount,
+                    hist, (float *)at(ws, L.zpart), out->z_loss, out->importance_loss,
+                    out->load_loss, s);
   if (e == hipSuccess)
     e = moe_host::launch_scan_aux(hist, qsum, fcount, moe_host::router_blocks(T), (int)cfg->E, T,
                                   capacity_of(cfg), offs, out->load, out->kept, term, s);
@@ -513,7 +667,9 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
   int rc = check_config(cfg);
   if (rc != MOE_OK) return rc;
   if (!w || !fwd || !gr) return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_BF16 || cfg->expert_wfmt != MOE_W_PLAIN) return MOE_ERR_UNSUPPORTED;
+  if (cfg->act_dtype != MOE_BF16 || cfg->expert_wfmt != MOE_W_PLAIN ||
+      cfg->router != MOE_ROUTER_TOPK)
+    return MOE_ERR_UNSUPPORTED;
   const int64_t T = cfg->T, Tk = T * cfg->k, E = cfg->E, C = capacity_of(cfg);
   const int64_t d = cfg->d, F = cfg->d_ff, Fd = cfg->d_ff_dense;
   const bool pr = cfg->pr_moe != 0;

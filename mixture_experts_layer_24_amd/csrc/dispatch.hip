@@ -191,14 +191,15 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
       rem &= ~mask;
     }
     if (a < a1) {
+      // an id that is not an expert (an unused TopP slot) is no assignment
       if (seg) {
         slots[a] = valid ? slot : -1;
         if (valid) seg[ebase + slot] = (int32_t)a;
-        else if (drop) drop[a] = 1;
+        else if (drop) drop[a] = 0;
       } else {
         const bool keep = valid && (int64_t)slot < C;
         slots[a] = keep ? slot : -1;
-        if (drop) drop[a] = keep ? 0 : 1;
+        if (drop) drop[a] = (valid && !keep) ? 1 : 0;
       }
     }
   }

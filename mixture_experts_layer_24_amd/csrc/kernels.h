@@ -19,6 +19,28 @@ struct RouterArgs {
   float *zpart;       // [nblk] per-block sum of squared log-sum-exp (or null)
   int64_t T;
   int d, E, k, normalize;
+  const void *w2;     // raw-score mode: weight rows nw1.. come from here
+  int nw1;
+};
+
+// router variants (router_var.hip); the values are the C ABI's MOE_ROUTER_*
+enum { RV_TOPK = 0, RV_TOP_P = 1, RV_COSINE = 2, RV_NOISY = 3 };
+
+struct RouteVarArgs {
+  const float *src;    // [T, E] products (TopK, TopP) or cosine logits; noisy: [T, 2E]
+                       // (the gate's products, then the noise scale's)
+  const float *noise;  // [T, E] standard-normal draws (noisy)
+  const float *bias;   // [E] or null
+  int32_t *ids;        // [T, k], -1 = unused slot
+  float *gates;        // [T, k]
+  float *logits;       // [T, E] or null
+  float *qsum;         // [E, nblk] as RouterArgs
+  int32_t *fcount, *hist;
+  float *zpart;        // [nblk] or null
+  float *imp, *loadp;  // [E, nblk] importance / load partials, or null
+  int64_t T;
+  int E, k, normalize, variant;
+  float top_p;
 };
 
 // Grouped "NT" GEMM: for each group g < G and row m < rows[g] (or M_cap):
@@ -59,6 +81,14 @@ namespace moe_host {
 int router_blocks(int64_t T);
 hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
 hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s);
+hipError_t launch_router_scores(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
+hipError_t launch_route_logits(const moe::RouteVarArgs &a, hipStream_t s);
+hipError_t launch_emb_normalize(const void *emb, int act_bf16, int E, int de, float *embn,
+                                hipStream_t s);
+hipError_t launch_cosine_logits(const float *u, const float *embn, int64_t T, int E, int de,
+                                float inv_tau, float *cosl, hipStream_t s);
+hipError_t launch_cov_loss(const float *imp, const float *loadp, int nblk, int E, float w_imp,
+                           float w_load, float *out_imp, float *out_load, hipStream_t s);
 hipError_t launch_gemm_gen(const moe::GenArgs &a, bool a_kmajor, bool b_kmajor, bool dgelu,
                            const char *role, hipStream_t s);
 hipError_t launch_gelu_map(const moe::bf16 *z, moe::bf16 *h, int64_t n, hipStream_t s);

@@ -143,7 +143,10 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
 
 // NTW = 32-wide expert tiles per wave (Ep <= 64 * NTW).  BK = K step (64,
 // or 128 when d allows it and the two stages fit LDS, i.e. Ep <= 128).
-template <int NTW, int BK>
+// SCORES: only the raw fp32 product tile is written, to a.logits with row
+// stride E (the router variants' first step); rows e >= a.nw1 of the product
+// come from a.w2 (row e - a.nw1), so two weight matrices act as one.
+template <int NTW, int BK, bool SCORES = false>
 __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
   constexpr int EPMAX = 64 * NTW;
   static_assert(BK == 64 || (BK == 128 && NTW <= 2), "router tile does not fit LDS");
@@ -184,7 +187,12 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
       int e = p * RPP + crow;
       if (p * RPP < Ep) {
         if (e >= E) e = E - 1;
-        rw[p] = *(const u32x4 *)(W + (int64_t)e * d + k0 + cchk * 8);
+        if constexpr (SCORES) {
+          const bf16 *Wr = e < a.nw1 ? W + (int64_t)e * d : (const bf16 *)a.w2 + (int64_t)(e - a.nw1) * d;
+          rw[p] = *(const u32x4 *)(Wr + k0 + cchk * 8);
+        } else {
+          rw[p] = *(const u32x4 *)(W + (int64_t)e * d + k0 + cchk * 8);
+        }
       }
     }
   };
@@ -245,6 +253,14 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     }
   }
   __syncthreads();
+  if constexpr (SCORES) {
+    for (int idx = tid; idx < RBM * E; idx += 256) {
+      const int r = idx / E, e = idx - (idx / E) * E;
+      const int64_t t = (int64_t)blk * RBM + r;
+      if (t < a.T) a.logits[t * E + e] = L[r * ldl + e];
+    }
+    return;
+  }
   if (a.k <= 2)
     router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
@@ -252,6 +268,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
 }
 
 // fp32 activations: plain fp32 dot products (small shapes; correctness path)
+template <bool SCORES = false>
 __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
   __shared__ float L[RBM * 260];
   __shared__ float qpart[4][256];
@@ -265,11 +282,21 @@ __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
     const int r = idx / E, e = idx % E;
     const int64_t t = (int64_t)blk * RBM + r;
     float s = 0.f;
+    const float *Wr = W + (int64_t)e * d;
+    if (SCORES && e >= a.nw1) Wr = (const float *)a.w2 + (int64_t)(e - a.nw1) * d;
     if (t < a.T)
-      for (int i = 0; i < d; i++) s = fmaf(X[t * d + i], W[(int64_t)e * d + i], s);
+      for (int i = 0; i < d; i++) s = fmaf(X[t * d + i], Wr[i], s);
     L[r * ldl + e] = s;
   }
   __syncthreads();
+  if constexpr (SCORES) {
+    for (int idx = tid; idx < RBM * E; idx += 256) {
+      const int r = idx / E, e = idx - (idx / E) * E;
+      const int64_t t = (int64_t)blk * RBM + r;
+      if (t < a.T) a.logits[t * E + e] = L[r * ldl + e];
+    }
+    return;
+  }
   if (a.k <= 2)
     router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
@@ -333,8 +360,35 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
         default: MOE_LAUNCH("router_bf16_e256", (router_bf16_kernel<4, 64>), g, b, 0, s, a); break;
       }
     } else {
-      MOE_LAUNCH("router_f32", router_f32_kernel, dim3(nblk), dim3(256), 0, s, a);
+      MOE_LAUNCH("router_f32", router_f32_kernel<false>, dim3(nblk), dim3(256), 0, s, a);
     }
+  }
+  return hipGetLastError();
+}
+
+// raw fp32 products [T, a.E] of x with the a.E weight rows (a.w, then a.w2
+// from row a.nw1) into a.logits: the first step of the router variants
+hipError_t launch_router_scores(const RouterArgs &a, int act_bf16, hipStream_t s) {
+  const int nblk = router_blocks(a.T);
+  if (nblk <= 0) return hipGetLastError();
+  const dim3 g(nblk), b(256);
+  if (!act_bf16) {
+    MOE_LAUNCH("router_scores_f32", router_f32_kernel<true>, g, b, 0, s, a);
+    return hipGetLastError();
+  }
+  const int ntw = ((a.E + 31) / 32 + 1) / 2;
+  const bool k128 = a.d % 128 == 0;
+  switch (ntw) {
+    case 1:
+      if (k128) MOE_LAUNCH("router_scores_n64", (router_bf16_kernel<1, 128, true>), g, b, 0, s, a);
+      else MOE_LAUNCH("router_scores_n64", (router_bf16_kernel<1, 64, true>), g, b, 0, s, a);
+      break;
+    case 2:
+      if (k128) MOE_LAUNCH("router_scores_n128", (router_bf16_kernel<2, 128, true>), g, b, 0, s, a);
+      else MOE_LAUNCH("router_scores_n128", (router_bf16_kernel<2, 64, true>), g, b, 0, s, a);
+      break;
+    case 3: MOE_LAUNCH("router_scores_n192", (router_bf16_kernel<3, 64, true>), g, b, 0, s, a); break;
+    default: MOE_LAUNCH("router_scores_n256", (router_bf16_kernel<4, 64, true>), g, b, 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -122,3 +122,20 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu",
         inp["wm1"] = inp["wm2"] = None
     return inp
 
+
+
+def router_inputs(wl: Workload, router: str, seed: int = 0, device="cpu",
+                  cos_dim: int = 64) -> dict:
+    """The extra inputs of a router variant: noisy TopK -> w_noise [E, d]
+    (std w_std) and the call's standard-normal draws noise [T, E] fp32;
+    cosine -> w_proj [cos_dim, d] (std w_std) and expert_emb [E, cos_dim]
+    (std 1).  Seeded like the other inputs; nothing for the other routers."""
+    dt = _act_dtype(wl)
+    out = {}
+    if router == "noisy_topk":
+        out["w_noise"] = normal((wl.E, wl.d), wl.w_std, seed, "w_noise", device, dt)
+        out["noise"] = normal((wl.T, wl.E), 1.0, seed, "noise", device, torch.float32)
+    if router == "cosine":
+        out["w_proj"] = normal((cos_dim, wl.d), wl.w_std, seed, "w_proj", device, dt)
+        out["expert_emb"] = normal((wl.E, cos_dim), 1.0, seed, "expert_emb", device, dt)
+    return out

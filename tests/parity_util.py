@@ -65,14 +65,18 @@ def check_ids(gpu_ids, ref_ids, logits64, k):
 
 
 def valid_token_order_dispatch(ids, slots, load, kept, C, E):
-    """Property check of a dispatch result against its own ids (used only when a
-    near-tie flipped an id, so the oracle's dispatch no longer applies)."""
+    """Property check of a dispatch result against its own ids (used when a
+    near-tie flipped an id, so the oracle's dispatch no longer applies, and at
+    full size); ids < 0 are unused slots."""
     ids, slots = np.asarray(ids), np.asarray(slots)
     T, k = ids.shape
     n = np.zeros(E, np.int64)
     for t in range(T):
         for j in range(k):
             e = ids[t, j]
+            if e < 0:  # an unused slot (TopP) is no assignment
+                assert slots[t, j] == -1
+                continue
             want = n[e] if n[e] < C else -1
             assert slots[t, j] == want
             n[e] += 1

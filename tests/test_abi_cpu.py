@@ -86,6 +86,13 @@ BAD_CONFIGS = [
     (dict(d=192, wfmt="int8"), binding.MOE_ERR_UNSUPPORTED),  # int8 needs d % 128 == 0
     (dict(act="f32", wfmt="int8"), binding.MOE_ERR_UNSUPPORTED),
     (dict(pr_moe=True, d_ff_dense=0), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="top_p", top_p=0.0), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="top_p", top_p=float("inf")), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="cosine", cos_tau=0.1, cos_dim=0), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="cosine", cos_tau=0.1, cos_dim=257), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="cosine", cos_tau=0.0, cos_dim=64), binding.MOE_ERR_INVALID_ARG),
+    (dict(router="noisy_topk", E=200), binding.MOE_ERR_UNSUPPORTED),  # 2E score columns
+    (dict(w_load=float("nan")), binding.MOE_ERR_INVALID_ARG),
 ]
 
 
@@ -183,3 +190,37 @@ def _header_fields(struct):
 def test_binding_structs_follow_the_header(struct, cls):
     # same members in the same order: the ctypes layout is the C layout
     assert [f[0] for f in getattr(binding, cls)._fields_] == _header_fields(struct)
+
+
+def test_router_variant_arguments(L):
+    ok = 1 << 20
+    cfg = binding.make_config(T=16, d=128, E=4, k=2, d_ff=128, router="top_p", top_p=0.5)
+    cfg.router = 9
+    assert L.moe_capacity(ctypes.byref(cfg)) == binding.MOE_ERR_INVALID_ARG
+    cfg.router = binding.ROUTERS["top_p"]
+    # the softmax-TopK entry point runs no other router
+    rc = L.moe_route(ctypes.byref(cfg), ok, ok, None, ok, ok, None, ok, None, ok, 1 << 30, None)
+    assert rc == binding.MOE_ERR_UNSUPPORTED
+    # the variants' buffers are in the router and layer workspaces
+    plain = binding.make_config(T=16, d=128, E=4, k=2, d_ff=128)
+    for entry in (binding.ENTRY_ROUTE, binding.ENTRY_LAYER):
+        assert binding.workspace_bytes(cfg, entry) > binding.workspace_bytes(plain, entry)
+    ws = binding.workspace_bytes(cfg, binding.ENTRY_ROUTE)
+
+    def route_ex(c, weights, **outs):
+        W = binding.Weights(**weights)
+        O = binding.Outputs(expert_ids=ok, gates=ok, aux_loss=ok, **outs)
+        return L.moe_route_ex(ctypes.byref(c), ok, ctypes.byref(W), ctypes.byref(O), ok,
+                              binding.workspace_bytes(c, binding.ENTRY_ROUTE), None)
+
+    assert route_ex(cfg, dict(w_router=None)) == binding.MOE_ERR_INVALID_ARG
+    # a loss output needs its weight
+    assert route_ex(cfg, dict(w_router=ok), importance_loss=ok) == binding.MOE_ERR_INVALID_ARG
+    noisy = binding.make_config(T=16, d=128, E=4, k=2, d_ff=128, router="noisy_topk")
+    assert route_ex(noisy, dict(w_router=ok, w_noise=ok)) == binding.MOE_ERR_INVALID_ARG
+    assert route_ex(noisy, dict(w_router=ok, noise=ok)) == binding.MOE_ERR_INVALID_ARG
+    cos = binding.make_config(T=16, d=128, E=4, k=2, d_ff=128, router="cosine", cos_tau=0.1,
+                              cos_dim=32)
+    assert route_ex(cos, dict(w_proj=ok)) == binding.MOE_ERR_INVALID_ARG
+    assert route_ex(cos, dict(w_proj=ok, expert_emb=ok + 4)) == binding.MOE_ERR_INVALID_ARG
+    assert ws > 0
