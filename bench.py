@@ -69,6 +69,14 @@ def parse():
                    help="time the layer backward (after one forward) instead of the forward")
     p.add_argument("--train", action="store_true",
                    help="time forward (keeping the FFN activations) + backward as one step")
+    p.add_argument("--router", default="topk", choices=["topk", "top_p", "cosine", "noisy_topk"],
+                   help="router variant (the workloads use topk)")
+    p.add_argument("--top-p", type=float, default=0.5, help="top_p router: threshold P")
+    p.add_argument("--cos-tau", type=float, default=0.1, help="cosine router: temperature")
+    p.add_argument("--cos-dim", type=int, default=64, help="cosine router: projection width")
+    p.add_argument("--k", type=int, default=0, help="override the workload's k (slots per token)")
+    p.add_argument("--router-losses", action="store_true",
+                   help="also compute the Importance and Load losses (weights 0.01)")
     p.add_argument("--recompute", action="store_true",
                    help="backward / train: do not keep the FFN activations in the forward; "
                         "the backward recomputes them")
@@ -84,7 +92,7 @@ def parse():
 
 
 # ------------------------------------------------------------- algorithmic work
-def kernel_work(wl, kept, cfg_C):
+def kernel_work(wl, kept, cfg_C, router="topk", cos_dim=64):
     """Algorithmic bytes and FLOPs of one launch of each kernel class.
 
     Expert GEMM1: reads the weights of experts with >= 1 kept row once, reads
@@ -130,6 +138,16 @@ def kernel_work(wl, kept, cfg_C):
             out[c] = dict(bytes=(T * d + F * d + T * F) * sa, flops=2.0 * T * d * F)
     out["bwd_router"] = dict(bytes=(wl.T * wl.d + wl.E * wl.d + wl.T * wl.E) * sa,
                              flops=2.0 * wl.T * wl.d * wl.E)
+    # router variants: raw products into [T, ns] fp32 (ns = E, 2E or the
+    # cosine width), the cosine logits, the variant epilogue
+    ns = {"noisy_topk": 2 * wl.E, "cosine": cos_dim}.get(router, wl.E)
+    out["router_scores"] = dict(bytes=(wl.T * wl.d + ns * wl.d) * sa + wl.T * ns * 4,
+                                flops=2.0 * wl.T * wl.d * ns)
+    out["cosine_logits"] = dict(bytes=(wl.T * cos_dim + wl.E * cos_dim + wl.T * wl.E) * 4,
+                                flops=2.0 * wl.T * wl.E * cos_dim)
+    out["route_logits"] = dict(bytes=wl.T * ns * 4 + (wl.T * wl.E * 4 if router == "noisy_topk"
+                                                      else 0) + wl.T * wl.k * 8,
+                               flops=0.0)
     out["gather"] = dict(bytes=2.0 * n_kept * wl.d * sa, flops=0.0)
     out["combine"] = dict(bytes=(n_kept + wl.T * (1 + int(wl.add_skip) + int(wl.pr_moe)))
                           * wl.d * sa, flops=2.0 * n_kept * wl.d)
@@ -145,7 +163,8 @@ def classify(name: str) -> str | None:
                         ("bwd_expert_dx", "bwd_expert_dx"), ("bwd_expert_dw", "bwd_expert_dw"),
                         ("bwd_dense_z", "bwd_dense_z"), ("bwd_dense_dz", "bwd_dense_dz"),
                         ("bwd_dense_dx", "bwd_dense_dx"), ("bwd_dense_dw", "bwd_dense_dw"),
-                        ("bwd_router_", "bwd_router"),
+                        ("bwd_router_", "bwd_router"), ("router_scores", "router_scores"),
+                        ("cosine_logits", "cosine_logits"), ("route_logits", "route_logits"),
                         ("router", "router"), ("gather", "gather"), ("combine", "combine")):
         if name.startswith(prefix):
             return cls
@@ -305,14 +324,30 @@ def main():
 
     name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]
+    if args.k:
+        wl = wl.replace(k=args.k)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = synth.make_inputs(wl, seed=args.seed, device=dev)
-    cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy)
+    rkw = {}
+    if args.router != "topk" or args.router_losses:
+        inp.update(synth.router_inputs(wl, args.router, seed=args.seed, device=dev,
+                                       cos_dim=args.cos_dim))
+        rkw = dict(router=args.router)
+        if args.router == "top_p":
+            rkw["top_p"] = args.top_p
+        if args.router == "cosine":
+            rkw.update(cos_tau=args.cos_tau, cos_dim=args.cos_dim)
+        if args.router_losses:
+            rkw.update(w_importance=0.01, w_load=0.01)
+    cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy,
+                            **rkw)
     C = binding.capacity(cfg)
     bwd = args.backward or args.train
     out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss, logits=bwd, x_disp=bwd,
-                                y_disp=bwd, saved_activations=bwd and not args.recompute)
+                                y_disp=bwd, saved_activations=bwd and not args.recompute,
+                                importance_loss=args.router_losses,
+                                load_loss=args.router_losses)
     ws = binding.alloc_workspace(cfg, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -373,7 +408,7 @@ def main():
           file=sys.stderr, flush=True)
 
     kept = out.kept.cpu().tolist()
-    work = kernel_work(wl, kept, C)
+    work = kernel_work(wl, kept, C, args.router, args.cos_dim)
     kern = {}
     for n, (cnt, tot) in prof.items():
         kern[n] = {"launches": cnt, "avg_ms": tot / cnt, "ms_per_step": tot / args.steps,
@@ -417,6 +452,8 @@ def main():
                    "pass": "train" if args.train else "backward" if args.backward else "forward",
                    **({"ffn_activations": "recomputed" if args.recompute else "saved"}
                       if bwd else {}),
+                   **({"router": args.router,
+                       **{n: v for n, v in rkw.items() if n != "router"}} if rkw else {}),
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
@@ -424,7 +461,7 @@ def main():
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not bwd:
+    if not args.no_cpu_baseline and not bwd and not rkw and not args.k:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(res))

@@ -18,6 +18,7 @@
 namespace moe {
 
 constexpr int VBT = 64;  // tokens per block, as the fused router
+constexpr int VW = 16;   // waves per block of the variant epilogue (4 tokens each)
 
 __device__ __forceinline__ float softplus_f(float z) {
   return z > 0.f ? z + log1pf(expf(-z)) : log1pf(expf(z));
@@ -26,7 +27,7 @@ __device__ __forceinline__ float softplus_f(float z) {
 // standard normal distribution function
 __device__ __forceinline__ float phi_cdf(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
 
-// One wave per token row (16 rows per wave), a lane holding experts
+// One wave per token row (VBT / VW rows per wave), a lane holding experts
 // lane + 64 i.  Logits: TopK / TopP: products + bias; cosine: the cosine
 // logits + bias; noisy: clean = products[e] + bias, sigma = softplus(
 // products[E + e]), logit = clean + noise * sigma.  Selection by repeated
@@ -40,16 +41,18 @@ __device__ __forceinline__ float phi_cdf(float z) { return 0.5f * erfcf(-z * 0.7
 // otherwise 1 for a taken expert, 0 else.  No float atomics: every per-expert
 // sum is owned by one lane and summed over the waves in a fixed order.
 template <int MAXK>
-__global__ __launch_bounds__(256) void route_logits_kernel(RouteVarArgs a) {
-  __shared__ float qpart[4][256], ipart[4][256], lpart[4][256];
+__global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
+  __shared__ float qpart[VW][256], ipart[VW][256], lpart[VW][256];
   __shared__ int fcnt[256], hcnt[256];
-  __shared__ float zw[4];
+  __shared__ float zw[VW];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, blk = blockIdx.x;
   const int E = a.E, k = a.k;
   const bool noisy = a.variant == RV_NOISY, topp = a.variant == RV_TOP_P;
   const int ns = noisy ? 2 * E : E;
-  fcnt[tid] = 0;
-  hcnt[tid] = 0;
+  if (tid < 256) {
+    fcnt[tid] = 0;
+    hcnt[tid] = 0;
+  }
   __syncthreads();
   float q[4] = {0.f, 0.f, 0.f, 0.f}, imp[4] = {0.f, 0.f, 0.f, 0.f}, ld[4] = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f, bias[4];
@@ -59,8 +62,8 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteVarArgs a) {
     bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
   }
   const bool renorm = noisy ? true : (topp ? a.normalize != 0 : (k >= 2 && a.normalize));
-  for (int rr = 0; rr < VBT / 4; rr++) {
-    const int r = wave * (VBT / 4) + rr;
+  for (int rr = 0; rr < VBT / VW; rr++) {
+    const int r = wave * (VBT / VW) + rr;
     const int64_t t = (int64_t)blk * VBT + r;
     if (t >= a.T) break;
     float v[4], clean[4], sig[4];
@@ -207,15 +210,25 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteVarArgs a) {
   }
   if (lane == 0) zw[wave] = zacc;
   __syncthreads();
-  if (a.zpart && tid == 0) a.zpart[blk] = ((zw[0] + zw[1]) + zw[2]) + zw[3];
+  if (a.zpart && tid == 0) {
+    float z = 0.f;
+    for (int w = 0; w < VW; w++) z += zw[w];
+    a.zpart[blk] = z;
+  }
   const int e = tid;
-  if (e < E) {
+  if (e < E) {  // the waves' partials summed in wave order
     const int64_t o = (int64_t)e * gridDim.x + blk;
-    a.qsum[o] = ((qpart[0][e] + qpart[1][e]) + qpart[2][e]) + qpart[3][e];
+    float sq = 0.f, si = 0.f, sl = 0.f;
+    for (int w = 0; w < VW; w++) {
+      sq += qpart[w][e];
+      si += ipart[w][e];
+      sl += lpart[w][e];
+    }
+    a.qsum[o] = sq;
     a.fcount[o] = fcnt[e];
     if (a.hist) a.hist[o] = hcnt[e];
-    if (a.imp) a.imp[o] = ((ipart[0][e] + ipart[1][e]) + ipart[2][e]) + ipart[3][e];
-    if (a.loadp) a.loadp[o] = ((lpart[0][e] + lpart[1][e]) + lpart[2][e]) + lpart[3][e];
+    if (a.imp) a.imp[o] = si;
+    if (a.loadp) a.loadp[o] = sl;
   }
 }
 
@@ -239,13 +252,17 @@ __global__ __launch_bounds__(256) void emb_normalize_kernel(const void *emb, int
 }
 
 // cosl[t][e] = <embn[e], u[t]> / (tau |u[t]|), 0 when |u[t]| = 0; u = the
-// projected tokens [T, de] fp32.  A block takes 64 tokens x all experts:
-// features in chunks of 64 through LDS, 64 * E / 256 outputs per thread.
+// projected tokens [T, de] fp32.  A block takes 64 tokens x all experts in
+// fp32 on the vector ALUs: features in chunks of 32 through LDS, stored
+// feature-major so that a thread's 4 tokens and 8 experts are 16-byte reads;
+// thread (tid / 16, tid % 16) owns tokens 4 (tid / 16) .. + 3 and experts
+// 8 (tid % 16) .. + 7 of each 128-expert half.
 __global__ __launch_bounds__(256) void cosine_logits_kernel(const float *u, const float *embn,
                                                             int64_t T, int E, int de,
                                                             float inv_tau, float *cosl) {
-  constexpr int JC = 64;
-  __shared__ float us[VBT][JC + 1], es[256][JC + 1];
+  constexpr int JC = 32, UP = VBT + 4, EP = 256 + 4;
+  __shared__ __attribute__((aligned(16))) float us[JC][UP];
+  __shared__ __attribute__((aligned(16))) float es[JC][EP];
   __shared__ float nrm[VBT];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int64_t t0 = (int64_t)blockIdx.x * VBT;
@@ -260,63 +277,85 @@ __global__ __launch_bounds__(256) void cosine_logits_kernel(const float *u, cons
     s = wave_sum(s);
     if (lane == 0) nrm[r] = sqrtf(s);
   }
-  const int nout = VBT * E;
-  float acc[VBT];  // outputs tid + 256 q, q < nout / 256 (<= 64)
+  const int tr = (tid / 16) * 4, tc = (tid % 16) * 8;
+  const int halves = E > 128 ? 2 : 1;
+  float acc[2][4][8];
 #pragma unroll
-  for (int q = 0; q < VBT; q++) acc[q] = 0.f;
+  for (int h = 0; h < 2; h++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int c = 0; c < 8; c++) acc[h][i][c] = 0.f;
   for (int j0 = 0; j0 < de; j0 += JC) {
     const int jn = de - j0 < JC ? de - j0 : JC;
     __syncthreads();
     for (int idx = tid; idx < VBT * JC; idx += 256) {
       const int r = idx / JC, jj = idx % JC;
-      us[r][jj] = (t0 + r < T && jj < jn) ? u[(t0 + r) * de + j0 + jj] : 0.f;
+      us[jj][r] = (t0 + r < T && jj < jn) ? u[(t0 + r) * de + j0 + jj] : 0.f;
     }
-    for (int idx = tid; idx < E * JC; idx += 256) {
+    for (int idx = tid; idx < 256 * JC; idx += 256) {
       const int e = idx / JC, jj = idx % JC;
-      es[e][jj] = jj < jn ? embn[(int64_t)e * de + j0 + jj] : 0.f;
+      es[jj][e] = (e < E && jj < jn) ? embn[(int64_t)e * de + j0 + jj] : 0.f;
     }
     __syncthreads();
+    for (int jj = 0; jj < jn; jj++) {
+      const f32x4 a = *(const f32x4 *)&us[jj][tr];
 #pragma unroll
-    for (int q = 0; q < VBT; q++) {
-      const int o = tid + 256 * q;
-      if (o < nout) {
-        const int r = o / E, e = o - (o / E) * E;
-        float s = acc[q];
-        for (int jj = 0; jj < jn; jj++) s = fmaf(us[r][jj], es[e][jj], s);
-        acc[q] = s;
+      for (int h = 0; h < 2; h++) {
+        if (h < halves) {
+          const f32x4 b0 = *(const f32x4 *)&es[jj][h * 128 + tc];
+          const f32x4 b1 = *(const f32x4 *)&es[jj][h * 128 + tc + 4];
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              acc[h][i][c] = fmaf(a[i], b0[c], acc[h][i][c]);
+              acc[h][i][c + 4] = fmaf(a[i], b1[c], acc[h][i][c + 4]);
+            }
+        }
       }
     }
   }
-  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < VBT; q++) {
-    const int o = tid + 256 * q;
-    if (o < nout) {
-      const int r = o / E, e = o - (o / E) * E;
-      if (t0 + r < T) cosl[(t0 + r) * E + e] = nrm[r] > 0.f ? acc[q] * inv_tau / nrm[r] : 0.f;
-    }
-  }
+  for (int h = 0; h < 2; h++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const int r = tr + i, e = h * 128 + tc + c;
+        if (h < halves && e < E && t0 + r < T)
+          cosl[(t0 + r) * E + e] = nrm[r] > 0.f ? acc[h][i][c] * inv_tau / nrm[r] : 0.f;
+      }
 }
 
 // Importance and Load losses: the per-expert sums of the block partials in
-// fp64 in a fixed order, then w * variance / mean^2 (population variance; 0
-// when the mean is 0), one per loss.
-__global__ __launch_bounds__(256) void cov_loss_kernel(const float *imp, const float *loadp,
-                                                       int nblk, int E, float w_imp, float w_load,
-                                                       float *out_imp, float *out_load) {
+// fp64 in a fixed order (a wave per expert: lane-strided sums, then a
+// butterfly), then w * variance / mean^2 (population variance; 0 when the
+// mean is 0), one per loss.
+__global__ __launch_bounds__(1024) void cov_loss_kernel(const float *imp, const float *loadp,
+                                                        int nblk, int E, float w_imp,
+                                                        float w_load, float *out_imp,
+                                                        float *out_load) {
   __shared__ double vi[256], vl[256];
-  const int e = threadIdx.x;
-  if (e < E) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  for (int e = wave; e < E; e += 16) {
     double si = 0.0, sl = 0.0;
-    for (int b = 0; b < nblk; b++) {
+    for (int b = lane; b < nblk; b += kWave) {
       si += (double)imp[(int64_t)e * nblk + b];
       sl += (double)loadp[(int64_t)e * nblk + b];
     }
-    vi[e] = si;
-    vl[e] = sl;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      si += __shfl_xor(si, m, kWave);
+      sl += __shfl_xor(sl, m, kWave);
+    }
+    if (lane == 0) {
+      vi[e] = si;
+      vl[e] = sl;
+    }
   }
   __syncthreads();
-  if (e == 0) {
+  if (threadIdx.x == 0) {
     auto cov2 = [&](const double *v) {
       double mean = 0.0;
       for (int i = 0; i < E; i++) mean += v[i];
@@ -341,9 +380,9 @@ hipError_t launch_route_logits(const RouteVarArgs &a, hipStream_t s) {
   const int nblk = router_blocks(a.T);
   if (nblk <= 0) return hipGetLastError();
   if (a.k <= 2)
-    MOE_LAUNCH("route_logits", route_logits_kernel<2>, dim3(nblk), dim3(256), 0, s, a);
+    MOE_LAUNCH("route_logits", route_logits_kernel<2>, dim3(nblk), dim3(64 * VW), 0, s, a);
   else
-    MOE_LAUNCH("route_logits", route_logits_kernel<8>, dim3(nblk), dim3(256), 0, s, a);
+    MOE_LAUNCH("route_logits", route_logits_kernel<8>, dim3(nblk), dim3(64 * VW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -365,7 +404,7 @@ hipError_t launch_cosine_logits(const float *u, const float *embn, int64_t T, in
 
 hipError_t launch_cov_loss(const float *imp, const float *loadp, int nblk, int E, float w_imp,
                            float w_load, float *out_imp, float *out_load, hipStream_t s) {
-  MOE_LAUNCH("cov_loss", cov_loss_kernel, dim3(1), dim3(256), 0, s, imp, loadp, nblk, E, w_imp,
+  MOE_LAUNCH("cov_loss", cov_loss_kernel, dim3(1), dim3(1024), 0, s, imp, loadp, nblk, E, w_imp,
              w_load, out_imp, out_load);
   return hipGetLastError();
 }
