@@ -367,34 +367,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
-  // pass 0 writes C; with the pre-activation output (GELU == 2), pass 1 writes Zpre
-  for (int pass = 0; pass < (GELU == 2 ? 2 : 1); pass++)
-  for (int band = 0; band < WM; band++) {
-    __syncthreads();  // stage buffers (or the previous band) no longer read
-    if (wm == band) {
+  // with the pre-activation output (GELU == 2) one pass writes the raw sums to
+  // Zpre first; then C (the GELU, if any, applied per element as it is
+  // written, so no second copy of the accumulators is ever live)
+  auto bands = [&](auto raw_tag) __attribute__((always_inline)) {
+    constexpr bool RAW = decltype(raw_tag)::value;
+    bf16 *Og = RAW ? Zg : Cg;
+    for (int band = 0; band < WM; band++) {
+      __syncthreads();  // stage buffers (or the previous band) no longer read
+      if (wm == band) {
 #pragma unroll
-      for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++)
+          for (int j = 0; j < TN; j++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int Cc = wn * WTN + j * 32 + (lane & 31);
-            float v = acc[i][j][r];
-            if (GELU && pass == 0) v = gelu_f(v);
-            *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
-          }
+            for (int r = 0; r < 16; r++) {
+              const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              const int Cc = wn * WTN + j * 32 + (lane & 31);
+              float v = acc[i][j][r];
+              if (GELU && !RAW) v = gelu_f(v);
+              *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
+            }
+      }
+      __syncthreads();
+      const int64_t r0 = m0 + band * WTM;
+      const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
+      for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
+        const int R = idx / OCPR, ch = idx - R * OCPR;
+        if (R < mrows)
+          *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+      }
     }
-    __syncthreads();
-    bf16 *Og = pass ? Zg : Cg;
-    const int64_t r0 = m0 + band * WTM;
-    const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
-    for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
-      const int R = idx / OCPR, ch = idx - R * OCPR;
-      if (R < mrows)
-        *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
-    }
+  };
+  if constexpr (GELU == 2) {
+    bands(std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);  // keep the two passes apart
   }
+  bands(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -581,34 +590,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   constexpr int CROW = BN * 2 + 16;
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;
-  // pass 0 writes C; with the pre-activation output (GELU == 2), pass 1 writes Zpre
-  for (int pass = 0; pass < (GELU == 2 ? 2 : 1); pass++)
-  for (int band = 0; band < WM; band++) {
-    __syncthreads();
-    if (wm == band) {
+  // with the pre-activation output (GELU == 2) one pass writes the raw sums to
+  // Zpre first; then C (the GELU, if any, applied per element as it is
+  // written, so no second copy of the accumulators is ever live)
+  auto bands = [&](auto raw_tag) __attribute__((always_inline)) {
+    constexpr bool RAW = decltype(raw_tag)::value;
+    bf16 *Og = RAW ? Zg : Cg;
+    for (int band = 0; band < WM; band++) {
+      __syncthreads();
+      if (wm == band) {
 #pragma unroll
-      for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++)
+          for (int j = 0; j < TN; j++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int Cc = wn * WTN + j * 32 + (lane & 31);
-            float v = acc[i][j][r];
-            if (GELU && pass == 0) v = gelu_f(v);
-            *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
-          }
+            for (int r = 0; r < 16; r++) {
+              const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              const int Cc = wn * WTN + j * 32 + (lane & 31);
+              float v = acc[i][j][r];
+              if (GELU && !RAW) v = gelu_f(v);
+              *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
+            }
+      }
+      __syncthreads();
+      const int64_t r0 = m0 + band * WTM;
+      const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
+      for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
+        const int R = idx / OCPR, ch = idx - R * OCPR;
+        if (R < mrows)
+          *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+      }
     }
-    __syncthreads();
-    bf16 *Og = pass ? Zg : Cg;
-    const int64_t r0 = m0 + band * WTM;
-    const int64_t mrows = rows - r0 < WTM ? rows - r0 : WTM;
-    for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
-      const int R = idx / OCPR, ch = idx - R * OCPR;
-      if (R < mrows)
-        *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
-    }
+  };
+  if constexpr (GELU == 2) {
+    bands(std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);  // keep the two passes apart
   }
+  bands(std::false_type{});
 }
 
 // fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
