@@ -217,10 +217,13 @@ __device__ __forceinline__ bf16x8 frag_kmajor(uint32_t tile, int row0, int kbase
   return out;
 }
 
-template <bool AKM, bool BKM, bool DGELU, int NS>
+template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32>
 __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
-  constexpr int BM = 128, BN = 128, BK = 32, TILE = 8192;  // bytes per operand tile
+  static_assert(BK == 32 || BK == 64, "K step");
+  constexpr int BM = 128, BN = 128, TILE = 128 * BK * 2;  // bytes per operand tile
   constexpr int STAGE = 2 * TILE;
+  constexpr int CH = TILE / 1024 / 4;      // 1-KB DMA chunks per wave per operand
+  constexpr int ROWB = BK * 2, CPR = ROWB / 16, RPC = 1024 / ROWB;  // K-contiguous rows
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   const int tid = threadIdx.x, lane = lane_id();
@@ -242,25 +245,25 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
   // per-tile operand bases (bytes) and this lane's offsets for its chunks:
-  // every wave moves 2 chunks (1 KB each) of A and 2 of B per stage
+  // every wave moves CH chunks (1 KB each) of A and CH of B per stage
   const char *abase, *bbase;
   int64_t astep, bstep;  // bytes per K step
-  uint32_t voa[2], vob[2];
+  uint32_t voa[CH], vob[CH];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int q = 2 * wave + i;
-    if constexpr (!AKM) {  // rows of 64 bytes: 16 rows per chunk
-      const int R = 16 * q + lane / 4, slot = lane % 4;
+  for (int i = 0; i < CH; i++) {
+    const int q = CH * wave + i;
+    if constexpr (!AKM) {  // rows of ROWB bytes: RPC rows per chunk
+      const int R = RPC * q + lane / CPR, slot = lane % CPR;
       int64_t m = m0 + R;
       if (m >= mvalid) m = mvalid - 1;
-      voa[i] = (uint32_t)((m - m0) * a.a_m * 2 + ((slot ^ swz_slot<32>(R)) << 4));
+      voa[i] = (uint32_t)((m - m0) * a.a_m * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
     } else {  // k rows of 256 bytes: 4 rows per chunk
       const int k = 4 * q + lane / 16, slot = lane % 16;
       voa[i] = (uint32_t)(k * a.a_k * 2 + ((slot ^ swz_km(k)) << 4));
     }
     if constexpr (!BKM) {
-      const int R = 16 * q + lane / 4, slot = lane % 4;
-      vob[i] = (uint32_t)(R * a.b_n * 2 + ((slot ^ swz_slot<32>(R)) << 4));
+      const int R = RPC * q + lane / CPR, slot = lane % CPR;
+      vob[i] = (uint32_t)(R * a.b_n * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
     } else {
       const int k = 4 * q + lane / 16, slot = lane % 16;
       vob[i] = (uint32_t)(k * a.b_k * 2 + ((slot ^ swz_km(k)) << 4));
@@ -283,13 +286,13 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   auto issue = [&](int st, int kt) __attribute__((always_inline)) {
     const char *ga = abase + (int64_t)kt * astep, *gb = bbase + (int64_t)kt * bstep;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < CH; i++)
       dma16<false>(ga, voa[i],
-                   __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (2 * wave + i) * 1024));
+                   __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (CH * wave + i) * 1024));
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < CH; i++)
       dma16<false>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILE +
-                                                              (2 * wave + i) * 1024));
+                                                              (CH * wave + i) * 1024));
   };
 
   f32x16 acc[2][2];
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
     if (p < ksteps) issue(p, p);
   for (int kt = 0; kt < ksteps; kt++) {
     if (kt + NS - 2 < ksteps)
-      wait_vmcnt<(NS - 2) * 4>();
+      wait_vmcnt<(NS - 2) * 2 * CH>();
     else
       wait_vmcnt<0>();
     __syncthreads();
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
           af[i] = frag_kmajor(ta, row0, 16 * s, lane);
         } else {
           const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
-          af[i] = *(const bf16x8 *)(smem + st * STAGE + R * 64 + ((c ^ swz_slot<32>(R)) << 4));
+          af[i] = *(const bf16x8 *)(smem + st * STAGE + R * ROWB + ((c ^ swz_slot<BK>(R)) << 4));
         }
       }
 #pragma unroll
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
         } else {
           const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
           bfr[j] =
-              *(const bf16x8 *)(smem + st * STAGE + TILE + R * 64 + ((c ^ swz_slot<32>(R)) << 4));
+              *(const bf16x8 *)(smem + st * STAGE + TILE + R * ROWB + ((c ^ swz_slot<BK>(R)) << 4));
         }
       }
 #pragma unroll
@@ -748,12 +751,20 @@ static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s
   return hipGetLastError();
 }
 
+// K steps of 64 (3 stages, one workgroup per CU) for a single 128-row panel
+// with a long reduction (the expert dX over d_ff, the router's dW over the
+// tokens: streaming-bound, measured 14-16% faster); else K steps of 32 (4
+// stages, two workgroups per CU, which the many-tile dense products need)
 template <bool AKM, bool BKM, bool DG>
 static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t s) {
   const int tiles = a.G * (int)(a.M / 128) * (a.N / 128);
   if (tiles <= 0) return hipGetLastError();
-  MOE_LAUNCH(intern_name(role, "dma128x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4>), dim3(tiles),
-             dim3(256), 0, s, a);
+  if (a.M <= 128 && a.K >= 4096 && a.K % 64 == 0)
+    MOE_LAUNCH(intern_name(role, "dma128x128k64"), (gemm_dmag_kernel<AKM, BKM, DG, 3, 64>),
+               dim3(tiles), dim3(256), 0, s, a);
+  else
+    MOE_LAUNCH(intern_name(role, "dma128x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32>),
+               dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -796,8 +807,8 @@ static bool dmag_ok(const GenArgs &a, bool akm, bool bkm) {
   if (bkm && (a.b_kmax < a.K || a.b_k % 8)) return false;
   if (!akm && (a.a_m % 8 || a.a_m * 2 * 128 >= (int64_t(1) << 31))) return false;
   if (!bkm && (a.b_n % 8 || a.b_n * 2 * 128 >= (int64_t(1) << 31))) return false;
-  if (akm && a.a_k * 2 * 32 >= (int64_t(1) << 31)) return false;
-  if (bkm && a.b_k * 2 * 32 >= (int64_t(1) << 31)) return false;
+  if (akm && a.a_k * 2 * 64 >= (int64_t(1) << 31)) return false;  // k < 64 rows per step
+  if (bkm && a.b_k * 2 * 64 >= (int64_t(1) << 31)) return false;
   return true;
 }
 
