@@ -217,19 +217,23 @@ __device__ __forceinline__ bf16x8 frag_kmajor(uint32_t tile, int row0, int kbase
   return out;
 }
 
-template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32>
+// BM = 128 (waves 2 x 2 of 64 x 64) or 64 (waves 1 x 4 of 64 x 32; the A
+// operand K-contiguous), for groups of at most 64 rows (a capacity of 64).
+template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32, int BM = 128>
 __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   static_assert(BK == 32 || BK == 64, "K step");
-  constexpr int BM = 128, BN = 128, TILE = 128 * BK * 2;  // bytes per operand tile
-  constexpr int STAGE = 2 * TILE;
-  constexpr int CH = TILE / 1024 / 4;      // 1-KB DMA chunks per wave per operand
+  static_assert(BM == 128 || (BM == 64 && !AKM), "tile rows");
+  constexpr int BN = 128, TILEA = BM * BK * 2, TILE = 128 * BK * 2;  // bytes per operand tile
+  constexpr int STAGE = TILEA + TILE;
+  constexpr int CHA = TILEA / 1024 / 4, CH = TILE / 1024 / 4;  // 1-KB DMA chunks per wave
+  constexpr int WM = BM / 64, WN = 4 / WM, WTN = BN / WN, TN = WTN / 32;
   constexpr int ROWB = BK * 2, CPR = ROWB / 16, RPC = 1024 / ROWB;  // K-contiguous rows
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / 2, wn = wave % 2;
-  const int tiles_m = (int)(a.M / BM), tiles_n = a.N / BN;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = a.N / BN;
   const int tile = blockIdx.x;
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
@@ -245,13 +249,13 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
   // per-tile operand bases (bytes) and this lane's offsets for its chunks:
-  // every wave moves CH chunks (1 KB each) of A and CH of B per stage
+  // every wave moves CHA chunks (1 KB each) of A and CH of B per stage
   const char *abase, *bbase;
   int64_t astep, bstep;  // bytes per K step
-  uint32_t voa[CH], vob[CH];
+  uint32_t voa[CHA], vob[CH];
 #pragma unroll
-  for (int i = 0; i < CH; i++) {
-    const int q = CH * wave + i;
+  for (int i = 0; i < CHA; i++) {
+    const int q = CHA * wave + i;
     if constexpr (!AKM) {  // rows of ROWB bytes: RPC rows per chunk
       const int R = RPC * q + lane / CPR, slot = lane % CPR;
       int64_t m = m0 + R;
@@ -261,6 +265,10 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
       const int k = 4 * q + lane / 16, slot = lane % 16;
       voa[i] = (uint32_t)(k * a.a_k * 2 + ((slot ^ swz_km(k)) << 4));
     }
+  }
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int q = CH * wave + i;
     if constexpr (!BKM) {
       const int R = RPC * q + lane / CPR, slot = lane % CPR;
       vob[i] = (uint32_t)(R * a.b_n * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
@@ -286,20 +294,20 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   auto issue = [&](int st, int kt) __attribute__((always_inline)) {
     const char *ga = abase + (int64_t)kt * astep, *gb = bbase + (int64_t)kt * bstep;
 #pragma unroll
-    for (int i = 0; i < CH; i++)
+    for (int i = 0; i < CHA; i++)
       dma16<false>(ga, voa[i],
-                   __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (CH * wave + i) * 1024));
+                   __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (CHA * wave + i) * 1024));
 #pragma unroll
     for (int i = 0; i < CH; i++)
-      dma16<false>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILE +
+      dma16<false>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILEA +
                                                               (CH * wave + i) * 1024));
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][TN];
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
     if (p < ksteps) issue(p, p);
   for (int kt = 0; kt < ksteps; kt++) {
     if (kt + NS - 2 < ksteps)
-      wait_vmcnt<(NS - 2) * 2 * CH>();
+      wait_vmcnt<(NS - 2) * (CHA + CH)>();
     else
       wait_vmcnt<0>();
     __syncthreads();
@@ -320,15 +328,15 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
         const int k = kleft + idx / 16, c = idx % 16;
         const u32x4 z = {0u, 0u, 0u, 0u};
         if (AKM) *(u32x4 *)(smem + st * STAGE + k * 256 + c * 16) = z;
-        if (BKM) *(u32x4 *)(smem + st * STAGE + TILE + k * 256 + c * 16) = z;
+        if (BKM) *(u32x4 *)(smem + st * STAGE + TILEA + k * 256 + c * 16) = z;
       }
       __syncthreads();
     }
     if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
-    const uint32_t ta = lds0 + st * STAGE, tb = ta + TILE;
+    const uint32_t ta = lds0 + st * STAGE, tb = ta + TILEA;
 #pragma unroll
     for (int s = 0; s < BK / 16; s++) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[2], bfr[TN];
 #pragma unroll
       for (int i = 0; i < 2; i++) {
         const int row0 = wm * 64 + i * 32;
@@ -340,20 +348,20 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int row0 = wn * 64 + j * 32;
+      for (int j = 0; j < TN; j++) {
+        const int row0 = wn * WTN + j * 32;
         if constexpr (BKM) {
           bfr[j] = frag_kmajor(tb, row0, 16 * s, lane);
         } else {
           const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
-          bfr[j] =
-              *(const bf16x8 *)(smem + st * STAGE + TILE + R * ROWB + ((c ^ swz_slot<BK>(R)) << 4));
+          bfr[j] = *(const bf16x8 *)(smem + st * STAGE + TILEA + R * ROWB +
+                                     ((c ^ swz_slot<BK>(R)) << 4));
         }
       }
 #pragma unroll
       for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TN; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
@@ -366,17 +374,17 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   constexpr int CROW = 132;
   static_assert(64 * CROW * 4 <= NS * STAGE, "band fits the stages");
   float *cs = (float *)smem;
-  for (int band = 0; band < 2; band++) {
+  for (int band = 0; band < WM; band++) {
     __syncthreads();  // stages (or the previous band) no longer read
     if (wm == band) {
 #pragma unroll
       for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TN; j++)
 #pragma unroll
           for (int r = 0; r < 16; r++) {
             const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int Cc = wn * 64 + j * 32 + (lane & 31);
+            const int Cc = wn * WTN + j * 32 + (lane & 31);
             cs[R * CROW + Cc] = acc[i][j][r];
           }
     }
@@ -757,6 +765,15 @@ static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s
 // stages, two workgroups per CU, which the many-tile dense products need)
 template <bool AKM, bool BKM, bool DG>
 static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t s) {
+  if constexpr (!AKM) {  // groups of at most 64 rows: 64-row tiles
+    if (a.M <= 64) {
+      const int tiles = a.G * (a.N / 128);
+      if (tiles <= 0) return hipGetLastError();
+      MOE_LAUNCH(intern_name(role, "dma64x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32, 64>),
+                 dim3(tiles), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int tiles = a.G * (int)(a.M / 128) * (a.N / 128);
   if (tiles <= 0) return hipGetLastError();
   if (a.M <= 128 && a.K >= 4096 && a.K % 64 == 0)
@@ -800,8 +817,10 @@ static bool dwk_ok(const GenArgs &a, bool akm, bool bkm, bool dgelu) {
 // the DMA kernel needs 128-multiples for M and N, K a multiple of 32, a
 // whole K for K-contiguous operands, K-major extents that cover the rounded-up
 // K, 16-byte aligned rows, and per-lane offsets below 2^32
+// (M a multiple of 128, or at most 64 with a K-contiguous A: one 64-row tile)
 static bool dmag_ok(const GenArgs &a, bool akm, bool bkm) {
-  if (a.M % 128 || a.N % 128 || a.K % 32 || a.K <= 0) return false;
+  const bool m64 = !akm && a.M > 0 && a.M <= 64;
+  if ((a.M % 128 && !m64) || a.N % 128 || a.K % 32 || a.K <= 0) return false;
   if ((!akm || !bkm) && a.krows) return false;
   if (akm && (a.a_kmax < a.K || a.a_k % 8)) return false;
   if (bkm && (a.b_kmax < a.K || a.b_k % 8)) return false;
