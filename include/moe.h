@@ -240,7 +240,10 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *expert_ids
 /* Every expert's two-layer GELU FFN over its kept rows (survey notes sec.
  * 1.1.2.1; weight-only int8 dequantisation, survey notes sec. 1.2.3.1).
  * x_disp [E, C, d], kept [E] (device), w1/w2 (+ fp16 scales for int8).
- * Out: y_disp [E, C, d]; rows s >= kept[e] are not written. */
+ * Out: y_disp [E, C, d]; rows s >= kept[e] are not written.
+ * Workspace: the hidden rows and, for int8 experts with C > 128 and
+ * 32 <= E <= 256, a schedule of the experts over the XCDs computed on the
+ * device from kept (16 E + 16 int32) that balances skewed expert loads. */
 int moe_expert_ffn(const moe_config *cfg, const void *x_disp,
                    const int32_t *kept, const void *w1, const void *w1_scale,
                    const void *w2, const void *w2_scale, void *y_disp, void *ws,

@@ -83,7 +83,7 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 // ---- workspace layout
 struct Layout {
   size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
-      total;
+      xsched, total;
   // router variants
   size_t scores, cosl, embn, imp, loadp;
   // backward
@@ -91,6 +91,14 @@ struct Layout {
 };
 
 int64_t padded_experts(const moe_config *c) { return (c->E + 7) / 8 * 8; }
+
+// int8 expert GEMMs on 256-row tiles with enough experts to balance: their
+// tiles follow a per-call XCD schedule (16 E + 16 int32 of workspace)
+bool sched_experts(const moe_config *c) {
+  return c->expert_wfmt == MOE_W_INT8_G128 && c->act_dtype == MOE_BF16 && capacity_of(c) > 128 &&
+         c->E >= 32 && c->E <= 256;
+}
+size_t sched_bytes(const moe_config *c) { return (size_t)(16 * c->E + 16) * 4; }
 
 static_assert(MOE_ROUTER_TOPK == moe::RV_TOPK && MOE_ROUTER_TOP_P == moe::RV_TOP_P &&
                   MOE_ROUTER_COSINE == moe::RV_COSINE && MOE_ROUTER_NOISY_TOPK == moe::RV_NOISY,
@@ -149,6 +157,7 @@ Layout layout(const moe_config *c, int entry) {
       break;
     case MOE_ENTRY_EXPERT_FFN:
       L.hidden = take((size_t)c->E * C * c->d_ff * as);
+      if (sched_experts(c)) L.xsched = take(sched_bytes(c));
       break;
     case MOE_ENTRY_COMBINE:
       break;
@@ -168,6 +177,7 @@ Layout layout(const moe_config *c, int entry) {
         L.hidden_dense = take((size_t)c->T * c->d_ff_dense * as);
         L.dense = take((size_t)c->T * c->d * as);
       }
+      if (sched_experts(c)) L.xsched = take(sched_bytes(c));
       break;
     }
     case MOE_ENTRY_BACKWARD: {
@@ -340,17 +350,27 @@ hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *id
                                  c->d * (int64_t)act_size(c), x_disp, s);
 }
 
-// hidden: GELU(W1 x) of the kept rows; zpre: W1 x itself, or null (not kept)
+// hidden: GELU(W1 x) of the kept rows; zpre: W1 x itself, or null (not kept);
+// xsched: workspace for the XCD schedule of the int8 tiles (sched_experts),
+// or null
 hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t *kept,
                          const void *w1, const void *s1, const void *w2, const void *s2,
-                         void *y_disp, void *hidden, hipStream_t s, void *zpre = nullptr) {
+                         void *y_disp, void *hidden, hipStream_t s, void *zpre = nullptr,
+                         int32_t *xsched = nullptr) {
   const int64_t C = capacity_of(c);
   if (C == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
-  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre};
-  hipError_t e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
+  hipError_t e = hipSuccess;
+  if (xsched && sched_experts(c)) {
+    e = moe_host::launch_tile_sched(kept, (int)c->E, C, xsched, s);
+    if (e != hipSuccess) return e;
+  } else {
+    xsched = nullptr;
+  }
+  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre, xsched};
+  e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
   if (e != hipSuccess) return e;
-  GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E};
+  GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E, nullptr, xsched};
   return moe_host::launch_gemm(g2, bf, q8, 0, "expert_ffn2", s);
 }
 
@@ -518,8 +538,9 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_disp, const int32_t *kep
   rc = check_ws(cfg, MOE_ENTRY_EXPERT_FFN, ws, ws_bytes);
   if (rc != MOE_OK) return rc;
   const Layout L = layout(cfg, MOE_ENTRY_EXPERT_FFN);
+  int32_t *xs = sched_experts(cfg) ? (int32_t *)at(ws, L.xsched) : nullptr;
   return hip_status(do_expert_ffn(cfg, x_disp, kept, w1, w1_scale, w2, w2_scale, y_disp,
-                                  at(ws, L.hidden), (hipStream_t)stream));
+                                  at(ws, L.hidden), (hipStream_t)stream, nullptr, xs));
 }
 
 int moe_dense_mlp(const moe_config *cfg, const void *x, const void *wm1, const void *wm2,
@@ -650,7 +671,8 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
                         out->slots, out->drop_mask, term, out->aux_loss, x_disp, s);
   if (e == hipSuccess)
     e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
-                      hidden, s, out->z_disp);
+                      hidden, s, out->z_disp,
+                      sched_experts(cfg) ? (int32_t *)at(ws, L.xsched) : nullptr);
   // join: the combine reads D(x)
   if (e == hipSuccess && side) e = hipStreamWaitEvent(s, side->join, 0);
   if (e == hipSuccess)

@@ -438,7 +438,7 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, f
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int GELU>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
+__device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn) {
   constexpr int BK = 64;
   constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -460,15 +460,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int tiles_n = a.N / BN;
-  const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
-  const int total = a.G * tiles_m * tiles_n;
-  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
-                                  : xcd_remap(blockIdx.x, total);
-  const int g = tile / (tiles_m * tiles_n);
-  const int rem = tile - g * tiles_m * tiles_n;
-  int tm, tn;
-  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t rows = a.M_cap;
   if (a.rows) {
     const int64_t r = a.rows[g];
@@ -629,6 +620,113 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   bands(std::false_type{});
 }
 
+// One tile per workgroup, tiles laid over the XCDs as in gemm_dma_kernel.
+template <int BM, int BN, int WM, int WN, int NS, int GELU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
+  const int tiles_n = a.N / BN;
+  const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
+  const int total = a.G * tiles_m * tiles_n;
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
+                                  : xcd_remap(blockIdx.x, total);
+  const int g = tile / (tiles_m * tiles_n);
+  const int rem = tile - g * tiles_m * tiles_n;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
+  i8_tile<BM, BN, WM, WN, NS, GELU>(a, g, tm, tn);
+}
+
+// Groups placed on the XCDs by a schedule (tile_sched_kernel): the
+// workgroups of XCD x (blockIdx % 8 == x) walk that XCD's queue -- its
+// groups in schedule order, each group's valid row tiles column by column --
+// so every group still runs on one XCD (operands shared in its L2) while
+// skewed row counts are spread evenly over the XCDs.
+template <int BM, int BN, int WM, int WN, int NS, int GELU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_sched_kernel(GemmArgs a) {
+  const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
+  const int tiles_n = a.N / BN;
+  const int32_t *xs = a.xsched;
+  const int nx = xs[x];
+  const int32_t *lst = xs + 8 + x * a.G;
+  const int32_t *pre = xs + 8 + 8 * a.G + x * (a.G + 1);
+  const int ntiles = pre[nx] * tiles_n;
+  for (int i = blockIdx.x >> 3; i < ntiles; i += nbx) {
+    // the last group of the queue whose tiles start at or before i
+    int lo = 0, hi = nx - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] * tiles_n <= i) lo = mid; else hi = mid - 1;
+    }
+    const int v = pre[lo + 1] - pre[lo], j = i - pre[lo] * tiles_n;
+    const int tn = j / v, tm = j - tn * v;
+    i8_tile<BM, BN, WM, WN, NS, GELU>(a, lst[lo], tm, tn);
+    __syncthreads();  // the next tile's DMA reuses the LDS of this epilogue
+  }
+}
+
+// Schedule of the 256-row int8 tiles over the 8 XCDs: each group's cost is
+// its row tiles in 32-row fragments (at least 4 per tile: a tile with few
+// rows still streams its weight slab), groups are taken largest first and
+// each goes to the XCD with the least cost so far.  Output (int32):
+// [0, 8) groups per XCD; [8 + x * G, ...) XCD x's groups in order;
+// [8 + 8 * G + x * (G + 1), ...) prefix sums of their row tiles.  One
+// workgroup of 256 threads, G <= 256.
+__global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, int G, int64_t M_cap,
+                                                         int32_t *xs) {
+  constexpr int BM = 256, FLOOR = 4;
+  __shared__ int cost[256], vm[256], order[256], scost[256], svm[256];
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    const int64_t r = rows[tid] < M_cap ? rows[tid] : M_cap;
+    const int v = r > 0 ? (int)((r + BM - 1) / BM) : 0;
+    int c = 0;
+    for (int t = 0; t < v; t++) {
+      const int64_t rt = r - (int64_t)t * BM < BM ? r - (int64_t)t * BM : BM;
+      const int f = (int)((rt + 31) / 32);
+      c += f > FLOOR ? f : FLOOR;
+    }
+    vm[tid] = v;
+    cost[tid] = c;
+  }
+  __syncthreads();
+  if (tid < G) {  // rank by cost, ties to the lower group
+    int rk = 0;
+    for (int h = 0; h < G; h++) rk += cost[h] > cost[tid] || (cost[h] == cost[tid] && h < tid);
+    order[rk] = tid;
+    scost[rk] = cost[tid];
+    svm[rk] = vm[tid];
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // lane x < 8 keeps XCD x's cost, group count and row tiles; each group
+    // goes to the lane with the least cost (ties: lower XCD)
+    // (lanes 8..63 shuffle among themselves and never write)
+    const int x = tid;
+    int load = x < 8 ? 0 : 0x7fffffff, cnt = 0, tiles = 0;
+    int32_t *lst = xs + 8 + x * G, *pre = xs + 8 + 8 * G + x * (G + 1);
+    for (int i = 0; i < G; i++) {
+      const int v = svm[i];
+      if (v == 0) break;  // the rest are empty too (cost 0 ranks last)
+      int bl = load, bx = x;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const int ol = __shfl_xor(bl, o), ox = __shfl_xor(bx, o);
+        if (ol < bl || (ol == bl && ox < bx)) { bl = ol; bx = ox; }
+      }
+      if (x < 8 && x == bx) {
+        lst[cnt] = order[i];
+        pre[cnt] = tiles;
+        cnt++;
+        tiles += v;
+        load += scost[i];
+      }
+    }
+    if (x < 8) {
+      xs[x] = cnt;
+      pre[cnt] = tiles;
+    }
+  }
+}
+
 // fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
 // any shape (bounds-checked); the correctness path for fp32 layers.
 template <int GELU>
@@ -747,14 +845,35 @@ static hipError_t launch_dma_i8(const GemmArgs &a, int gelu, hipStream_t s, cons
   const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
-  const char *name = intern_name(role, tile);
   const int epi = epi_of(a, gelu);
+  if constexpr (BM == 256) {  // the schedule counts 256-row tiles
+    if (a.xsched) {
+      const dim3 sgrid((tiles + 7) / 8 * 8);
+      const char *name = intern_name(role, "dma256x256_i8_sched");
+      if (epi == 2)
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 2>), sgrid, block, 0, s, a);
+      else if (epi == 1)
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 1>), sgrid, block, 0, s, a);
+      else
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 0>), sgrid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  const char *name = intern_name(role, tile);
   if (epi == 2)
     MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, s, a);
   else if (epi == 1)
     MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, s, a);
   else
     MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int32_t *xs,
+                             hipStream_t s) {
+  if (G < 1 || G > 256) return hipErrorInvalidValue;
+  MOE_LAUNCH(intern_name("expert_tile_sched", "lpt"), tile_sched_kernel, dim3(1), dim3(256), 0, s,
+             rows, G, M_cap, xs);
   return hipGetLastError();
 }
 

@@ -55,6 +55,9 @@ struct GemmArgs {
   int64_t M_cap;
   int N, K, G;
   void *Zpre;  // GELU epilogue only: also store the pre-activation here (as C), or null
+  // int8 groups with more than 128 rows: the XCD schedule written by
+  // launch_tile_sched for these rows (16 G + 16 int32), or null
+  const int32_t *xsched;
 };
 
 // general grouped GEMM of the backward (backward.hip)
@@ -128,6 +131,9 @@ hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots
 // in the per-kernel timing ("expert_ffn1", "expert_ffn2", "dense_mlp1", ...)
 hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gelu,
                        const char *role, hipStream_t s);
+// XCD schedule of G groups' 256-row int8 tiles from their row counts (G <= 256)
+hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int32_t *xs,
+                             hipStream_t s);
 
 // a stable C string for a profiling name built at run time
 const char *intern_name(const char *a, const char *b);

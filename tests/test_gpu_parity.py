@@ -252,6 +252,45 @@ def test_expert_ffn_alone(C, d, F, wfmt):
     assert np.all(np.isnan(ydn[3, kept[3]:]))
 
 
+def test_int8_expert_schedule_matches_unscheduled_tiles():
+    # 40 int8 experts with C > 128 run on the XCD schedule (skewed loads,
+    # empty and single-row experts, one and two 256-row tiles); the same
+    # experts eight at a time take the unscheduled tile order.  Same tiles,
+    # same arithmetic: bit-identical rows.  Sampled rows against the oracle.
+    E, C, d, F = 40, 300, 1024, 1024
+    wl = W("s", T=C, d=d, E=E, k=1, d_ff=F, capacity_factor=float(E), wfmt="int8")
+    cfg = binding.config_of(wl)
+    assert binding.capacity(cfg) == C
+    inp = synth.make_inputs(wl, seed=5)
+    kept = np.array([C, C, 0, 1, 256, 257, 255, 3] + [int(C * 0.8 ** i) for i in range(32)],
+                    np.int32)
+    xd = synth.normal((E, C, d), 1.0, 9, "xd", "cpu", torch.bfloat16)
+    w1, s1, w2, s2 = (inp[n].to(DEV) for n in ("w1", "w1_scale", "w2", "w2_scale"))
+    ys = torch.full((E, C, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    binding.moe_expert_ffn(cfg, xd.to(DEV), torch.from_numpy(kept).to(DEV), w1, s1, w2, s2, ys,
+                           binding.alloc_workspace(cfg, binding.ENTRY_EXPERT_FFN))
+    w8 = W("s8", T=C, d=d, E=8, k=1, d_ff=F, capacity_factor=8.0, wfmt="int8")
+    cfg8 = binding.config_of(w8)
+    ws8 = binding.alloc_workspace(cfg8, binding.ENTRY_EXPERT_FFN)
+    yu = torch.full((E, C, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for e0 in range(0, E, 8):
+        sl = slice(e0, e0 + 8)
+        binding.moe_expert_ffn(cfg8, xd[sl].to(DEV), torch.from_numpy(kept[sl].copy()).to(DEV),
+                               w1[sl], s1[sl], w2[sl], s2[sl], yu[sl], ws8)
+    torch.cuda.synchronize()
+    for e in range(E):
+        n = int(kept[e])
+        assert torch.equal(ys[e, :n], yu[e, :n]), f"expert {e}"
+        assert torch.isnan(ys[e, n:].float()).all(), f"expert {e}: rows past kept written"
+    rng = np.random.default_rng(3)
+    for e in (0, 3, 5, 12):
+        n = int(kept[e])
+        rows = sorted({0, n - 1, *rng.integers(0, n, size=3).tolist()})
+        ref = oracle.ffn_rows(xd[e, rows], inp["w1"][e], inp["w2"][e], inp["w1_scale"][e],
+                              inp["w2_scale"][e])
+        check_close(f"y_disp[{e}]", ys[e, rows], ref, TAU["bf16"])
+
+
 @pytest.mark.parametrize("T,d,Fd", [(300, 256, 512), (1000, 256, 512), (17, 64, 128)])
 def test_dense_mlp_alone(T, d, Fd):
     wl = W("dm", T=T, d=d, E=2, k=1, d_ff=64, capacity_factor=1.0, d_ff_dense=Fd, pr_moe=True)
