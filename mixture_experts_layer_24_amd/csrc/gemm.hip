@@ -909,7 +909,10 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
   }
   if (a.N % 128 == 0) {
     if (a.M_cap <= 32) return launch_dma<32, 128, 1, 4, 64, 4>(a, nt, gelu, s, role, "dma32x128");
-    if (a.M_cap <= 64) return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");
+    if (a.M_cap <= 64) {  // 64x256: two workgroups per CU, 64 KB of weights in flight
+      if (a.N % 256 == 0) return launch_dma<64, 256, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x256");
+      return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");
+    }
     if (a.M_cap <= 128 && a.N % 256 == 0)
       return launch_dma<128, 256, 2, 4, 64, 3>(a, nt, gelu, s, role, "dma128x256");
     if (a.M_cap > 128 && a.N % 256 == 0)
