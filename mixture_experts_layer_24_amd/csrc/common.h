@@ -23,31 +23,69 @@ constexpr int kWave = 64;
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Cross-lane reductions on VALU data movement instead of the LDS crossbar
+// (ds_bpermute): DPP within each 16-lane row -- quad permutes [1,0,3,2] and
+// [2,3,0,1], then the half-row mirror (lane i <-> 7 - i) and the row mirror
+// (i <-> 15 - i), each pairing two groups that already hold their own
+// totals -- then the four row totals read from lanes 0, 16, 32, 48 and
+// combined in a fixed order.  Every lane returns the same value; the caller
+// must run the whole wave (no divergent lanes).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-  // butterfly: every lane ends with the same value, summed in a fixed order
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  // each step adds a lane and its partner, so a row's lanes agree bit for
+  // bit; the rows are summed as (r0 + r1) + (r2 + r3)
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 // (value, index) arg-max over the wave: larger value wins, equal values go
-// to the smaller index.  Every lane returns the winner.
-__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float ov = __shfl_xor(v, m, kWave);
-    int oi = __shfl_xor(idx, m, kWave);
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-    }
+// to the smaller index (a total order, so the reduction order does not
+// matter).  Every lane returns the winner.
+__device__ __forceinline__ void argmax_step(float &v, int &idx, float ov, int oi) {
+  if (ov > v || (ov == v && oi < idx)) {
+    v = ov;
+    idx = oi;
   }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &idx) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(idx);
+  argmax_step(v, idx, ov, oi);
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+  argmax_dpp<0xB1>(v, idx);
+  argmax_dpp<0x4E>(v, idx);
+  argmax_dpp<0x141>(v, idx);
+  argmax_dpp<0x140>(v, idx);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(idx, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) argmax_step(bv, bi, lane_f(v, r), __builtin_amdgcn_readlane(idx, r));
+  v = bv;
+  idx = bi;
 }
 
 // ------------------------------------------------------------- conversions

@@ -18,6 +18,7 @@
 // row's E logits sit 1-4 per lane and wave shuffles give the row max, the
 // softmax sum and the arg-max rounds of the top-k.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace moe {
@@ -25,18 +26,20 @@ namespace moe {
 constexpr int RBM = 64;  // tokens per block
 
 
-// L: LDS logits tile [RBM][ldl] fp32 (bias not yet added).
-template <int MAXK>
+// L: LDS logits tile [RBM][ldl] fp32 (bias not yet added).  SL = expert
+// slots per lane (E <= 64 SL): lane l holds experts l, l + 64, ...
+template <int MAXK, int SL>
 __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
                                 float (*qpart)[256], int *fcnt, int *hcnt, int blk) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int E = a.E, k = a.k;
   __shared__ float zw[4];
-  float q[4] = {0.f, 0.f, 0.f, 0.f};
+  float q[SL];
   float zacc = 0.f;
-  float bias[4];
+  float bias[SL];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < SL; i++) {
+    q[i] = 0.f;
     const int e = lane + kWave * i;
     bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
   }
@@ -44,20 +47,22 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
     const int r = wave * (RBM / 4) + rr;
     const int64_t t = (int64_t)blk * RBM + r;
     if (t >= a.T) break;
-    float v[4];
-    bool live[4];
+    float v[SL];
+    bool live[SL];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < SL; i++) {
       const int e = lane + kWave * i;
       live[i] = e < E;
       v[i] = live[i] ? L[r * ldl + e] + bias[i] : neg_inf();
       if (a.logits && live[i]) a.logits[t * E + e] = v[i];
     }
-    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    m = wave_max(m);
-    float p[4], s = 0.f;
+    float m = v[0];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 1; i < SL; i++) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    float p[SL], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < SL; i++) {
       p[i] = live[i] ? expf(v[i] - m) : 0.f;
       s += p[i];
     }
@@ -67,12 +72,16 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
       zacc += lz * lz;
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < SL; i++) {
       p[i] = p[i] / s;
       q[i] += p[i];
     }
-    // top-k by repeated wave arg-max (larger logit, then lower index)
-    bool taken[4] = {false, false, false, false};
+    // top-k: round j takes the largest logit not yet taken (the softmax max m
+    // in round 0) and the lowest expert holding it, from one ballot per slot
+    // (slot i holds experts 64 i .. 64 i + 63, so the first hit is the lowest)
+    bool taken[SL];
+#pragma unroll
+    for (int i = 0; i < SL; i++) taken[i] = false;
     int sel[MAXK];
     float selp[MAXK];
 #pragma unroll
@@ -80,26 +89,36 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
       sel[j] = 0;
       selp[j] = 0.f;
       if (j < k) {
-        float bv = neg_inf();
-        int be = 0x7fffffff;
+        float mj = m;
+        if (j > 0) {
+          float c = neg_inf();
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int e = lane + kWave * i;
-          if (live[i] && !taken[i] && (be == 0x7fffffff || v[i] > bv)) {
-            bv = v[i];
-            be = e;
+          for (int i = 0; i < SL; i++)
+            if (live[i] && !taken[i]) c = fmaxf(c, v[i]);
+          mj = wave_max(c);
+        }
+        int be = -1;
+#pragma unroll
+        for (int i = 0; i < SL; i++) {
+          const unsigned long long b = __ballot(live[i] && !taken[i] && v[i] == mj);
+          if (be < 0 && b) be = kWave * i + __builtin_ctzll(b);
+        }
+        if (be < 0) {  // only NaN logits left: the lowest expert not taken
+#pragma unroll
+          for (int i = 0; i < SL; i++) {
+            const unsigned long long b = __ballot(live[i] && !taken[i]);
+            if (be < 0 && b) be = kWave * i + __builtin_ctzll(b);
           }
         }
-        wave_argmax(bv, be);
         const int owner_i = be / kWave;
         float pi = p[0];
-        if (owner_i == 1) pi = p[1];
-        if (owner_i == 2) pi = p[2];
-        if (owner_i == 3) pi = p[3];
-        selp[j] = __shfl(pi, be % kWave, kWave);
+#pragma unroll
+        for (int i = 1; i < SL; i++)
+          if (owner_i == i) pi = p[i];
+        selp[j] = lane_f(pi, be % kWave);  // be is wave-uniform
         sel[j] = be;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < SL; i++)
           if (lane + kWave * i == be) taken[i] = true;
       }
     }
@@ -125,7 +144,7 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < SL; i++) {
     const int e = lane + kWave * i;
     if (e < E) qpart[wave][e] = q[i];
   }
@@ -262,9 +281,135 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     return;
   }
   if (a.k <= 2)
-    router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<2, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
-    router_epilogue<8>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<8, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
+}
+
+// The same contraction with the operand tiles moved global -> LDS by DMA in
+// 64-wide K steps, NS - 1 steps ahead (the router's blocks each read the
+// whole weight matrix, so the stream of K steps must keep several steps in
+// flight; the register-staged kernel above keeps one).  Tile rows are 128
+// bytes with the 16-byte chunks XOR-swizzled as in the GEMMs.  The K order
+// of the MFMAs is that of router_bf16_kernel: identical logits.  One weight
+// matrix (SCORES with two matrices uses router_bf16_kernel).
+template <int NTW, int NS, bool SCORES = false>
+__global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
+  constexpr int EPMAX = 64 * NTW;
+  constexpr int ROWB = 128;                         // bytes per tile row (64 bf16)
+  constexpr int STAGE = (RBM + EPMAX) * ROWB;
+  constexpr int A_PW = RBM * ROWB / 1024 / 4;       // 1 KB chunks per wave per stage
+  constexpr int W_PW = EPMAX * ROWB / 1024 / 4;
+  constexpr int CPW = A_PW + W_PW;
+  constexpr int LOGIT_BYTES = RBM * (EPMAX + 4) * 4;
+  constexpr int SMEM = NS * STAGE > LOGIT_BYTES ? NS * STAGE : LOGIT_BYTES;
+  static_assert(NS >= 2 && (NS - 2) * CPW < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ float qpart[4][256];
+  __shared__ int fcnt[256], hcnt[256];
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int blk = blockIdx.x;
+  const int E = a.E, Ep = (E + 31) & ~31, d = a.d;
+  fcnt[tid] = 0;
+  hcnt[tid] = 0;
+  const int64_t t0 = (int64_t)blk * RBM;
+  const char *Xb = (const char *)a.x + t0 * d * 2;
+  const char *Wb = (const char *)a.w;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  // chunk = 8 rows of 128 bytes; lane -> row lane / 8, slot lane % 8
+  const int lr = lane / 8, slot = lane % 8;
+  uint32_t voffa[A_PW], voffw[W_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; i++) {
+    const int R = 8 * (wave * A_PW + i) + lr;
+    int64_t r = R;
+    if (t0 + r >= a.T) r = a.T - 1 - t0;  // clamp to the last token
+    voffa[i] = (uint32_t)(r * d * 2 + ((slot ^ swz_slot<64>(R)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < W_PW; i++) {
+    const int R = 8 * (wave * W_PW + i) + lr;
+    const int e = R < E ? R : E - 1;      // clamp to the last expert
+    voffw[i] = (uint32_t)((int64_t)e * d * 2 + ((slot ^ swz_slot<64>(R)) << 4));
+  }
+  const uint32_t dsta = lds0 + wave * A_PW * 1024;
+  const uint32_t dstw = lds0 + RBM * ROWB + wave * W_PW * 1024;
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+    const char *ga = Xb + (int64_t)kt * ROWB;
+    const char *gw = Wb + (int64_t)kt * ROWB;
+#pragma unroll
+    for (int i = 0; i < A_PW; i++)
+      dma16<false>(ga, voffa[i], __builtin_amdgcn_readfirstlane(dsta + st * STAGE + i * 1024));
+#pragma unroll
+    for (int i = 0; i < W_PW; i++)
+      dma16<false>(gw, voffw[i], __builtin_amdgcn_readfirstlane(dstw + st * STAGE + i * 1024));
+  };
+
+  f32x16 acc[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; i++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
+
+  const int mt = wave & 1;  // 32-row half of the token tile
+  const int ksteps = d / 64;
+#pragma unroll
+  for (int p = 0; p < NS - 1; p++)
+    if (p < ksteps) issue(p, p);
+  for (int kt = 0; kt < ksteps; kt++) {
+    if (kt + NS - 2 < ksteps)
+      wait_vmcnt<(NS - 2) * CPW>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // every wave's chunks of step kt; stage (kt - 1) % NS free
+    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
+    const char *sa = smem + (kt % NS) * STAGE;
+    const char *sw = sa + RBM * ROWB;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const int c = 2 * s + (lane >> 5);
+      const int Ra = mt * 32 + (lane & 31);
+      const bf16x8 av = *(const bf16x8 *)(sa + Ra * ROWB + ((c ^ swz_slot<64>(Ra)) << 4));
+#pragma unroll
+      for (int i = 0; i < NTW; i++) {
+        const int nt = (wave >> 1) + 2 * i;
+        if (nt * 32 < Ep) {
+          const int Rw = nt * 32 + (lane & 31);
+          const bf16x8 bv = *(const bf16x8 *)(sw + Rw * ROWB + ((c ^ swz_slot<64>(Rw)) << 4));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the stages are read; the logits tile reuses them
+  float *L = (float *)smem;
+  const int ldl = EPMAX + 4;
+#pragma unroll
+  for (int i = 0; i < NTW; i++) {
+    const int nt = (wave >> 1) + 2 * i;
+    if (nt * 32 < Ep) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        L[m * ldl + nt * 32 + (lane & 31)] = acc[i][r];
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (SCORES) {
+    for (int idx = tid; idx < RBM * E; idx += 256) {
+      const int r = idx / E, e = idx - (idx / E) * E;
+      const int64_t t = t0 + r;
+      if (t < a.T) a.logits[t * E + e] = L[r * ldl + e];
+    }
+    return;
+  }
+  if (a.k <= 2)
+    router_epilogue<2, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
+  else
+    router_epilogue<8, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
 }
 
 // fp32 activations: plain fp32 dot products (small shapes; correctness path)
@@ -298,9 +443,9 @@ __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
     return;
   }
   if (a.k <= 2)
-    router_epilogue<2>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<2, 4>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
-    router_epilogue<8>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<8, 4>(a, L, ldl, qpart, fcnt, hcnt, blk);
 }
 
 // Switch load-balance loss, final step (moe_route): see aux_sum_wave.
@@ -343,21 +488,14 @@ hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, h
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   const int nblk = router_blocks(a.T);
   if (nblk > 0) {
-    if (act_bf16) {
+    if (act_bf16) {  // the bf16 path guarantees d % 64 == 0
       const int ntw = ((a.E + 31) / 32 + 1) / 2;
-      const bool k128 = a.d % 128 == 0;  // the bf16 path guarantees d % 64 == 0
       const dim3 g(nblk), b(256);
       switch (ntw) {
-        case 1:
-          if (k128) MOE_LAUNCH("router_bf16_e64", (router_bf16_kernel<1, 128>), g, b, 0, s, a);
-          else MOE_LAUNCH("router_bf16_e64", (router_bf16_kernel<1, 64>), g, b, 0, s, a);
-          break;
-        case 2:
-          if (k128) MOE_LAUNCH("router_bf16_e128", (router_bf16_kernel<2, 128>), g, b, 0, s, a);
-          else MOE_LAUNCH("router_bf16_e128", (router_bf16_kernel<2, 64>), g, b, 0, s, a);
-          break;
-        case 3: MOE_LAUNCH("router_bf16_e192", (router_bf16_kernel<3, 64>), g, b, 0, s, a); break;
-        default: MOE_LAUNCH("router_bf16_e256", (router_bf16_kernel<4, 64>), g, b, 0, s, a); break;
+        case 1: MOE_LAUNCH("router_bf16_e64", (router_dma_kernel<1, 4>), g, b, 0, s, a); break;
+        case 2: MOE_LAUNCH("router_bf16_e128", (router_dma_kernel<2, 4>), g, b, 0, s, a); break;
+        case 3: MOE_LAUNCH("router_bf16_e192", (router_dma_kernel<3, 4>), g, b, 0, s, a); break;
+        default: MOE_LAUNCH("router_bf16_e256", (router_dma_kernel<4, 3>), g, b, 0, s, a); break;
       }
     } else {
       MOE_LAUNCH("router_f32", router_f32_kernel<false>, dim3(nblk), dim3(256), 0, s, a);
@@ -377,6 +515,15 @@ hipError_t launch_router_scores(const RouterArgs &a, int act_bf16, hipStream_t s
     return hipGetLastError();
   }
   const int ntw = ((a.E + 31) / 32 + 1) / 2;
+  if (!a.w2 || a.nw1 >= a.E) {  // one weight matrix: the DMA pipeline
+    switch (ntw) {
+      case 1: MOE_LAUNCH("router_scores_n64", (router_dma_kernel<1, 4, true>), g, b, 0, s, a); break;
+      case 2: MOE_LAUNCH("router_scores_n128", (router_dma_kernel<2, 4, true>), g, b, 0, s, a); break;
+      case 3: MOE_LAUNCH("router_scores_n192", (router_dma_kernel<3, 4, true>), g, b, 0, s, a); break;
+      default: MOE_LAUNCH("router_scores_n256", (router_dma_kernel<4, 3, true>), g, b, 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   const bool k128 = a.d % 128 == 0;
   switch (ntw) {
     case 1:

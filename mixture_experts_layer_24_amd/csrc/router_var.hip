@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
           if (oi == 1) pi = p[1];
           if (oi == 2) pi = p[2];
           if (oi == 3) pi = p[3];
-          pi = __shfl(pi, be % kWave, kWave);
+          pi = lane_f(pi, be % kWave);  // be is wave-uniform
           sel[j] = be;
           selp[j] = pi;
           thr_out = bv;  // the k-th largest once the loop ends (noisy: n == k)
