@@ -19,6 +19,17 @@
 
 namespace moe {
 
+// V elements of src into dst: one 16-byte load when they are 16 bytes
+template <typename T, int V>
+__device__ __forceinline__ void load_v(T (&dst)[V], const T *src) {
+  if constexpr (sizeof(T) * V == 16) {
+    *(u32x4 *)dst = *(const u32x4 *)src;
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; v++) dst[v] = src[v];
+  }
+}
+
 template <typename T, int V>  // V elements per lane per step
 __global__ __launch_bounds__(256) void combine_kernel(const T *y_disp, const int32_t *ids,
                                                       const int32_t *slots, const float *gates,
@@ -29,6 +40,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *y_disp, const int
   const int lane = lane_id();
   const int64_t nw = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave; t < n_tok; t += nw) {
+    // lane j < k loads the token's assignment j (one round trip for all k)
+    int sl = -1, el = -1;
+    float gl = 0.f;
+    if (lane < k) {
+      sl = slots[t * k + lane];
+      el = ids[t * k + lane];
+      gl = gates[t * k + lane];
+    }
     const T *row[MAXK];
     float g[MAXK];
 #pragma unroll
@@ -36,38 +55,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *y_disp, const int
       row[j] = nullptr;
       g[j] = 0.f;
       if (j < k) {
-        const int s = __builtin_amdgcn_readfirstlane(slots[t * k + j]);
-        const int e = __builtin_amdgcn_readfirstlane(ids[t * k + j]);
+        const int s = __builtin_amdgcn_readlane(sl, j);
+        const int e = __builtin_amdgcn_readlane(el, j);
         if (s >= 0 && s < C && e >= 0 && e < E) {
           row[j] = y_disp + ((int64_t)e * C + s) * d;
-          g[j] = gates[t * k + j];
+          g[j] = lane_f(gl, j);
         }
       }
     }
+    // every operand of a column chunk is loaded (16-byte vectors when V
+    // elements are 16 bytes) before any is used, so the k expert rows and
+    // the residual terms are in flight together
+#pragma unroll 2
     for (int c = lane * V; c < d; c += kWave * V) {
+      T in[MAXK][V], b1[V], b2[V];
+#pragma unroll
+      for (int j = 0; j < MAXK; j++)
+        if (row[j] != nullptr) load_v<T, V>(in[j], row[j] + c);
+      if (base) load_v<T, V>(b1, base + t * d + c);
+      if (base2) load_v<T, V>(b2, base2 + t * d + c);
       float acc[V];
 #pragma unroll
       for (int v = 0; v < V; v++) acc[v] = 0.f;
 #pragma unroll
-      for (int j = 0; j < MAXK; j++) {
+      for (int j = 0; j < MAXK; j++)
         if (row[j] != nullptr) {
-          T in[V];
-          if constexpr (sizeof(T) * V == 16) {
-            *(u32x4 *)in = *(const u32x4 *)(row[j] + c);
-          } else {
 #pragma unroll
-            for (int v = 0; v < V; v++) in[v] = row[j][c + v];
-          }
-#pragma unroll
-          for (int v = 0; v < V; v++) acc[v] = fmaf(g[j], ActTraits<T>::to_f(in[v]), acc[v]);
+          for (int v = 0; v < V; v++) acc[v] = fmaf(g[j], ActTraits<T>::to_f(in[j][v]), acc[v]);
         }
-      }
       T out[V];
 #pragma unroll
       for (int v = 0; v < V; v++) {
         float b = 0.f;
-        if (base) b = ActTraits<T>::to_f(base[t * d + c + v]);
-        if (base2) b += ActTraits<T>::to_f(base2[t * d + c + v]);
+        if (base) b = ActTraits<T>::to_f(b1[v]);
+        if (base2) b += ActTraits<T>::to_f(b2[v]);
         out[v] = ActTraits<T>::from_f(b + acc[v]);
       }
       if constexpr (sizeof(T) * V == 16) {
