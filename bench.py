@@ -17,12 +17,18 @@ with --workload.  One JSON line is printed:
 
   value      whole-job tokens/s over the K timed steps (host clock around
              device-synchronised steps)
-  roofline   the dominant kernel (most time per step): algorithmic bytes or
-             FLOPs per launch divided by its mean launch time, measured with
-             HIP events recorded on the launch stream around each kernel
-             during the timed steps; traffic = HBM bytes per launch from the
-             committed rocprofv3 counter summary when it was taken on the
-             current kernel source, else null
+  roofline   the dominant kernel (most time per step in a two-step survey
+             after the warmup, where every kernel is timed): algorithmic bytes
+             or FLOPs per launch divided by its mean launch time, measured
+             with HIP events recorded on the launch stream around that
+             kernel's launches during the timed steps (no other kernel carries
+             events there); traffic = HBM bytes per launch from the committed
+             rocprofv3 counter summary when it was taken on the current kernel
+             source, else null
+  kernels    per-kernel mean launch times from the survey steps
+  cold_cache steps timed one by one after a 512 MiB read that evicts the
+             Infinity Cache (the timed steps above run back to back, so inputs
+             smaller than the cache may be partly warm there)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
              (routing and dispatch on every token, expert FFN and dense MLP on a
              seeded token sample, extrapolated linearly in tokens)
@@ -83,6 +89,9 @@ def parse():
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
+    p.add_argument("--cold-steps", type=int, default=5,
+                   help="extra steps, each after a 512 MiB read that evicts the 256 MB "
+                        "Infinity Cache, timed one by one with HIP events (0 = skip)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     p.add_argument("--label")
     p.add_argument("--symbol")
@@ -386,9 +395,25 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {name}: warmup {args.warmup} done", file=sys.stderr, flush=True)
 
-    # timed region: host clock around K device-synchronised steps; the library
-    # records a HIP event pair around every kernel on the launch stream
+    # survey: two steps with a HIP event pair around every kernel, for the
+    # per-kernel table and to find the dominant kernel (most time per step)
+    survey_steps = 2
     binding.profile_reset()
+    binding.profile_filter(None)
+    binding.profile_enable(True)
+    for _ in range(survey_steps):
+        step()
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    survey = binding.profile_read()
+    dom_name = max(survey, key=lambda n: survey[n][1])
+
+    # timed region: host clock around K device-synchronised steps; the library
+    # records a HIP event pair on the launch stream around the dominant
+    # kernel's launches only (an event pair around every kernel would add a
+    # bubble per launch to the steps being timed)
+    binding.profile_reset()
+    binding.profile_filter(dom_name)
     binding.profile_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -400,6 +425,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     binding.profile_enable(False)
+    binding.profile_filter(None)
     prof = binding.profile_read()
     elapsed = t1 - t0
     ms_per_step = 1e3 * elapsed / args.steps
@@ -407,14 +433,41 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.3f})",
           file=sys.stderr, flush=True)
 
+    # cold-cache steps: the timed steps above run back to back, so inputs
+    # smaller than the Infinity Cache (the token batch, the router weights)
+    # can be partly resident from the previous step; here each step follows a
+    # 512 MiB read and is timed alone (the read is outside the event pair)
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        times = []
+        for i in range(args.cold_steps):
+            # a 512 MiB read: evicts without leaving dirty lines to drain
+            # during the timed step
+            _ = flush.sum()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del flush
+        times.sort()
+        cold = {"ms_per_step_median": round(times[len(times) // 2], 4),
+                "ms_per_step_min": round(times[0], 4), "steps": args.cold_steps,
+                "evict_read_bytes": 512 << 20}
+        print(f"[bench] cold-cache steps: median {cold['ms_per_step_median']:.3f} ms",
+              file=sys.stderr, flush=True)
+
     kept = out.kept.cpu().tolist()
     work = kernel_work(wl, kept, C, args.router, args.cos_dim)
     kern = {}
-    for n, (cnt, tot) in prof.items():
-        kern[n] = {"launches": cnt, "avg_ms": tot / cnt, "ms_per_step": tot / args.steps,
+    for n, (cnt, tot) in survey.items():
+        kern[n] = {"launches": cnt, "avg_ms": tot / cnt, "ms_per_step": tot / survey_steps,
                    "class": classify(n)}
-    dom_name = max(kern, key=lambda n: kern[n]["ms_per_step"])
-    dom = kern[dom_name]
+    cnt, tot = prof[dom_name]
+    dom = {"avg_ms": tot / cnt, "class": classify(dom_name)}
     cls = dom["class"]
     wk = work.get(cls, {"bytes": 0.0, "flops": 0.0})
     avg_s = dom["avg_ms"] / 1e3
@@ -457,8 +510,9 @@ def main():
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
-                        k["launches"] // args.steps, "class": k["class"]}
+                        k["launches"] // survey_steps, "class": k["class"]}
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
+        "cold_cache": cold,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and not bwd and not rkw and not args.k:

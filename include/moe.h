@@ -305,6 +305,11 @@ const char *moe_status_string(int status);
  * launches and the summed duration in milliseconds since the last reset.
  * Not thread-safe; meant for one benchmarking thread. */
 int moe_profile_enable(int on);
+/* Restrict the timing records to launches whose name ("role:tile", as
+ * moe_profile_read reports it) equals `name`; NULL or "" records every
+ * launch.  Each record adds an event pair to its stream, so a benchmark that
+ * times one kernel class keeps the others free of them. */
+int moe_profile_filter(const char *name);
 int moe_profile_reset(void);
 /* Fills up to `cap` entries; returns the number of kernel names recorded. */
 int moe_profile_read(char *names /* cap x 64 chars */, int64_t *launches,

@@ -31,7 +31,7 @@ ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_ex", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_mlp", "moe_combine", "moe_layer_forward",
             "moe_layer_backward",
-            "moe_status_string", "moe_profile_enable", "moe_profile_reset",
+            "moe_status_string", "moe_profile_enable", "moe_profile_filter", "moe_profile_reset",
             "moe_profile_read")
 
 
@@ -116,6 +116,8 @@ def lib():
             L.moe_status_string.argtypes = [i32]
             L.moe_profile_enable.restype = i32
             L.moe_profile_enable.argtypes = [i32]
+            L.moe_profile_filter.restype = i32
+            L.moe_profile_filter.argtypes = [ctypes.c_char_p]
             L.moe_profile_reset.restype = i32
             L.moe_profile_reset.argtypes = []
             L.moe_profile_read.restype = i32
@@ -459,6 +461,11 @@ def _outputs_struct(cfg, out: LayerOutputs, router_only: bool = False) -> Output
 # ------------------------------------------------------------------ profiling
 def profile_enable(on: bool = True):
     lib().moe_profile_enable(int(on))
+
+
+def profile_filter(name=None):
+    """Time only launches named `name` ("role:tile"); None times every launch."""
+    lib().moe_profile_filter(None if not name else name.encode())
 
 
 def profile_reset():

@@ -391,6 +391,8 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 bool g_prof = false;
+bool g_open = false;       // a record was begun for the launch in flight
+std::string g_only;        // profile only launches of this name ("" = all)
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -416,13 +418,16 @@ const char *intern_name(const char *a, const char *b) {
 }
 
 void prof_begin(hipStream_t s, const char *name) {
-  if (!g_prof) return;
+  g_open = false;
+  if (!g_prof || (!g_only.empty() && g_only != name)) return;
   ProfRec r{name, pool_event(), pool_event()};
   if (r.a) (void)hipEventRecord(r.a, s);
   g_recs.push_back(r);
+  g_open = true;
 }
 void prof_end(hipStream_t s) {
-  if (!g_prof || g_recs.empty()) return;
+  if (!g_open || g_recs.empty()) return;
+  g_open = false;
   if (g_recs.back().b) (void)hipEventRecord(g_recs.back().b, s);
 }
 }  // namespace moe_host
@@ -852,6 +857,11 @@ const char *moe_status_string(int status) {
 
 int moe_profile_enable(int on) {
   g_prof = on != 0;
+  return MOE_OK;
+}
+
+int moe_profile_filter(const char *name) {
+  g_only = name ? name : "";
   return MOE_OK;
 }
 
