@@ -767,7 +767,7 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
     a.A = dY; a.a_g = C * d; a.a_m = d; a.a_k = 1;
     a.B = (const bf16 *)w->w2; a.b_g = d * F; a.b_n = 1; a.b_k = F; a.b_kmax = d;
     a.C = dZ; a.c_g = C * F; a.c_m = F; a.Z = Z; a.mrows = kept; a.M = C; a.K = d;
-    a.N = (int)F; a.G = (int)E;
+    a.N = (int)F; a.G = (int)E; a.b_stream = 1;
     e = moe_host::launch_gemm_gen(a, false, true, true, "bwd_expert_dz", s);
   }
   if (e == hipSuccess && C > 0) {  // dX = dZ W1
@@ -775,7 +775,7 @@ int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *
     a.A = dZ; a.a_g = C * F; a.a_m = F; a.a_k = 1;
     a.B = (const bf16 *)w->w1; a.b_g = F * d; a.b_n = 1; a.b_k = d; a.b_kmax = F;
     a.C = dX; a.c_g = C * d; a.c_m = d; a.mrows = kept; a.M = C; a.K = F; a.N = (int)d;
-    a.G = (int)E;
+    a.G = (int)E; a.b_stream = 1;
     e = moe_host::launch_gemm_gen(a, false, true, false, "bwd_expert_dx", s);
   }
   if (e == hipSuccess) {  // dW2 = dY^T H  (K = kept rows of the expert)

@@ -50,10 +50,15 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(GenArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = a.N / BN;
-  const int tile = blockIdx.x;
-  const int g = tile / (tiles_m * tiles_n);
-  const int rem = tile - g * tiles_m * tiles_n;
-  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  // a group's tiles on one XCD (its operand panels shared in that L2), in
+  // grouped order, as in the forward GEMMs
+  const int per = tiles_m * tiles_n, total = a.G * per;
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, per)
+                                  : xcd_remap(blockIdx.x, total);
+  const int g = tile / per;
+  const int rem = tile - g * per;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t mvalid = a.M;
   if (a.mrows) mvalid = a.mrows[g] < mvalid ? a.mrows[g] : mvalid;
   const int64_t m0 = (int64_t)tm * BM;
@@ -219,7 +224,7 @@ __device__ __forceinline__ bf16x8 frag_kmajor(uint32_t tile, int row0, int kbase
 
 // BM = 128 (waves 2 x 2 of 64 x 64) or 64 (waves 1 x 4 of 64 x 32; the A
 // operand K-contiguous), for groups of at most 64 rows (a capacity of 64).
-template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32, int BM = 128>
+template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32, int BM = 128, bool NTB = false>
 __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(BM == 128 || (BM == 64 && !AKM), "tile rows");
@@ -234,10 +239,15 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = a.N / BN;
-  const int tile = blockIdx.x;
-  const int g = tile / (tiles_m * tiles_n);
-  const int rem = tile - g * tiles_m * tiles_n;
-  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  // a group's tiles on one XCD (its operand panels shared in that L2), in
+  // grouped order, as in the forward GEMMs
+  const int per = tiles_m * tiles_n, total = a.G * per;
+  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, per)
+                                  : xcd_remap(blockIdx.x, total);
+  const int g = tile / per;
+  const int rem = tile - g * per;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
   int64_t mvalid = a.M;
   if (a.mrows) mvalid = a.mrows[g] < mvalid ? a.mrows[g] : mvalid;
   const int64_t m0 = (int64_t)tm * BM;
@@ -299,8 +309,8 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
                    __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + (CHA * wave + i) * 1024));
 #pragma unroll
     for (int i = 0; i < CH; i++)
-      dma16<false>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILEA +
-                                                              (CH * wave + i) * 1024));
+      dma16<NTB>(gb, vob[i], __builtin_amdgcn_readfirstlane(lds0 + st * STAGE + TILEA +
+                                                            (CH * wave + i) * 1024));
   };
 
   f32x16 acc[2][TN];
@@ -763,13 +773,14 @@ static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s
 // with a long reduction (the expert dX over d_ff, the router's dW over the
 // tokens: streaming-bound, measured 14-16% faster); else K steps of 32 (4
 // stages, two workgroups per CU, which the many-tile dense products need)
-template <bool AKM, bool BKM, bool DG>
+// NT: the B operand is streamed once (expert weights): non-temporal loads
+template <bool AKM, bool BKM, bool DG, bool NT>
 static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t s) {
   if constexpr (!AKM) {  // groups of at most 64 rows: 64-row tiles
     if (a.M <= 64) {
       const int tiles = a.G * (a.N / 128);
       if (tiles <= 0) return hipGetLastError();
-      MOE_LAUNCH(intern_name(role, "dma64x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32, 64>),
+      MOE_LAUNCH(intern_name(role, "dma64x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32, 64, NT>),
                  dim3(tiles), dim3(256), 0, s, a);
       return hipGetLastError();
     }
@@ -777,10 +788,10 @@ static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t 
   const int tiles = a.G * (int)(a.M / 128) * (a.N / 128);
   if (tiles <= 0) return hipGetLastError();
   if (a.M <= 128 && a.K >= 4096 && a.K % 64 == 0)
-    MOE_LAUNCH(intern_name(role, "dma128x128k64"), (gemm_dmag_kernel<AKM, BKM, DG, 3, 64>),
+    MOE_LAUNCH(intern_name(role, "dma128x128k64"), (gemm_dmag_kernel<AKM, BKM, DG, 3, 64, 128, NT>),
                dim3(tiles), dim3(256), 0, s, a);
   else
-    MOE_LAUNCH(intern_name(role, "dma128x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32>),
+    MOE_LAUNCH(intern_name(role, "dma128x128"), (gemm_dmag_kernel<AKM, BKM, DG, 4, 32, 128, NT>),
                dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -840,9 +851,13 @@ hipError_t launch_gemm_gen(const GenArgs &a, bool a_kmajor, bool b_kmajor, bool 
     return launch_dwk_t<128>(a, role, s);
   }
   if (dmag_ok(a, a_kmajor, b_kmajor)) {
-    if (!a_kmajor && b_kmajor && dgelu) return launch_dmag_t<false, true, true>(a, role, s);
-    if (!a_kmajor && b_kmajor) return launch_dmag_t<false, true, false>(a, role, s);
-    if (a_kmajor && b_kmajor) return launch_dmag_t<true, true, false>(a, role, s);
+    if (!a_kmajor && b_kmajor && dgelu)
+      return a.b_stream ? launch_dmag_t<false, true, true, true>(a, role, s)
+                        : launch_dmag_t<false, true, true, false>(a, role, s);
+    if (!a_kmajor && b_kmajor)
+      return a.b_stream ? launch_dmag_t<false, true, false, true>(a, role, s)
+                        : launch_dmag_t<false, true, false, false>(a, role, s);
+    if (a_kmajor && b_kmajor) return launch_dmag_t<true, true, false, false>(a, role, s);
   }
   const bool n128 = a.N % 128 == 0;
 #define MOE_GEN(BN_)                                                                     \

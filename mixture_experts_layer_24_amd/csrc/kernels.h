@@ -75,6 +75,7 @@ struct GenArgs {
   int64_t K;
   int N, G;
   int nsplit;  // short-reduction weight-gradient kernel: N sweeps per row panel (set by the launcher)
+  int b_stream;  // B is read once (expert weights): non-temporal loads
 };
 
 }  // namespace moe
