@@ -88,6 +88,10 @@ def parse():
                         "the backward recomputes them")
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
+    p.add_argument("--expert-weights", default="auto", choices=["auto", "plain", "packed"],
+                   help="bf16 expert weights row-major (plain) or in 128-row x 64-k blocks "
+                        "(packed once before timing); auto = packed for a forward pass "
+                        "with bf16 experts and d, d_ff multiples of 128")
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB")
     p.add_argument("--cold-steps", type=int, default=5,
                    help="extra steps, each after a 512 MiB read that evicts the 256 MB "
@@ -349,10 +353,24 @@ def main():
             rkw.update(cos_tau=args.cos_tau, cos_dim=args.cos_dim)
         if args.router_losses:
             rkw.update(w_importance=0.01, w_load=0.01)
+    bwd = args.backward or args.train
+    packable = (wl.act == "bf16" and wl.wfmt == "plain" and wl.d % 128 == 0 and
+                wl.d_ff % 128 == 0)
+    packed = args.expert_weights == "packed" or (args.expert_weights == "auto" and packable
+                                                 and not bwd)
+    if packed:
+        if not packable or bwd:
+            raise SystemExit("bench.py: packed expert weights need a forward pass with bf16 "
+                             "experts and d, d_ff multiples of 128")
+        wl = wl.replace(wfmt="packed")
     cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy,
                             **rkw)
+    oracle_inp = inp  # the CPU oracle reads the row-major weights
+    if packed:  # once, where a model's weights are loaded: outside the timed steps
+        inp = dict(inp, w1=binding.pack_expert_weights(cfg, 1, inp["w1"]),
+                   w2=binding.pack_expert_weights(cfg, 2, inp["w2"]))
+        torch.cuda.synchronize()
     C = binding.capacity(cfg)
-    bwd = args.backward or args.train
     out = binding.alloc_outputs(cfg, dev, z_loss=args.z_loss, logits=bwd, x_disp=bwd,
                                 y_disp=bwd, saved_activations=bwd and not args.recompute,
                                 importance_loss=args.router_losses,
@@ -498,7 +516,9 @@ def main():
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02^2), bf16 RNE)",
         "config": {"workload": name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k,
                    "d_ff": wl.d_ff, "d_ff_dense": wl.d_ff_dense, "capacity": C,
-                   "capacity_factor": wl.capacity_factor, "expert_weights": wl.wfmt,
+                   "capacity_factor": wl.capacity_factor,
+                   "expert_weights": ("bf16 packed (128-row x 64-k blocks, packed once "
+                                      "before timing)" if packed else wl.wfmt),
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
                    "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
@@ -517,7 +537,7 @@ def main():
     }
     if not args.no_cpu_baseline and not bwd and not rkw and not args.k:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, oracle_inp, args.cpu_seconds)
     print(json.dumps(res))
 
 

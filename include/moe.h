@@ -68,6 +68,16 @@ extern "C" {
 #define MOE_W_INT8_G128 1 /* symmetric int8 codes q, fp16 scale s per 128
                              consecutive input-dim elements of an output row;
                              weight = s * q (survey notes sec. 1.2.2) */
+#define MOE_W_BF16_PACKED 2 /* bf16 weights of an [E, N, K] expert matrix
+                               in blocks of 128 output rows x 64 inputs:
+                               element (e, n, k) sits at e*N*K +
+                               (n/128)*128*K + (k/64)*8192 + (n%128)*64 +
+                               k%64, so each 64-wide K step of a 128-row
+                               block is 16 KB of contiguous memory (the
+                               weight stream of the expert GEMMs reads whole
+                               blocks).  bf16 activations, d and d_ff
+                               multiples of 128; forward entry points only.
+                               moe_pack_expert_weights writes it. */
 
 /* capacity overflow policy */
 #define MOE_DROP_TOKEN_ORDER 0   /* first come, first served in token order */
@@ -118,7 +128,8 @@ typedef struct moe_config {
   double capacity_factor; /* > 0; C = min(T, ceil(k*T*cf/E)) */
   int64_t capacity;       /* > 0 overrides the formula (still clamped to T) */
   int32_t act_dtype;      /* MOE_F32 | MOE_BF16 */
-  int32_t expert_wfmt;    /* MOE_W_PLAIN | MOE_W_INT8_G128 (bf16 acts only) */
+  int32_t expert_wfmt;    /* MOE_W_PLAIN | MOE_W_INT8_G128 | MOE_W_BF16_PACKED
+                             (the last two: bf16 acts only) */
   int32_t normalize_topk; /* k >= 2: 1 = gates renormalised over the k */
   int32_t pr_moe;         /* 1 = add the fixed dense MLP D(x) */
   int32_t add_skip;       /* 1 = add x (the residual a dropped token rides) */
@@ -295,6 +306,18 @@ int moe_layer_forward(const moe_config *cfg, const void *x,
 int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *w,
                        const moe_outputs *fwd, const void *dy, float g_aux, float g_z,
                        moe_grads *grads, void *ws, size_t ws_bytes, void *stream);
+
+/* Rewrites one row-major bf16 expert weight tensor in MOE_W_BF16_PACKED
+ * order, device to device, on `stream`: which = 1 packs W1 [E, d_ff, d],
+ * which = 2 packs W2 [E, d, d_ff] (E, d, d_ff from cfg).  Both buffers are
+ * the caller's, the same size, and must not overlap.  Meant to run once,
+ * where the weights are loaded; the packed tensors then serve every forward
+ * call with expert_wfmt = MOE_W_BF16_PACKED.
+ * Errors: MOE_ERR_INVALID_ARG (null or misaligned pointer, which not 1 or 2,
+ * an invalid cfg), MOE_ERR_UNSUPPORTED (fp32 activations, d or d_ff not a
+ * multiple of 128). */
+int moe_pack_expert_weights(const moe_config *cfg, int which, const void *w, void *w_packed,
+                            void *stream);
 
 /* Static description of a status code. */
 const char *moe_status_string(int status);

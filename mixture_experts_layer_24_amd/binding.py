@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_W_PLAIN, MOE_W_INT8_G128 = 0, 1
+MOE_W_PLAIN, MOE_W_INT8_G128, MOE_W_BF16_PACKED = 0, 1, 2
+WFMTS = {"plain": MOE_W_PLAIN, "int8": MOE_W_INT8_G128, "packed": MOE_W_BF16_PACKED}
 MOE_DROP_TOKEN_ORDER = 0
 MOE_DROP_GATE_PRIORITY = 1
 ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY_BACKWARD = \
@@ -30,7 +31,7 @@ ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_ex", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_mlp", "moe_combine", "moe_layer_forward",
-            "moe_layer_backward",
+            "moe_layer_backward", "moe_pack_expert_weights",
             "moe_status_string", "moe_profile_enable", "moe_profile_filter", "moe_profile_reset",
             "moe_profile_read")
 
@@ -116,6 +117,8 @@ def lib():
             L.moe_status_string.argtypes = [i32]
             L.moe_profile_enable.restype = i32
             L.moe_profile_enable.argtypes = [i32]
+            L.moe_pack_expert_weights.restype = i32
+            L.moe_pack_expert_weights.argtypes = [cfgp, i32, vp, vp, vp]
             L.moe_profile_filter.restype = i32
             L.moe_profile_filter.argtypes = [ctypes.c_char_p]
             L.moe_profile_reset.restype = i32
@@ -149,10 +152,12 @@ def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16"
         raise ValueError(f"drop_policy {drop_policy!r}")
     if router not in ROUTERS:
         raise ValueError(f"router {router!r}")
+    if wfmt not in WFMTS:
+        raise ValueError(f"wfmt {wfmt!r}")
     return Config(T=T, d=d, E=E, k=k, d_ff=d_ff, d_ff_dense=d_ff_dense,
                   capacity_factor=capacity_factor, capacity=capacity,
                   act_dtype=MOE_F32 if act == "f32" else MOE_BF16,
-                  expert_wfmt=MOE_W_INT8_G128 if wfmt == "int8" else MOE_W_PLAIN,
+                  expert_wfmt=WFMTS[wfmt],
                   normalize_topk=int(normalize_topk), pr_moe=int(pr_moe),
                   add_skip=int(add_skip),
                   drop_policy=(MOE_DROP_GATE_PRIORITY if drop_policy == "gate_priority"
@@ -271,6 +276,18 @@ def moe_expert_ffn(cfg, x_disp, kept, w1, w1_scale, w2, w2_scale, y_disp, ws, st
         _ptr(w2, (E, d, F), wd, "w2"),
         _ptr(w2_scale, (E, d, F // 128), torch.float16, "w2_scale", not q8),
         _ptr(y_disp, (E, C, d), a, "y_disp"), wsp, wsn, _stream(stream)))
+
+
+def pack_expert_weights(cfg, which, w, out=None, stream=None):
+    """Row-major bf16 expert weights (which = 1: W1 [E, d_ff, d]; 2: W2 [E, d,
+    d_ff]) in MOE_W_BF16_PACKED order, in a tensor of the same shape."""
+    shape = (cfg.E, cfg.d_ff, cfg.d) if which == 1 else (cfg.E, cfg.d, cfg.d_ff)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
+    _check("moe_pack_expert_weights", lib().moe_pack_expert_weights(
+        ctypes.byref(cfg), which, _ptr(w, shape, torch.bfloat16, "w"),
+        _ptr(out, shape, torch.bfloat16, "w_packed"), _stream(stream)))
+    return out
 
 
 def moe_dense_mlp(cfg, x, wm1, wm2, dense_out, ws, stream=None):

@@ -28,7 +28,8 @@ int check_config(const moe_config *c) {
   if (c->T < 0 || c->d < 1 || c->E < 1 || c->k < 1 || c->k > c->E || c->d_ff < 1)
     return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (c->expert_wfmt != MOE_W_PLAIN && c->expert_wfmt != MOE_W_INT8_G128)
+  if (c->expert_wfmt != MOE_W_PLAIN && c->expert_wfmt != MOE_W_INT8_G128 &&
+      c->expert_wfmt != MOE_W_BF16_PACKED)
     return MOE_ERR_INVALID_ARG;
   if ((c->normalize_topk | c->pr_moe | c->add_skip) & ~1) return MOE_ERR_INVALID_ARG;
   if (c->capacity < 0) return MOE_ERR_INVALID_ARG;
@@ -54,7 +55,7 @@ int check_config(const moe_config *c) {
     if (c->d % 64 || c->d_ff % 64 || (c->pr_moe && c->d_ff_dense % 64))
       return MOE_ERR_UNSUPPORTED;
   }
-  if (c->expert_wfmt == MOE_W_INT8_G128) {
+  if (c->expert_wfmt == MOE_W_INT8_G128 || c->expert_wfmt == MOE_W_BF16_PACKED) {
     if (c->act_dtype != MOE_BF16 || c->d % 128 || c->d_ff % 128) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
@@ -367,10 +368,13 @@ hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t 
   } else {
     xsched = nullptr;
   }
-  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre, xsched};
+  const int pk = c->expert_wfmt == MOE_W_BF16_PACKED;
+  GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre, xsched,
+              pk};
   e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
   if (e != hipSuccess) return e;
-  GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E, nullptr, xsched};
+  GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E, nullptr, xsched,
+              pk};
   return moe_host::launch_gemm(g2, bf, q8, 0, "expert_ffn2", s);
 }
 
@@ -853,6 +857,20 @@ const char *moe_status_string(int status) {
     case MOE_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+int moe_pack_expert_weights(const moe_config *cfg, int which, const void *w, void *w_packed,
+                            void *stream) {
+  const int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  if (which != 1 && which != 2) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_BF16 || cfg->d % 128 || cfg->d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t N = which == 1 ? cfg->d_ff : cfg->d, K = which == 1 ? cfg->d : cfg->d_ff;
+  const uint64_t bytes = (uint64_t)cfg->E * N * K * 2;
+  if (!need(w, 1, 16) || !need(w_packed, 1, 16)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t a = (uintptr_t)w, b = (uintptr_t)w_packed;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  return hip_status(moe_host::launch_pack_weights(w, w_packed, cfg->E, N, K, (hipStream_t)stream));
 }
 
 int moe_profile_enable(int on) {

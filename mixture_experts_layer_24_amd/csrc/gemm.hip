@@ -238,9 +238,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 // barrier that publishes a stage, because the compiler would otherwise wait
 // for every outstanding load before each LDS read.
 // NTB: load the weight operand non-temporally (read once)
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, int GELU>
+// PB: B in blocks of 128 rows x 64 K (MOE_W_BF16_PACKED): a tile's K step
+// reads 16 KB of contiguous memory per 128 weight rows instead of 128 bytes
+// from each row, which the DRAM streams at a higher rate.
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool NTB, int GELU, bool PB = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   static_assert(BK == 64 || BK == 32, "K step");
+  static_assert(!PB || (BK == 64 && BN % 128 == 0), "packed weights: 64-wide K steps, 128-row blocks");
   constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -299,13 +303,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < B_PW; i++) {
     const int R = RPC * (wave * B_PW + i) + lr;
-    voffb[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
+    if constexpr (PB)  // block R / 128 of the tile, row R % 128 of it (n0 is a block start)
+      voffb[i] = (uint32_t)((int64_t)(R / 128) * 128 * K * 2 + (R % 128) * ROWB +
+                            ((slot ^ swz_slot<BK>(R)) << 4));
+    else
+      voffb[i] = (uint32_t)((int64_t)R * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
   }
   const uint32_t dsta = lds0 + wave * A_PW * 1024;
   const uint32_t dstb = lds0 + BM * ROWB + wave * B_PW * 1024;
   auto issue = [&](int st, int kt) __attribute__((always_inline)) {
     const char *ga = Abase + (int64_t)kt * ROWB;
-    const char *gb = Bbase + (int64_t)kt * ROWB;
+    const char *gb = Bbase + (int64_t)kt * (PB ? 128 * ROWB : ROWB);
 #pragma unroll
     for (int i = 0; i < A_PW; i++)
       dma16<false>(ga, voffa[i], __builtin_amdgcn_readfirstlane(dsta + st * STAGE + i * 1024));
@@ -727,6 +735,26 @@ __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, in
   }
 }
 
+// Row-major [G][N][K] bf16 weights -> MOE_W_BF16_PACKED order: per group,
+// blocks of 128 rows, each as K/64 consecutive 128 x 64 pieces.  Thread o
+// writes 16-byte unit o of the packed tensor (writes coalesced; eight
+// consecutive units read one 128-byte row piece).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4 *src, u32x4 *dst, int64_t N,
+                                                           int64_t K, int64_t total) {
+  const int64_t per = N * K / 8, kb_n = K / 64;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t g = o / per;
+    int64_t r = o - g * per;
+    const int64_t c = r & 7;  // unit within the row's 64-wide piece
+    r >>= 3;
+    const int64_t row = r & 127;  // row within the 128-row block
+    r >>= 7;
+    const int64_t kb = r % kb_n, nb = r / kb_n;
+    dst[o] = src[g * per + ((nb * 128 + row) * K + kb * 64) / 8 + c];
+  }
+}
+
 // fp32 activations and weights: a plain 64x64 tile, 4x4 outputs per thread,
 // any shape (bounds-checked); the correctness path for fp32 layers.
 template <int GELU>
@@ -815,15 +843,15 @@ static hipError_t launch_cfg(const GemmArgs &a, int b_int8, int gelu, hipStream_
   return launch_cfg_t<BM, BN, WM, WN, MF, false>(a, epi_of(a, gelu), grid, block, name, s);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool NT>
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool NT, bool PB = false>
 static hipError_t launch_dma_t(const GemmArgs &a, int epi, dim3 grid, dim3 block, const char *name,
                                hipStream_t s) {
   if (epi == 2)
-    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 2>), grid, block, 0, s, a);
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 2, PB>), grid, block, 0, s, a);
   else if (epi == 1)
-    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 1>), grid, block, 0, s, a);
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 1, PB>), grid, block, 0, s, a);
   else
-    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 0>), grid, block, 0, s, a);
+    MOE_LAUNCH(name, (gemm_dma_kernel<BM, BN, WM, WN, BK, NS, NT, 0, PB>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -833,6 +861,11 @@ static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t 
   const int tiles = a.G * (int)((a.M_cap + BM - 1) / BM) * (a.N / BN);
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
+  if constexpr (BK == 64) {
+    if (a.b_packed)  // packed expert weights: streamed once, non-temporal
+      return launch_dma_t<BM, BN, WM, WN, BK, NS, true, true>(
+          a, epi_of(a, gelu), grid, block, intern_name(role, tile), s);
+  }
   const char *name = intern_name(role, tile);
   if (nt_b)
     return launch_dma_t<BM, BN, WM, WN, BK, NS, true>(a, epi_of(a, gelu), grid, block, name, s);
@@ -866,6 +899,17 @@ static hipError_t launch_dma_i8(const GemmArgs &a, int gelu, hipStream_t s, cons
     MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, s, a);
   else
     MOE_LAUNCH(name, (gemm_dma_i8_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const void *w, void *wp, int64_t G, int64_t N, int64_t K,
+                               hipStream_t s) {
+  const int64_t total = G * N * K / 8;  // 16-byte units
+  if (total <= 0) return hipGetLastError();
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  MOE_LAUNCH(intern_name("pack_weights", "b128x64"), pack_weights_kernel, dim3((unsigned)blocks),
+             dim3(256), 0, s, (const u32x4 *)w, (u32x4 *)wp, N, K, total);
   return hipGetLastError();
 }
 

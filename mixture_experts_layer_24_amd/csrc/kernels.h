@@ -58,6 +58,8 @@ struct GemmArgs {
   // int8 groups with more than 128 rows: the XCD schedule written by
   // launch_tile_sched for these rows (16 G + 16 int32), or null
   const int32_t *xsched;
+  // B in blocks of 128 rows x 64 K (MOE_W_BF16_PACKED) instead of row-major
+  int b_packed;
 };
 
 // general grouped GEMM of the backward (backward.hip)
@@ -132,6 +134,9 @@ hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots
 // in the per-kernel timing ("expert_ffn1", "expert_ffn2", "dense_mlp1", ...)
 hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gelu,
                        const char *role, hipStream_t s);
+// [G][N][K] row-major bf16 -> blocks of 128 rows x 64 K (N % 128 == 0, K % 64 == 0)
+hipError_t launch_pack_weights(const void *w, void *wp, int64_t G, int64_t N, int64_t K,
+                               hipStream_t s);
 // XCD schedule of G groups' 256-row int8 tiles from their row counts (G <= 256)
 hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int32_t *xs,
                              hipStream_t s);

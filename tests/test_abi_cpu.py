@@ -85,6 +85,9 @@ BAD_CONFIGS = [
     (dict(d=100), binding.MOE_ERR_UNSUPPORTED),           # bf16 needs d % 64 == 0
     (dict(d=192, wfmt="int8"), binding.MOE_ERR_UNSUPPORTED),  # int8 needs d % 128 == 0
     (dict(act="f32", wfmt="int8"), binding.MOE_ERR_UNSUPPORTED),
+    (dict(d=192, wfmt="packed"), binding.MOE_ERR_UNSUPPORTED),  # packed: 128-row blocks
+    (dict(d_ff=320, wfmt="packed"), binding.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", wfmt="packed"), binding.MOE_ERR_UNSUPPORTED),
     (dict(pr_moe=True, d_ff_dense=0), binding.MOE_ERR_INVALID_ARG),
     (dict(router="top_p", top_p=0.0), binding.MOE_ERR_INVALID_ARG),
     (dict(router="top_p", top_p=float("inf")), binding.MOE_ERR_INVALID_ARG),
@@ -224,3 +227,30 @@ def test_router_variant_arguments(L):
     assert route_ex(cos, dict(w_proj=ok)) == binding.MOE_ERR_INVALID_ARG
     assert route_ex(cos, dict(w_proj=ok, expert_emb=ok + 4)) == binding.MOE_ERR_INVALID_ARG
     assert ws > 0
+
+
+def test_pack_expert_weights_arguments(L):
+    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=256)
+    ok, other = 1 << 20, 1 << 30  # never dereferenced: validation fails first
+    for which in (0, 3):
+        assert L.moe_pack_expert_weights(ctypes.byref(cfg), which, ok, other, None) == \
+            binding.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(ctypes.byref(cfg), 1, None, other, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(ctypes.byref(cfg), 1, ok + 2, other, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    # the two buffers overlap (W1 is 4 * 256 * 128 * 2 bytes)
+    assert L.moe_pack_expert_weights(ctypes.byref(cfg), 1, ok, ok + 4096, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    bad = binding.make_config(T=16, d=192, E=4, k=1, d_ff=256)
+    assert L.moe_pack_expert_weights(ctypes.byref(bad), 2, ok, other, None) == \
+        binding.MOE_ERR_UNSUPPORTED
+
+
+def test_backward_rejects_packed_weights(L):
+    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, wfmt="packed")
+    ok = 1 << 20
+    w, f, g = binding.Weights(), binding.Outputs(), binding.Grads()
+    rc = L.moe_layer_backward(ctypes.byref(cfg), ok, ctypes.byref(w), ctypes.byref(f), ok, 0.0,
+                              0.0, ctypes.byref(g), ok, 1 << 40, None)
+    assert rc == binding.MOE_ERR_UNSUPPORTED
