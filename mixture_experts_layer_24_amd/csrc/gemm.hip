@@ -23,9 +23,14 @@
 // past rows[g] exit at once, so only kept rows cost MFMA time, and only
 // experts with at least one kept row stream their weights.
 // Blocks are mapped to tiles XCD by XCD: with a multiple of 8 groups, XCD x
-// takes experts x, x+8, ... (skewed loads spread evenly) and runs each
-// expert's tiles back to back so they share its L2 for their A rows;
-// otherwise each XCD takes a contiguous range of tiles.
+// takes experts x, x+8, ... and runs each expert's tiles back to back so
+// they share its L2 for their A rows; otherwise each XCD takes a contiguous
+// range of tiles.  The int8 kernel can instead follow a per-call schedule
+// that deals the experts to the XCDs by their row counts
+// (tile_sched_kernel), which evens out skewed loads.  The DMA kernels below
+// read bf16 weights either row-major or packed in blocks of 128 rows x 64 K
+// (MOE_W_BF16_PACKED), where a K step of a block is 16 KB of contiguous
+// memory.
 #include "common.h"
 #include "dma.h"
 #include "kernels.h"

@@ -11,12 +11,15 @@
 //
 // One block = 64 tokens x all experts (E <= 256, padded to a multiple of 32).
 // bf16: the 64 x Ep logit tile is a bf16 MFMA contraction (32x32x16, fp32
-// accumulate; the bf16 products are exact in fp32) over d in 128- or 64-wide
-// K steps, double-buffered through LDS (rows padded by 16 bytes so the
-// 16-byte operand reads are free of bank conflicts).  fp32: plain fp32 FMA dot products.
-// The epilogue is shared: the tile goes to LDS, each wave takes 16 rows; a
-// row's E logits sit 1-4 per lane and wave shuffles give the row max, the
-// softmax sum and the arg-max rounds of the top-k.
+// accumulate; the bf16 products are exact in fp32) over d in 64-wide K steps
+// whose operand tiles move global -> LDS by DMA three steps ahead
+// (router_dma_kernel); the register-staged router_bf16_kernel serves the
+// raw products of two weight matrices (noisy TopK).  fp32: plain fp32 FMA
+// dot products.  The epilogue is shared: the tile goes to LDS, each wave
+// takes 16 rows; a row's E logits sit 1-4 per lane (one slot per 64
+// experts); wave reductions (DPP within 16-lane rows, then the four row
+// totals) give the row max and the softmax sum, and each top-k round takes
+// the largest remaining logit and the lowest expert holding it by a ballot.
 #include "common.h"
 #include "dma.h"
 #include "kernels.h"
