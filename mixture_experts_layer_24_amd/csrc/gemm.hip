@@ -962,8 +962,15 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
       if (a.N % 256 == 0) return launch_dma<64, 256, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x256");
       return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");
     }
-    if (a.M_cap <= 128 && a.N % 256 == 0)
-      return launch_dma<128, 256, 2, 4, 64, 3>(a, nt, gelu, s, role, "dma128x256");
+    if (a.M_cap <= 128) {
+      // 128x512, one K step in flight: the same 64 KB of weights in flight
+      // as 128x256 with two, and 0.75 instead of 1 KB of LDS operand reads
+      // per MFMA.  Keeping the pre-activation spills at 256 VGPRs, so that
+      // form stays on 128x256.
+      if (a.N % 512 == 0 && epi_of(a, gelu) != 2)
+        return launch_dma<128, 512, 2, 4, 64, 2>(a, nt, gelu, s, role, "dma128x512");
+      if (a.N % 256 == 0) return launch_dma<128, 256, 2, 4, 64, 3>(a, nt, gelu, s, role, "dma128x256");
+    }
     if (a.M_cap > 128 && a.N % 256 == 0)
       return launch_dma<256, 256, 2, 4, 64, 2>(a, nt, gelu, s, role, "dma256x256");
     return launch_dma<128, 128, 2, 2, 64, 2>(a, nt, gelu, s, role, "dma128x128");

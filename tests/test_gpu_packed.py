@@ -39,9 +39,10 @@ def test_pack_matches_the_stated_layout(E, d, F):
     assert torch.equal(p2.cpu(), _pack_ref(w2))
 
 
-# capacities reaching each tile shape: 32x128, 64x256 / 64x128, 128x256, 256x256
+# capacities reaching each tile shape: 32x128, 64x256 / 64x128, 128x512 (N a
+# multiple of 512) / 128x256, 256x256
 FFN_CASES = [(20, 256, 512), (50, 256, 512), (60, 384, 256), (128, 256, 1024), (100, 1024, 2048),
-             (300, 512, 256)]
+             (90, 512, 768), (300, 512, 256)]
 
 
 @pytest.mark.parametrize("C,d,F", FFN_CASES)

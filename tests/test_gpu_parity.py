@@ -211,9 +211,11 @@ def test_dispatch_alone(T, E, k, C):
                 assert np.array_equal(xdn[ids[t, j], ref["slots"][t, j]], xn[t])
 
 
-# (C, d, d_ff): weight-streaming tiles for C <= 32 / 64 / 128, 256x256 and
-# 128x128 block tiles above, the 16x64 tile when N is not a multiple of 128
+# (C, d, d_ff): weight-streaming tiles for C <= 32 / 64 / 128 (128x512 when N
+# is a multiple of 512, else 128x256 or 128x128), 256x256 and 128x128 block
+# tiles above, the 16x64 tile when N is not a multiple of 128
 FFN_CASES = [(10, 128, 256), (20, 128, 256), (50, 128, 256), (100, 256, 384), (128, 128, 128),
+             (90, 512, 768),
              (300, 256, 512), (200, 384, 384), (40, 192, 320),
              # K a multiple of 1024: the DMA int8 tiles (256- and 128-row), partial tiles
              (300, 1024, 1024), (100, 1024, 2048)]

@@ -21,7 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 @pytest.mark.parametrize("src,kernel", [("gemm.hip", "gemm_dma"), ("backward.hip", "gemm_dmag"),
-                                        ("backward.hip", "gemm_dwk")])
+                                        ("backward.hip", "gemm_dwk"),
+                                        ("router.hip", "router_dma")])
 def test_dma_kernels_use_m0_only_for_their_own_loads(tmp_path, src, kernel):
     out = tmp_path / "k.s"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S",
