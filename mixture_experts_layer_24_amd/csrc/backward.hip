@@ -222,13 +222,18 @@ __device__ __forceinline__ bf16x8 frag_kmajor(uint32_t tile, int row0, int kbase
   return out;
 }
 
-// BM = 128 (waves 2 x 2 of 64 x 64) or 64 (waves 1 x 4 of 64 x 32; the A
+// BM = 128 (waves 2 x 2 of 64 x BN/2) or 64 (waves 1 x 4 of 64 x BN/4; the A
 // operand K-contiguous), for groups of at most 64 rows (a capacity of 64).
-template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32, int BM = 128, bool NTB = false>
+template <bool AKM, bool BKM, bool DGELU, int NS, int BK = 32, int BM = 128, bool NTB = false,
+          int BN = 128>
 __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(BM == 128 || (BM == 64 && !AKM), "tile rows");
-  constexpr int BN = 128, TILEA = BM * BK * 2, TILE = 128 * BK * 2;  // bytes per operand tile
+  // BN = 256 (K-major B only): the B tile is two 128-column sub-tiles, each
+  // laid out as a 128-column tile, so a K row of B is 512 contiguous bytes
+  static_assert(BN == 128 || (BN == 256 && BKM), "tile columns");
+  constexpr int NSUB = BN / 128;
+  constexpr int TILEA = BM * BK * 2, TILE = BN * BK * 2;  // bytes per operand tile
   constexpr int STAGE = TILEA + TILE;
   constexpr int CHA = TILEA / 1024 / 4, CH = TILE / 1024 / 4;  // 1-KB DMA chunks per wave
   constexpr int WM = BM / 64, WN = 4 / WM, WTN = BN / WN, TN = WTN / 32;
@@ -282,9 +287,9 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
     if constexpr (!BKM) {
       const int R = RPC * q + lane / CPR, slot = lane % CPR;
       vob[i] = (uint32_t)(R * a.b_n * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
-    } else {
-      const int k = 4 * q + lane / 16, slot = lane % 16;
-      vob[i] = (uint32_t)(k * a.b_k * 2 + ((slot ^ swz_km(k)) << 4));
+    } else {  // sub-tile q / (BK / 4), its k rows 4 (q % (BK / 4)) ..
+      const int h = q / (BK / 4), k = 4 * (q % (BK / 4)) + lane / 16, slot = lane % 16;
+      vob[i] = (uint32_t)(k * a.b_k * 2 + h * 256 + ((slot ^ swz_km(k)) << 4));
     }
   }
   if constexpr (!AKM) {
@@ -338,7 +343,10 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
         const int k = kleft + idx / 16, c = idx % 16;
         const u32x4 z = {0u, 0u, 0u, 0u};
         if (AKM) *(u32x4 *)(smem + st * STAGE + k * 256 + c * 16) = z;
-        if (BKM) *(u32x4 *)(smem + st * STAGE + TILEA + k * 256 + c * 16) = z;
+        if (BKM)
+#pragma unroll
+          for (int h = 0; h < NSUB; h++)
+            *(u32x4 *)(smem + st * STAGE + TILEA + h * BK * 256 + k * 256 + c * 16) = z;
       }
       __syncthreads();
     }
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
       for (int j = 0; j < TN; j++) {
         const int row0 = wn * WTN + j * 32;
         if constexpr (BKM) {
-          bfr[j] = frag_kmajor(tb, row0, 16 * s, lane);
+          bfr[j] = frag_kmajor(tb + (row0 / 128) * BK * 256, row0 % 128, 16 * s, lane);
         } else {
           const int R = row0 + (lane & 31), c = 2 * s + (lane >> 5);
           bfr[j] = *(const bf16x8 *)(smem + st * STAGE + TILEA + R * ROWB +
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
   // GELU' factor applied before the single rounding to bf16
   bf16 *Cg = a.C + (int64_t)g * a.c_g;
   const bf16 *Zg = DGELU ? a.Z + (int64_t)g * a.c_g : nullptr;
-  constexpr int CROW = 132;
+  constexpr int CROW = BN + 4, CPRW = BN / 8;  // floats per LDS row, 8-wide chunks per row
   static_assert(64 * CROW * 4 <= NS * STAGE, "band fits the stages");
   float *cs = (float *)smem;
   for (int band = 0; band < WM; band++) {
@@ -400,8 +408,8 @@ __global__ __launch_bounds__(256) void gemm_dmag_kernel(GenArgs a) {
     }
     __syncthreads();
     const int64_t r0 = m0 + band * 64;
-    for (int idx = tid; idx < 64 * 16; idx += 256) {
-      const int R = idx >> 4, ch = idx & 15;
+    for (int idx = tid; idx < 64 * CPRW; idx += 256) {
+      const int R = idx / CPRW, ch = idx % CPRW;
       const int64_t m = r0 + R;
       if (m >= mvalid) continue;
       const float *src = cs + R * CROW + ch * 8;
@@ -769,13 +777,50 @@ static hipError_t launch_gen_t(const GenArgs &a, const char *role, hipStream_t s
   return hipGetLastError();
 }
 
-// K steps of 64 (3 stages, one workgroup per CU) for a single 128-row panel
-// with a long reduction (the expert dX over d_ff, the router's dW over the
-// tokens: streaming-bound, measured 14-16% faster); else K steps of 32 (4
-// stages, two workgroups per CU, which the many-tile dense products need)
+// A K-contiguous, B K-major and N a multiple of 256 (the expert and dense dZ
+// and dX, the router's dx): 256-column tiles, K steps of 32, 3 stages (4 for
+// 64-row tiles), two workgroups per CU -- each K row of the weight operand
+// is read as 512 contiguous bytes and the activation panel is read half as
+// often (measured: expert dZ 1.12 -> 0.87 ms, dense dZ / dX 0.71 / 0.62 ->
+// 0.62 / 0.52 ms at the 1.3B shape; the 350M shape's 64-row dZ / dX 0.25 /
+// 0.23 -> 0.22 / 0.19 ms).  Both operands K-major (the dense dW): the same
+// 256-column tiles while they number at least one per CU (dense dW1 / dW2
+// 0.59 / 0.58 -> 0.49 / 0.48 ms; the router's dW, 8 such tiles, stays on
+// 128 columns: 0.19 vs 0.30 ms).  Otherwise 128-column tiles: K steps of 64 (3
+// stages, one workgroup per CU) for a single 128-row panel with a long
+// reduction (the router's dW over the tokens: streaming-bound, measured
+// 14-16% faster than 32), else K steps of 32 (4 stages, two workgroups per
+// CU, which the many-tile dense products need).
 // NT: the B operand is streamed once (expert weights): non-temporal loads
 template <bool AKM, bool BKM, bool DG, bool NT>
 static hipError_t launch_dmag_t(const GenArgs &a, const char *role, hipStream_t s) {
+  if constexpr (AKM && BKM) {  // 256-column tiles when they still fill the chip
+    const int64_t tiles = (int64_t)a.G * (a.M / 128) * (a.N / 256);
+    if (a.N % 256 == 0 && tiles >= 256) {
+      MOE_LAUNCH(intern_name(role, "dma128x256"),
+                 (gemm_dmag_kernel<AKM, BKM, DG, 3, 32, 128, NT, 256>), dim3((unsigned)tiles),
+                 dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (!AKM && BKM) {  // 256-column tiles where N allows
+    if (a.N % 256 == 0) {
+      if (a.M <= 64) {
+        const int tiles = a.G * (a.N / 256);
+        if (tiles <= 0) return hipGetLastError();
+        MOE_LAUNCH(intern_name(role, "dma64x256"),
+                   (gemm_dmag_kernel<AKM, BKM, DG, 4, 32, 64, NT, 256>), dim3(tiles), dim3(256), 0,
+                   s, a);
+        return hipGetLastError();
+      }
+      const int tiles = a.G * (int)(a.M / 128) * (a.N / 256);
+      if (tiles <= 0) return hipGetLastError();
+      MOE_LAUNCH(intern_name(role, "dma128x256"),
+                 (gemm_dmag_kernel<AKM, BKM, DG, 3, 32, 128, NT, 256>), dim3(tiles), dim3(256), 0,
+                 s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (!AKM) {  // groups of at most 64 rows: 64-row tiles
     if (a.M <= 64) {
       const int tiles = a.G * (a.N / 128);

@@ -35,6 +35,10 @@ CASES = [
     W("bwd_dma_top2", T=512, d=384, E=8, k=2, d_ff=256, capacity_factor=1.0, zipf_s=0.5),
     # d_ff = 2048: the expert dW2 sweep over 16 column tiles is split in two
     W("bwd_split_sweep", T=512, d=256, E=8, k=2, d_ff=2048, capacity_factor=1.0, zipf_s=0.3),
+    # dense dW1 / dW2 with 256 tiles of 128 x 256 each (the wide tiles of the
+    # products with both operands K-major, reducing over T = 64 tokens)
+    W("bwd_wide_dense_dw", T=64, d=2048, E=8, k=1, d_ff=256, capacity_factor=1.0,
+      d_ff_dense=4096, pr_moe=True, add_skip=True),
 ]
 
 
