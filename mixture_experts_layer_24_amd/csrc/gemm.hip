@@ -225,6 +225,64 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// GELU epilogue that also keeps the pre-activation (Zpre): per row band (the
+// waves with wm == band) and sub-band of RB rows, the fp32 sums go through
+// LDS once, and every thread turns 8 consecutive sums into both outputs (the
+// sum and its GELU, each rounded once to bf16) with coalesced 16-byte
+// stores.  One pass over the accumulators, so nothing beyond them is live
+// while they are written.  LDSB: bytes of LDS the sub-band may use.
+template <int TM, int TN, int WM, int WTM, int WTN, int BN, int LDSB, int NT>
+__device__ __forceinline__ void store_keep_pre(const f32x16 (&acc)[TM][TN], char *smem, int wm,
+                                               int wn, int lane, int tid, int64_t m0, int n0,
+                                               int64_t rows, int N, bf16 *Zg, bf16 *Cg) {
+  constexpr int ROWF = BN * 4 + 16;  // bytes per LDS row (fp32, padded)
+  constexpr int RB = WTM * ROWF <= LDSB ? WTM : (WTM / 2 * ROWF <= LDSB ? WTM / 2 : WTM / 4);
+  static_assert(RB >= 32 && RB % 32 == 0 && RB * ROWF <= LDSB && WTM % RB == 0, "sub-band");
+  constexpr int FPB = RB / 32;  // row fragments per sub-band
+  constexpr int OCPR = BN / 8;  // 8-wide chunks per row
+  for (int band = 0; band < WM; band++) {
+#pragma unroll
+    for (int h = 0; h < WTM / RB; h++) {
+      __syncthreads();  // stage buffers (or the previous sub-band) no longer read
+      if (wm == band) {
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+          if (i / FPB != h) continue;
+#pragma unroll
+          for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int R = (i - h * FPB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              const int Cc = wn * WTN + j * 32 + (lane & 31);
+              *(float *)(smem + R * ROWF + Cc * 4) = acc[i][j][r];
+            }
+        }
+      }
+      __syncthreads();
+      const int64_t r0 = m0 + band * WTM + h * RB;
+      const int64_t mrows = rows - r0 < RB ? rows - r0 : RB;
+      for (int idx = tid; idx < RB * OCPR; idx += NT) {
+        const int R = idx / OCPR, ch = idx - R * OCPR;
+        if (R < mrows) {
+          const f32x4 *src = (const f32x4 *)(smem + R * ROWF + ch * 32);
+          const f32x4 lo = src[0], hi = src[1];
+          bf16x8 z, c;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            z[q] = (bf16)lo[q];
+            z[4 + q] = (bf16)hi[q];
+            c[q] = (bf16)gelu_f(lo[q]);
+            c[4 + q] = (bf16)gelu_f(hi[q]);
+          }
+          *(bf16x8 *)(Zg + (r0 + R) * N + n0 + ch * 8) = z;
+          *(bf16x8 *)(Cg + (r0 + R) * N + n0 + ch * 8) = c;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // DMA-pipelined bf16 GEMM.  Both operands travel global -> LDS with gfx950's
 // global_load_lds_dwordx4 (each lane's 16 bytes land at M0 + 16 * lane), so no
 // registers stage the tiles and NS - 1 K steps can be in flight per block.
@@ -380,12 +438,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
-  // with the pre-activation output (GELU == 2) one pass writes the raw sums to
-  // Zpre first; then C (the GELU, if any, applied per element as it is
-  // written, so no second copy of the accumulators is ever live)
-  auto bands = [&](auto raw_tag) __attribute__((always_inline)) {
-    constexpr bool RAW = decltype(raw_tag)::value;
-    bf16 *Og = RAW ? Zg : Cg;
+  // (the GELU, if any, applied per element as it is written to LDS); with the
+  // pre-activation output (GELU == 2) the fp32 sums go through LDS instead
+  if constexpr (GELU == 2) {
+    store_keep_pre<TM, TN, WM, WTM, WTN, BN, NS * STAGE, 64 * W>(acc, smem, wm, wn, lane, tid, m0,
+                                                                  n0, rows, N, Zg, Cg);
+  } else {
     for (int band = 0; band < WM; band++) {
       __syncthreads();  // stage buffers (or the previous band) no longer read
       if (wm == band) {
@@ -398,7 +456,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
               const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
               const int Cc = wn * WTN + j * 32 + (lane & 31);
               float v = acc[i][j][r];
-              if (GELU && !RAW) v = gelu_f(v);
+              if (GELU) v = gelu_f(v);
               *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
             }
       }
@@ -408,15 +466,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
       for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
         const int R = idx / OCPR, ch = idx - R * OCPR;
         if (R < mrows)
-          *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+          *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
       }
     }
-  };
-  if constexpr (GELU == 2) {
-    bands(std::true_type{});
-    __builtin_amdgcn_sched_barrier(0);  // keep the two passes apart
   }
-  bands(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -594,12 +647,10 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
   constexpr int CROW = BN * 2 + 16;
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;
-  // with the pre-activation output (GELU == 2) one pass writes the raw sums to
-  // Zpre first; then C (the GELU, if any, applied per element as it is
-  // written, so no second copy of the accumulators is ever live)
-  auto bands = [&](auto raw_tag) __attribute__((always_inline)) {
-    constexpr bool RAW = decltype(raw_tag)::value;
-    bf16 *Og = RAW ? Zg : Cg;
+  if constexpr (GELU == 2) {  // with the pre-activation: fp32 sums through LDS
+    store_keep_pre<TM, TN, WM, WTM, WTN, BN, NS * STAGE, 64 * W>(acc, smem, wm, wn, lane, tid, m0,
+                                                                  n0, rows, N, Zg, Cg);
+  } else {
     for (int band = 0; band < WM; band++) {
       __syncthreads();
       if (wm == band) {
@@ -612,7 +663,7 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
               const int R = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
               const int Cc = wn * WTN + j * 32 + (lane & 31);
               float v = acc[i][j][r];
-              if (GELU && !RAW) v = gelu_f(v);
+              if (GELU) v = gelu_f(v);
               *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
             }
       }
@@ -622,15 +673,10 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
       for (int idx = tid; idx < WTM * OCPR; idx += 64 * W) {
         const int R = idx / OCPR, ch = idx - R * OCPR;
         if (R < mrows)
-          *(u32x4 *)(Og + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
+          *(u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8) = *(const u32x4 *)(smem + R * CROW + ch * 16);
       }
     }
-  };
-  if constexpr (GELU == 2) {
-    bands(std::true_type{});
-    __builtin_amdgcn_sched_barrier(0);  // keep the two passes apart
   }
-  bands(std::false_type{});
 }
 
 // One tile per workgroup, tiles laid over the XCDs as in gemm_dma_kernel.
@@ -870,6 +916,8 @@ static hipError_t launch_dma(const GemmArgs &a, int nt_b, int gelu, hipStream_t 
     if (a.b_packed)  // packed expert weights: streamed once, non-temporal
       return launch_dma_t<BM, BN, WM, WN, BK, NS, true, true>(
           a, epi_of(a, gelu), grid, block, intern_name(role, tile), s);
+  } else {
+    if (a.b_packed) return hipErrorInvalidValue;  // the packed layout is in 64-wide K steps
   }
   const char *name = intern_name(role, tile);
   if (nt_b)
@@ -965,9 +1013,8 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
     if (a.M_cap <= 128) {
       // 128x512, one K step in flight: the same 64 KB of weights in flight
       // as 128x256 with two, and 0.75 instead of 1 KB of LDS operand reads
-      // per MFMA.  Keeping the pre-activation spills at 256 VGPRs, so that
-      // form stays on 128x256.
-      if (a.N % 512 == 0 && epi_of(a, gelu) != 2)
+      // per MFMA
+      if (a.N % 512 == 0)
         return launch_dma<128, 512, 2, 4, 64, 2>(a, nt, gelu, s, role, "dma128x512");
       if (a.N % 256 == 0) return launch_dma<128, 256, 2, 4, 64, 3>(a, nt, gelu, s, role, "dma128x256");
     }
