@@ -81,6 +81,12 @@ SMALL = [
     W("skewed_int8_small", T=700, d=256, E=8, k=2, d_ff=512, capacity_factor=1.25,
       wfmt="int8", zipf_s=1.2),
     W("top3_bigE", T=333, d=128, E=200, k=3, d_ff=128, capacity_factor=2.0),
+    # degenerate routings: one expert (C = T, nothing dropped, gate 1), every
+    # token to every expert (k = E), the largest E and k the library takes
+    W("one_expert", T=100, d=128, E=1, k=1, d_ff=256, capacity_factor=1.0),
+    W("k_equals_E", T=90, d=128, E=4, k=4, d_ff=128, capacity_factor=1.0),
+    W("max_E_k_plain_gates", T=256, d=128, E=256, k=8, d_ff=128, capacity_factor=1.0,
+      normalize_topk=False),
 ]
 
 
