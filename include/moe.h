@@ -118,13 +118,18 @@ extern "C" {
 #define MOE_ENTRY_LAYER 4
 #define MOE_ENTRY_BACKWARD 5
 
+/* Sizes: with MOE_BF16 activations d, d_ff and (PR-MoE) d_ff_dense must be
+ * multiples of 64, and with int8 or packed expert weights d and d_ff
+ * multiples of 128; other values return MOE_ERR_UNSUPPORTED.  MOE_F32 takes
+ * any positive sizes. */
 typedef struct moe_config {
   int64_t T;          /* tokens (>= 0) */
-  int64_t d;          /* model dim (>= 1) */
+  int64_t d;          /* model dim (>= 1; bf16: a multiple of 64) */
   int64_t E;          /* experts, 1..256 */
   int64_t k;          /* experts per token, 1..min(E, 8) */
-  int64_t d_ff;       /* expert hidden dim (>= 1) */
-  int64_t d_ff_dense; /* PR-MoE dense MLP hidden dim (used when pr_moe) */
+  int64_t d_ff;       /* expert hidden dim (>= 1; bf16: a multiple of 64) */
+  int64_t d_ff_dense; /* PR-MoE dense MLP hidden dim (used when pr_moe;
+                         bf16: a multiple of 64) */
   double capacity_factor; /* > 0; C = min(T, ceil(k*T*cf/E)) */
   int64_t capacity;       /* > 0 overrides the formula (still clamped to T) */
   int32_t act_dtype;      /* MOE_F32 | MOE_BF16 */
