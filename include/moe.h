@@ -58,6 +58,12 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2) /* a valid configuration this build does not run */
 #define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
 #define MOE_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+#define MOE_ERR_SCRATCH (-5)     /* moe_layer_forward_noalloc: the configuration needs
+                                    more than MOE_NOALLOC_SCRATCH_BYTES of scratch */
+
+/* Size of the library's own per-device scratch array that
+ * moe_layer_forward_noalloc uses instead of a caller workspace (32 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* activation types */
 #define MOE_F32 0
@@ -288,6 +294,33 @@ int moe_combine(const moe_config *cfg, const void *y_disp,
 int moe_layer_forward(const moe_config *cfg, const void *x,
                       const moe_weights *w, moe_outputs *out, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* moe_layer_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * moe_layer_forward, except:
+ *   - out->x_disp, out->y_disp and out->h_disp (each [E, C, *]) are required,
+ *     and with pr_moe so are out->dense_out [T, d] and out->h_dense
+ *     [T, d_ff_dense]: the caller owns every large buffer;
+ *   - the remaining scratch (router partials, histograms, offsets, aux and
+ *     z-loss partials, gate-priority segments, the int8 XCD schedule, the
+ *     variant routers' scores) lives in the library's per-device array of
+ *     MOE_NOALLOC_SCRATCH_BYTES; a configuration that needs more returns
+ *     MOE_ERR_SCRATCH before anything is enqueued
+ *     (moe_layer_forward_noalloc_scratch_bytes tells how much it needs);
+ *   - the PR-MoE dense MLP runs in order on `stream` (overlap_dense is
+ *     ignored: no side stream or event is created).
+ * It calls no hipMalloc or hipFree and creates no stream or event (unless
+ * moe_profile_enable is on).  Every call on one GPU uses that GPU's one
+ * scratch array, which keeps the last call's contents: calls that overlap on
+ * one GPU (concurrent streams or threads) race and must be serialised by the
+ * caller; calls on different GPUs do not share it. */
+int moe_layer_forward_noalloc(const moe_config *cfg, const void *x,
+                              const moe_weights *w, moe_outputs *out,
+                              void *stream);
+/* Scratch bytes moe_layer_forward_noalloc needs for cfg (0 for an invalid
+ * configuration); it runs when this is <= MOE_NOALLOC_SCRATCH_BYTES. */
+size_t moe_layer_forward_noalloc_scratch_bytes(const moe_config *cfg);
 
 /* Backward of moe_layer_forward: the gradients of
  *   <dy, y> + g_aux * aux_loss + g_z * z_loss

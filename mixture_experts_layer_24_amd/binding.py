@@ -21,6 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 MOE_F32, MOE_BF16 = 0, 1
 MOE_W_PLAIN, MOE_W_INT8_G128, MOE_W_BF16_PACKED = 0, 1, 2
 WFMTS = {"plain": MOE_W_PLAIN, "int8": MOE_W_INT8_G128, "packed": MOE_W_BF16_PACKED}
@@ -31,7 +33,8 @@ ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER, ENTRY
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_ex", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_mlp", "moe_combine", "moe_layer_forward",
-            "moe_layer_backward", "moe_pack_expert_weights",
+            "moe_layer_backward", "moe_pack_expert_weights", "moe_layer_forward_noalloc",
+            "moe_layer_forward_noalloc_scratch_bytes",
             "moe_status_string", "moe_profile_enable", "moe_profile_filter", "moe_profile_reset",
             "moe_profile_read")
 
@@ -106,6 +109,11 @@ def lib():
             L.moe_layer_forward.restype = i32
             L.moe_layer_forward.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
                                             ctypes.POINTER(Outputs), vp, sz, vp]
+            L.moe_layer_forward_noalloc.restype = i32
+            L.moe_layer_forward_noalloc.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
+                                                    ctypes.POINTER(Outputs), vp]
+            L.moe_layer_forward_noalloc_scratch_bytes.restype = sz
+            L.moe_layer_forward_noalloc_scratch_bytes.argtypes = [cfgp]
             L.moe_route_ex.restype = i32
             L.moe_route_ex.argtypes = [cfgp, vp, ctypes.POINTER(Weights),
                                        ctypes.POINTER(Outputs), vp, sz, vp]
@@ -338,9 +346,11 @@ class LayerOutputs:
 def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
                   x_disp=False, y_disp=False, dense_out=False, z_loss=False,
                   saved_activations=False, importance_loss=False,
-                  load_loss=False) -> LayerOutputs:
+                  load_loss=False, hidden=False) -> LayerOutputs:
     """saved_activations: also keep the FFN hidden activations and their
-    pre-activations, which the backward then reads instead of recomputing."""
+    pre-activations, which the backward then reads instead of recomputing.
+    hidden: caller-owned hidden rows (h_disp, and h_dense for PR-MoE) without
+    the pre-activations."""
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     C = capacity(cfg)
     a = _act_dtype(cfg)
@@ -354,9 +364,10 @@ def alloc_outputs(cfg: Config, device="cuda", *, drop_mask=True, logits=False,
         x_disp=e(E, C, d) if x_disp else None, y_disp=e(E, C, d) if y_disp else None,
         dense_out=e(T, d) if (dense_out and cfg.pr_moe) else None,
         z_loss=e(1, dt=torch.float32) if z_loss else None,
-        h_disp=e(E, C, cfg.d_ff) if saved_activations else None,
+        h_disp=e(E, C, cfg.d_ff) if (saved_activations or hidden) else None,
         z_disp=e(E, C, cfg.d_ff) if saved_activations else None,
-        h_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None,
+        h_dense=(e(T, cfg.d_ff_dense) if ((saved_activations or hidden) and cfg.pr_moe)
+                 else None),
         z_dense=e(T, cfg.d_ff_dense) if (saved_activations and cfg.pr_moe) else None,
         importance_loss=e(1, dt=torch.float32) if importance_loss else None,
         load_loss=e(1, dt=torch.float32) if load_loss else None)
@@ -369,6 +380,21 @@ def moe_layer_forward(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None)
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), _ptr(x, (cfg.T, cfg.d), _act_dtype(cfg), "x"), ctypes.byref(W),
         ctypes.byref(O), wsp, wsn, _stream(stream)))
+
+
+def noalloc_scratch_bytes(cfg: Config) -> int:
+    """Scratch bytes moe_layer_forward_noalloc needs for cfg."""
+    return int(lib().moe_layer_forward_noalloc_scratch_bytes(ctypes.byref(cfg)))
+
+
+def moe_layer_forward_noalloc(cfg, x, weights: dict, out: LayerOutputs, stream=None):
+    """The layer without a workspace: out must hold x_disp, y_disp and h_disp
+    (and dense_out and h_dense for PR-MoE); the library's own per-device
+    scratch holds the rest."""
+    W, O = _weights_struct(cfg, weights), _outputs_struct(cfg, out)
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(cfg), _ptr(x, (cfg.T, cfg.d), _act_dtype(cfg), "x"), ctypes.byref(W),
+        ctypes.byref(O), _stream(stream)))
 
 
 def moe_route_ex(cfg, x, weights: dict, out: LayerOutputs, ws, stream=None):

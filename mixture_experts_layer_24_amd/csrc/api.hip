@@ -91,6 +91,9 @@ struct Layout {
   size_t dg, fcnt, ecount, dlog, dlog16, dY, Z, H, dZ, dX, dxr, Zd, Hd, dZd, dxd;
 };
 
+// layout() selector of the allocation-free layer forward (not a C ABI entry)
+constexpr int kEntryLayerScratch = 100;
+
 int64_t padded_experts(const moe_config *c) { return (c->E + 7) / 8 * 8; }
 
 // int8 expert GEMMs on 256-row tiles with enough experts to balance: their
@@ -162,7 +165,11 @@ Layout layout(const moe_config *c, int entry) {
       break;
     case MOE_ENTRY_COMBINE:
       break;
-    case MOE_ENTRY_LAYER: {
+    case MOE_ENTRY_LAYER:
+    case kEntryLayerScratch: {
+      // kEntryLayerScratch: the allocation-free layer, whose caller gives
+      // x_disp, y_disp, the hidden rows and (PR-MoE) D(x) and its hidden
+      const bool big = entry == MOE_ENTRY_LAYER;
       L.qsum = take(blkE);
       L.fcount = take(blkE);
       L.hist = take(blkE);
@@ -171,12 +178,14 @@ Layout layout(const moe_config *c, int entry) {
       L.zpart = take((size_t)nblk * 4);
       take_variant();
       if (gp) L.seg = take(segB);
-      L.x_disp = take((size_t)c->E * C * c->d * as);
-      L.y_disp = take((size_t)c->E * C * c->d * as);
-      L.hidden = take((size_t)c->E * C * c->d_ff * as);
-      if (c->pr_moe) {
-        L.hidden_dense = take((size_t)c->T * c->d_ff_dense * as);
-        L.dense = take((size_t)c->T * c->d * as);
+      if (big) {
+        L.x_disp = take((size_t)c->E * C * c->d * as);
+        L.y_disp = take((size_t)c->E * C * c->d * as);
+        L.hidden = take((size_t)c->E * C * c->d_ff * as);
+        if (c->pr_moe) {
+          L.hidden_dense = take((size_t)c->T * c->d_ff_dense * as);
+          L.dense = take((size_t)c->T * c->d * as);
+        }
       }
       if (sched_experts(c)) L.xsched = take(sched_bytes(c));
       break;
@@ -436,6 +445,39 @@ void prof_end(hipStream_t s) {
 }
 }  // namespace moe_host
 
+// ---- scratch of the allocation-free layer forward
+// Per-device scratch of moe_layer_forward_noalloc: a file-scope device array
+// of MOE_NOALLOC_SCRATCH_BYTES (each GPU the library runs on holds its own
+// copy until the process ends).  Host code never passes `scratch` itself to a
+// kernel (on the host it only names the symbol); it uses the device address
+// that hipGetSymbolAddress returns, taken once per device on that device's
+// first call and kept in g_scratch_ptr.  Nothing in it needs to start at
+// zero: every kernel writes the scratch it reads earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int64_t moe_capacity(const moe_config *cfg) {
@@ -611,12 +653,11 @@ static hipError_t side_stream(SideStream **out) {
   return hipSuccess;
 }
 
-int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w,
-                      moe_outputs *out, void *ws, size_t ws_bytes, void *stream) {
-  int rc = check_config(cfg);
-  if (rc != MOE_OK) return rc;
+// argument checks of the layer forward (both entry points)
+static int check_layer_args(const moe_config *cfg, const void *x, const moe_weights *w,
+                     const moe_outputs *out) {
   if (!w || !out) return MOE_ERR_INVALID_ARG;
-  const int64_t T = cfg->T, Tk = T * cfg->k, rowsE = cfg->E * capacity_of(cfg);
+  const int64_t T = cfg->T, Tk = T * cfg->k;
   const bool q8 = cfg->expert_wfmt == MOE_W_INT8_G128;
   if (!need(x, T, 16) || !router_weights_ok(cfg, w) || !need(w->w1, 1, 16) ||
       !need(w->w2, 1, 16))
@@ -632,11 +673,16 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
       !opt(out->z_loss, 4) || !opt(out->h_disp, 16) || !opt(out->z_disp, 16) ||
       !opt(out->h_dense, 16) || !opt(out->z_dense, 16) || !loss_outputs_ok(cfg, out))
     return MOE_ERR_INVALID_ARG;
-  (void)rowsE;
-  rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
-  if (rc != MOE_OK) return rc;
-  const Layout L = layout(cfg, MOE_ENTRY_LAYER);
-  hipStream_t s = (hipStream_t)stream;
+  return MOE_OK;
+}
+
+// the layer's launch sequence; `L` places the scratch in `ws` (the buffers
+// the caller gives in `out` are not taken from it); side_ok: PR-MoE may run
+// the dense MLP on the side stream (cfg->overlap_dense)
+static hipError_t layer_forward_launch(const moe_config *cfg, const void *x, const moe_weights *w,
+                                moe_outputs *out, void *ws, const Layout &L, hipStream_t s,
+                                bool side_ok) {
+  const int64_t T = cfg->T;
   float *qsum = (float *)at(ws, L.qsum);
   int32_t *fcount = (int32_t *)at(ws, L.fcount), *hist = (int32_t *)at(ws, L.hist);
   int32_t *offs = (int32_t *)at(ws, L.offs);
@@ -654,7 +700,7 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
   // fork: the dense MLP on the side stream
   std::unique_lock<std::mutex> side_lock;
   SideStream *side = nullptr;
-  if (cfg->pr_moe && cfg->overlap_dense && T > 0) {
+  if (cfg->pr_moe && cfg->overlap_dense && side_ok && T > 0) {
     side_lock = std::unique_lock<std::mutex>(g_side_mu);
     e = side_stream(&side);
     if (e == hipSuccess) e = hipEventRecord(side->fork, s);
@@ -689,7 +735,45 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
                                  cfg->add_skip ? x : nullptr, dense, out->y, T, (int)cfg->d,
                                  (int)cfg->k, capacity_of(cfg), (int)cfg->E,
                                  cfg->act_dtype == MOE_BF16, s);
-  return hip_status(e);
+  return e;
+}
+
+int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w,
+                      moe_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  rc = check_layer_args(cfg, x, w, out);
+  if (rc != MOE_OK) return rc;
+  rc = check_ws(cfg, MOE_ENTRY_LAYER, ws, ws_bytes);
+  if (rc != MOE_OK) return rc;
+  return hip_status(layer_forward_launch(cfg, x, w, out, ws, layout(cfg, MOE_ENTRY_LAYER),
+                                         (hipStream_t)stream, true));
+}
+
+size_t moe_layer_forward_noalloc_scratch_bytes(const moe_config *cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return layout(cfg, kEntryLayerScratch).total;
+}
+
+int moe_layer_forward_noalloc(const moe_config *cfg, const void *x, const moe_weights *w,
+                              moe_outputs *out, void *stream) {
+  int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  rc = check_layer_args(cfg, x, w, out);
+  if (rc != MOE_OK) return rc;
+  const int64_t C = capacity_of(cfg);
+  const bool rows = cfg->E * C > 0;
+  if (!need(out->x_disp, rows, 16) || !need(out->y_disp, rows, 16) ||
+      !need(out->h_disp, rows, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->pr_moe && (!need(out->dense_out, cfg->T, 16) || !need(out->h_dense, cfg->T, 16)))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(cfg, kEntryLayerScratch);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void *ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(layer_forward_launch(cfg, x, w, out, ws, L, (hipStream_t)stream, false));
 }
 
 int moe_layer_backward(const moe_config *cfg, const void *x, const moe_weights *w,
@@ -855,6 +939,8 @@ const char *moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH:
+      return "configuration needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert binding.status_string(s) not in ("", "unknown status")
     assert binding.status_string(-99) == "unknown status"
 
@@ -254,3 +254,50 @@ def test_backward_rejects_packed_weights(L):
     rc = L.moe_layer_backward(ctypes.byref(cfg), ok, ctypes.byref(w), ctypes.byref(f), ok, 0.0,
                               0.0, ctypes.byref(g), ok, 1 << 40, None)
     assert rc == binding.MOE_ERR_UNSUPPORTED
+
+
+def _fake_outputs(ok, **nulls):
+    # the loss outputs stay NULL: they need their loss weights
+    nulls = dict(nulls, importance_loss=1, load_loss=1)
+    names = [f[0] for f in binding.Outputs._fields_]
+    return binding.Outputs(**{n: (None if n in nulls else ok) for n in names})
+
+
+def test_noalloc_scratch_bounds(L):
+    # every workload (and the variant routers at its shape) fits the scratch
+    for wl in workloads.WORKLOADS.values():
+        for over in ({}, dict(drop_policy="gate_priority"),
+                     dict(router="noisy_topk", w_importance=1.0, w_load=1.0),
+                     dict(router="cosine", cos_tau=0.1, cos_dim=64)):
+            if over.get("router") == "noisy_topk" and wl.E > 128:
+                continue
+            cfg = binding.config_of(wl, **over)
+            need = binding.noalloc_scratch_bytes(cfg)
+            assert 0 < need <= binding.NOALLOC_SCRATCH_BYTES, (wl.name, over, need)
+            # none of the caller-owned buffers is counted
+            assert need < binding.workspace_bytes(cfg, binding.ENTRY_LAYER)
+    assert binding.status_string(binding.MOE_ERR_SCRATCH) not in ("", "unknown status")
+
+
+def test_noalloc_rejections_before_launch(L):
+    ok = 1 << 20
+    W = binding.Weights(w_router=ok, w1=ok, w2=ok, wm1=ok, wm2=ok)
+    cfg = binding.make_config(T=64, d=128, E=4, k=1, d_ff=128, d_ff_dense=128, pr_moe=True)
+    f = L.moe_layer_forward_noalloc
+    # every caller-owned large buffer is required
+    for n in ("x_disp", "y_disp", "h_disp", "dense_out", "h_dense"):
+        O = _fake_outputs(ok, **{n: 1})
+        assert f(ctypes.byref(cfg), ok, ctypes.byref(W), ctypes.byref(O), None) == \
+            binding.MOE_ERR_INVALID_ARG, n
+    # a configuration whose scratch exceeds the array: 2^20 tokens over 256
+    # experts needs 4 x 16 MiB of per-block router and dispatch partials
+    big = binding.make_config(T=1 << 20, d=128, E=256, k=1, d_ff=128)
+    assert binding.noalloc_scratch_bytes(big) > binding.NOALLOC_SCRATCH_BYTES
+    O = _fake_outputs(ok)
+    assert f(ctypes.byref(big), ok, ctypes.byref(W), ctypes.byref(O), None) == \
+        binding.MOE_ERR_SCRATCH
+    # invalid configuration: no scratch size, invalid-argument status
+    bad = binding.make_config(T=64, d=128, E=4, k=5, d_ff=128)
+    assert binding.noalloc_scratch_bytes(bad) == 0
+    assert f(ctypes.byref(bad), ok, ctypes.byref(W), ctypes.byref(O), None) == \
+        binding.MOE_ERR_INVALID_ARG
