@@ -82,3 +82,99 @@ def valid_token_order_dispatch(ids, slots, load, kept, C, E):
             n[e] += 1
     assert np.array_equal(np.asarray(load), n)
     assert np.array_equal(np.asarray(kept), np.minimum(n, C))
+
+
+def oracle_rows_by_expert(x, inp, want):
+    """{e: [token, ...]} -> {e: fp64 [n, d]}: the oracle's expert FFN of the
+    rows x[token] through expert e.  x is a CPU tensor; each expert's
+    weights (and int8 scales) are moved to the CPU once."""
+    import oracle
+    out = {}
+    s1, s2 = inp.get("w1_scale"), inp.get("w2_scale")
+    for e, toks in want.items():
+        if len(toks) == 0:
+            continue
+        out[e] = oracle.ffn_rows(x[list(toks)], inp["w1"][e].cpu(), inp["w2"][e].cpu(),
+                                 None if s1 is None else s1[e].cpu(),
+                                 None if s2 is None else s2[e].cpu())
+    return out
+
+
+def check_expert_terms(wl, x, inp, ids, slots, gates, y_disp, m, y, tokens, dense=None,
+                       tag=""):
+    """Element-by-element checks of the expert term on `tokens` under the
+    routing (ids, slots, gates: numpy [T, k]) the layer used:
+      y_disp[ids[t,j], slots[t,j]] against the oracle FFN of x[t] through
+      expert ids[t,j], for every kept (t, j);
+      M[t] = sum over kept j of gates[t,j] E_j(x[t])  (the layer's
+      moe_combine without bases, `m`);
+      y[t] = [x[t]] + [D(x[t])] + M[t]   (dense: fp64 D rows of `tokens`).
+    The bound is the workload's tolerance relative to the largest reference
+    value of each quantity, so a zeroed or misplaced expert term fails it
+    although y's residual is much larger."""
+    import oracle
+    tau = TAU[wl.act]
+    tokens = np.asarray(sorted(set(int(t) for t in tokens)), np.int64)
+    n, k = len(tokens), ids.shape[1]
+    sl, ii, gg = slots[tokens], ids[tokens], np.asarray(gates, np.float64)[tokens]
+    want = {}
+    for a, t in enumerate(tokens):
+        for j in range(k):
+            if sl[a, j] >= 0:
+                want.setdefault(int(ii[a, j]), []).append(int(t))
+    rows = oracle_rows_by_expert(x, inp, want)
+    eo = np.zeros((n, k, wl.d))
+    used = {e: 0 for e in want}
+    ei, si, at = [], [], []
+    for a in range(n):
+        for j in range(k):
+            if sl[a, j] >= 0:
+                e = int(ii[a, j])
+                eo[a, j] = rows[e][used[e]]
+                used[e] += 1
+                ei.append(e)
+                si.append(int(sl[a, j]))
+                at.append((a, j))
+    if ei:
+        got = to_np(y_disp[torch.as_tensor(ei, device=y_disp.device),
+                           torch.as_tensor(si, device=y_disp.device)])
+        ref = np.stack([eo[a, j] for a, j in at])
+        check_close(f"y_disp{tag}", got, ref, tau)
+    base = np.zeros((n, wl.d))
+    if wl.add_skip:
+        base += to_np(x[torch.as_tensor(tokens)]).astype(np.float64)
+    if dense is not None:
+        base += dense
+    yref, mref = oracle.combine(sl, gg, eo, base)
+    tdev = torch.as_tensor(tokens, device=m.device)
+    err_m = check_close(f"M{tag}", m[tdev], mref, tau)
+    check_close(f"y{tag}", y[tdev], yref, tau)
+    return err_m, len(ei)
+
+
+GUARD_BYTES = 256
+CANARY = 0xA5
+
+
+def guard_outputs(out):
+    """Replace every tensor of a LayerOutputs by one of the same shape and
+    type that sits at the start of a larger buffer whose last GUARD_BYTES are
+    a canary; returns a function that asserts no canary byte changed (a
+    kernel wrote past the end of an output)."""
+    import dataclasses
+    guards = []
+    for f in dataclasses.fields(out):
+        t = getattr(out, f.name)
+        if not isinstance(t, torch.Tensor):
+            continue
+        n = t.numel() * t.element_size()
+        raw = torch.empty(n + GUARD_BYTES, dtype=torch.uint8, device=t.device)
+        raw[n:].fill_(CANARY)
+        setattr(out, f.name, raw[:n].view(t.dtype).view(t.shape))
+        guards.append((f.name, raw, n))
+
+    def check():
+        for name, raw, n in guards:
+            tail = raw[n:]
+            assert bool((tail == CANARY).all()), f"{name}: bytes written past the end"
+    return check

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 from mixture_experts_layer_24_amd import binding, synth, workloads
-from parity_util import (TAU, check_close, check_ids, to_np,
-                         valid_token_order_dispatch)
+from parity_util import (TAU, check_close, check_expert_terms, check_ids, guard_outputs,
+                         oracle_rows_by_expert, to_np, valid_token_order_dispatch)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +29,13 @@ def _run_layer(wl, inp, overlap_dense=True, **alloc):
     cfg = binding.config_of(wl, overlap_dense=overlap_dense)
     out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=True, y_disp=True,
                                 dense_out=True, **alloc)
+    check_guards = guard_outputs(out)  # canaries past the end of every output
     ws = binding.alloc_workspace(cfg)
     binding.moe_layer_forward(cfg, inp["x"], inp, out, ws)
     m = torch.empty_like(out.y)
     binding.moe_combine(cfg, out.y_disp, out.expert_ids, out.slots, out.gates, None, None, m)
     torch.cuda.synchronize()
+    check_guards()
     return cfg, out, m
 
 
@@ -443,43 +445,34 @@ def test_full_size_layer_sampled(name):
     tau = TAU[wl.act]
     rng = np.random.default_rng(0)
     inv = _inverse(ref["ids"], ref["slots"], wl.E)
-    xd, yd = out.x_disp, out.y_disp
-    # sampled expert rows (first, last and random kept slots of a few experts)
-    active = [e for e in range(wl.E) if inv[e]]
-    for e in rng.choice(active, size=min(3, len(active)), replace=False):
-        rows = inv[e]
-        pick = sorted({0, len(rows) - 1, *rng.integers(0, len(rows), size=6).tolist()})
-        slots_e = [rows[i][0] for i in pick]
-        toks = [rows[i][1] for i in pick]
-        assert torch.equal(xd[e, slots_e].cpu(), x[toks])
-        s1 = None if inp["w1_scale"] is None else inp["w1_scale"][e].cpu()
-        s2 = None if inp["w2_scale"] is None else inp["w2_scale"][e].cpu()
-        o = oracle.ffn_rows(x[toks], inp["w1"][e].cpu(), inp["w2"][e].cpu(), s1, s2)
-        check_close(f"y_disp[{e}]", yd[e, slots_e], o, tau)
-    # sampled tokens: M, D and y
-    toks = sorted(set(rng.choice(wl.T, size=min(8, wl.T), replace=False).tolist()))
-    eo = np.zeros((len(toks), wl.k, wl.d))
-    need = {}
-    for i, t in enumerate(toks):
-        for j in range(wl.k):
-            if ref["slots"][t, j] >= 0:
-                need.setdefault(int(ref["ids"][t, j]), []).append((i, j, t))
-    for e, lst in need.items():
-        s1 = None if inp["w1_scale"] is None else inp["w1_scale"][e].cpu()
-        s2 = None if inp["w2_scale"] is None else inp["w2_scale"][e].cpu()
-        o = oracle.ffn_rows(x[[t for _, _, t in lst]], inp["w1"][e].cpu(), inp["w2"][e].cpu(),
-                            s1, s2)
-        for (i, j, _), row in zip(lst, o):
-            eo[i, j] = row
-    base = np.zeros((len(toks), wl.d))
-    if wl.add_skip:
-        base += x[toks].double().numpy()
+    xd = out.x_disp
+    # the first and last kept row of every active expert: the gather is an
+    # exact copy, the expert rows match the oracle's FFN of those tokens
+    want, where = {}, []
+    for e in range(wl.E):
+        if inv[e]:
+            ends = sorted({0, len(inv[e]) - 1})
+            for i in ends:
+                s_, t_, _ = inv[e][i]
+                want.setdefault(e, []).append(t_)
+                where.append((e, s_, t_))
+    es = torch.as_tensor([w[0] for w in where], device=DEV)
+    ss = torch.as_tensor([w[1] for w in where], device=DEV)
+    assert torch.equal(xd[es, ss].cpu(), x[[w[2] for w in where]])
+    rows = oracle_rows_by_expert(x, inp, want)
+    ref_rows = np.concatenate([rows[e] for e in sorted(rows)])
+    check_close("y_disp (first/last kept row of every expert)", out.y_disp[es, ss], ref_rows,
+                tau)
+    print(f"  {len(where)} expert rows over {len(rows)} active experts", flush=True)
+    # 64 sampled tokens: every kept expert row of theirs, M, D and y
+    toks = np.sort(rng.choice(wl.T, size=min(64, wl.T), replace=False))
+    dref = None
     if wl.pr_moe:
-        dref = oracle.ffn_rows(x[toks], inp["wm1"].cpu(), inp["wm2"].cpu())
-        check_close("D", out.dense_out[toks], dref, tau)
-        base += dref
-    yref, mref = oracle.combine(ref["slots"][toks], ref["gates"][toks], eo, base)
-    check_close("M", m[toks], mref, tau)
-    check_close("y", out.y[toks], yref, tau)
+        dref = oracle.ffn_rows(x[torch.as_tensor(toks)], inp["wm1"].cpu(), inp["wm2"].cpu())
+        check_close("D", out.dense_out[torch.as_tensor(toks, device=DEV)], dref, tau)
+    err_m, n_rows = check_expert_terms(wl, x, inp, ref["ids"], ref["slots"], ref["gates"],
+                                       out.y_disp, m, out.y, toks, dense=dref)
+    print(f"  {len(toks)} tokens, {n_rows} of their rows kept; M rel err {err_m:.2e}",
+          flush=True)
     del inp, out, m
     torch.cuda.empty_cache()

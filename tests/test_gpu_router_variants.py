@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from mixture_experts_layer_24_amd import binding, synth, workloads
-from parity_util import TAU, check_close, to_np, valid_token_order_dispatch
+from parity_util import (TAU, check_close, check_expert_terms, guard_outputs, to_np,
+                         valid_token_order_dispatch)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -115,9 +116,14 @@ def test_route_ex_matches_oracle(name, wl, router, params):
 def test_layer_with_router_variant(name, wl, router, params):
     print(f"[layer] {name}", flush=True)
     inp, cfg = _setup(wl, router, params, seed=3)
-    out = binding.alloc_outputs(cfg, DEV, logits=True, importance_loss=True, load_loss=True)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, importance_loss=True, load_loss=True,
+                                y_disp=True)
+    check_guards = guard_outputs(out)
     binding.moe_layer_forward(cfg, inp["x"].to(DEV), _dev(inp), out, binding.alloc_workspace(cfg))
+    m = torch.empty_like(out.y)  # the expert term alone: combine without bases
+    binding.moe_combine(cfg, out.y_disp, out.expert_ids, out.slots, out.gates, None, None, m)
     torch.cuda.synchronize()
+    check_guards()
     w = inp["w_proj"] if router == "cosine" else inp["w_router"]
     ref = oracle.layer_forward(
         inp["x"], w, inp["w1"], inp["w2"], k=wl.k, capacity_factor=wl.capacity_factor,
@@ -135,10 +141,17 @@ def test_layer_with_router_variant(name, wl, router, params):
         assert np.array_equal(to_np(out.drop_mask), ref["drop"])
         assert np.array_equal(to_np(out.load), ref["load"])
         assert np.array_equal(to_np(out.kept), ref["kept"])
+        check_close("M", m, ref["m"], TAU[wl.act])
         check_close("y", out.y, ref["y"], TAU[wl.act])
+        gates = ref["gates"]
     else:
         valid_token_order_dispatch(ids, to_np(out.slots), to_np(out.load), to_np(out.kept), C,
                                    wl.E)
+        gates = to_np(out.gates).astype(np.float64)
+    # every kept row, M and y element by element under the routing the layer
+    # used (the oracle's own unless an undecidable token flipped)
+    check_expert_terms(wl, inp["x"], inp, ids, to_np(out.slots), gates, out.y_disp, m, out.y,
+                       np.arange(wl.T))
     # an unused TopP slot is no assignment: not kept, not dropped
     unused = ids < 0
     assert (to_np(out.slots)[unused] == -1).all() and (to_np(out.drop_mask)[unused] == 0).all()
@@ -156,8 +169,11 @@ def test_full_size_layer_with_router_variant(router, params):
     inp.update(synth.router_inputs(wl, router, seed=0, device=DEV,
                                    cos_dim=params.get("cos_dim", 64)))
     cfg = binding.config_of(wl, router=router, w_importance=0.01, w_load=0.01, **params)
-    out = binding.alloc_outputs(cfg, DEV, logits=True, importance_loss=True, load_loss=True)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, importance_loss=True, load_loss=True,
+                                y_disp=True, dense_out=True)
     binding.moe_layer_forward(cfg, inp["x"], inp, out, binding.alloc_workspace(cfg))
+    m = torch.empty_like(out.y)
+    binding.moe_combine(cfg, out.y_disp, out.expert_ids, out.slots, out.gates, None, None, m)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(1).choice(wl.T, 256, replace=False))
     cpu = {n: (None if v is None else v.cpu()) for n, v in inp.items()}
@@ -177,6 +193,14 @@ def test_full_size_layer_with_router_variant(router, params):
     valid_token_order_dispatch(to_np(out.expert_ids), to_np(out.slots), to_np(out.load),
                                to_np(out.kept), binding.capacity(cfg), wl.E)
     assert torch.isfinite(out.y).all()
+    # expert rows, M, D and y on 64 of the sampled tokens under the layer's
+    # own routing and fp32 gates
+    toks = rows[:64]
+    dref = oracle.ffn_rows(cpu["x"][toks], cpu["wm1"], cpu["wm2"])
+    check_close("D", out.dense_out[torch.as_tensor(toks, device=DEV)], dref, TAU[wl.act])
+    check_expert_terms(wl, cpu["x"], cpu, to_np(out.expert_ids), to_np(out.slots),
+                       to_np(out.gates).astype(np.float64), out.y_disp, m, out.y, toks,
+                       dense=dref)
     for t in (out.importance_loss, out.load_loss):
         assert np.isfinite(float(to_np(t)[0]))
     del inp, cpu, out

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from mixture_experts_layer_24_amd import binding, synth, workloads
-from parity_util import TAU, check_close, check_ids, to_np
+from parity_util import TAU, check_close, check_expert_terms, guard_outputs, check_ids, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -127,8 +127,12 @@ def test_gate_priority_layer(wl):
     dinp = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     cfg = binding.config_of(wl, drop_policy="gate_priority")
     out = binding.alloc_outputs(cfg, DEV, logits=True, y_disp=True, dense_out=True, z_loss=True)
+    check_guards = guard_outputs(out)
     binding.moe_layer_forward(cfg, dinp["x"], dinp, out, binding.alloc_workspace(cfg))
+    m = torch.empty_like(out.y)  # the expert term alone: combine without bases
+    binding.moe_combine(cfg, out.y_disp, out.expert_ids, out.slots, out.gates, None, None, m)
     torch.cuda.synchronize()
+    check_guards()
     C = binding.capacity(cfg)
     ref = oracle.layer_forward(
         inp["x"], inp["w_router"], inp["w1"], inp["w2"], k=wl.k,
@@ -145,24 +149,19 @@ def test_gate_priority_layer(wl):
     assert np.array_equal(to_np(out.drop_mask), rep["drop"])
     assert np.array_equal(to_np(out.kept), rep["kept"])
     assert float(out.z_loss.item()) == pytest.approx(oracle.z_loss(ref["logits"]), rel=2e-5)
-    if np.array_equal(rep["slots"], ref["slots"]):  # same decisions as the fp64 oracle
-        check_close("y", out.y, ref["y"], TAU[wl.act])
-    else:
-        print(f"[{wl.name}] fp32 and fp64 gate orders differ; y compared on the replay only")
-        # y from the oracle's FFN and combine on the GPU's routing
-        yd = to_np(out.y_disp)
-        mask = rep["slots"] >= 0
-        rows = np.zeros((wl.T, wl.k, wl.d))
-        for t, j in zip(*np.nonzero(mask)):
-            e = ids[t, j]
-            s1 = None if inp["w1_scale"] is None else inp["w1_scale"][e]
-            s2 = None if inp["w2_scale"] is None else inp["w2_scale"][e]
-            rows[t, j] = oracle.ffn_rows(inp["x"][t:t + 1], inp["w1"][e], inp["w2"][e],
-                                         s1, s2)[0]
-        got = np.zeros_like(rows)
-        for t, j in zip(*np.nonzero(mask)):
-            got[t, j] = yd[ids[t, j], rep["slots"][t, j]]
-        check_close("y_disp", got[mask], rows[mask], TAU[wl.act])
+    if not np.array_equal(rep["slots"], ref["slots"]):
+        print(f"[{wl.name}] fp32 and fp64 gate orders differ; expert terms compared on the "
+              "replay")
+    # every kept row, M and y, element by element, under the routing the
+    # layer used (equal to the oracle's own when the gate orders agree)
+    tau = TAU[wl.act]
+    if wl.pr_moe:
+        check_close("D", out.dense_out, ref["dense"], tau)
+    check_expert_terms(wl, inp["x"], inp, ids, rep["slots"], ref["gates"], out.y_disp, m,
+                       out.y, np.arange(wl.T), dense=ref["dense"] if wl.pr_moe else None)
+    if np.array_equal(rep["slots"], ref["slots"]):
+        check_close("M", m, ref["m"], tau)
+        check_close("y", out.y, ref["y"], tau)
 
 
 @pytest.mark.parametrize("name", ["prmoe128_1p3b", "skewed_top2_int8"])
