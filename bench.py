@@ -1,6 +1,6 @@
 """Benchmark: MoE-layer forward tokens/s on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--headline-only]
                     [--no-cpu-baseline] [--copy-calibration GIB]
                     [--backward | --train] [--recompute]
     python bench.py --pmc-summary FETCH.csv WRITE.csv --label L --symbol RE
@@ -12,8 +12,11 @@ tokens already resident in HBM (--backward: one moe_layer_backward of that
 forward; --train: forward keeping the FFN activations, then the backward).
 The default workload is the 1.3B+PR-MoE-128
 layer (T=16384, d=2048, E=128 top-1 experts with d_ff=8192 plus a dense MLP
-with d_ff=8192, bf16); the other workloads are parity cases and can be timed
-with --workload.  One JSON line is printed:
+with d_ff=8192, bf16); its record is the top level of the JSON line.  Without
+--workload (and without a variant flag) the other four workloads -- the tiny
+fp32 layer, the 350M+MoE-128 layer, the decode layer and the skewed int8
+layer -- are measured the same way and reported under "workloads" (their own
+records, not part of "value").  One JSON line is printed:
 
   value      whole-job tokens/s over the K timed steps (host clock around
              device-synchronised steps)
@@ -25,6 +28,11 @@ with --workload.  One JSON line is printed:
              events there); traffic = HBM bytes per launch from the committed
              rocprofv3 counter summary when it was taken on the current kernel
              source, else null
+  layer      the whole layer's algorithmic FLOPs and HBM bytes per step
+             (hidden rows excluded) against the bf16 MFMA and HBM peaks
+  routing    assignments, drops, expert load and kept extremes, near-tie
+             tokens (k-th and (k+1)-th fp32 logits within 1e-5) and whether
+             the expert ids equal the oracle's on every other token
   kernels    per-kernel mean launch times from the survey steps
   cold_cache steps timed one by one after a 512 MiB read that evicts the
              Infinity Cache (the timed steps above run back to back, so inputs
@@ -68,7 +76,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="target CPU time of the oracle sample")
+                   help="target CPU time of the oracle sample (headline workload)")
+    p.add_argument("--sub-cpu-seconds", type=float, default=6.0,
+                   help="target CPU time of the oracle sample of each other workload")
+    p.add_argument("--headline-only", action="store_true",
+                   help="skip the sub-records of the other four workloads")
     p.add_argument("--drop-policy", default="token_order", choices=["token_order", "gate_priority"])
     p.add_argument("--z-loss", action="store_true", help="also compute the router z-loss")
     p.add_argument("--backward", action="store_true",
@@ -108,10 +120,11 @@ def parse():
 def kernel_work(wl, kept, cfg_C, router="topk", cos_dim=64):
     """Algorithmic bytes and FLOPs of one launch of each kernel class.
 
-    Expert GEMM1: reads the weights of experts with >= 1 kept row once, reads
-    the kept rows of x_disp, writes the kept rows of H; FLOPs 2*N_kept*d*d_ff.
-    Expert GEMM2: weights of active experts, kept rows of H in, kept rows of
-    y_disp out; FLOPs 2*N_kept*d_ff*d.  Dense GEMM1/2: x, Wm1, Hd / Hd, Wm2,
+    Expert GEMM1: reads the weights of experts with >= 1 kept row once and
+    the kept rows of x_disp; FLOPs 2*N_kept*d*d_ff.  Expert GEMM2: weights of
+    active experts, kept rows of y_disp out; FLOPs 2*N_kept*d_ff*d.  The
+    hidden rows H are excluded (they can stay on chip; this build writes and
+    reads them, reported as h_bytes).  Dense GEMM1/2: x, Wm1, Hd / Hd, Wm2,
     D; FLOPs 2*T*d*d_ff_dense each.  int8 weights count 1 byte plus 2 bytes
     of scale per 128.
     """
@@ -122,11 +135,14 @@ def kernel_work(wl, kept, cfg_C, router="topk", cos_dim=64):
         wbytes = n_act * wl.d * wl.d_ff * (1 + 2 / 128)
     else:
         wbytes = n_act * wl.d * wl.d_ff * sa
+    # the hidden rows H (written by GEMM1, read by GEMM2) are not counted:
+    # the method need not send them to HBM; h_bytes reports them apart
+    h = n_kept * wl.d_ff * sa
     out = {
-        "expert_gemm1": dict(bytes=wbytes + n_kept * (wl.d + wl.d_ff) * sa,
-                             flops=2.0 * n_kept * wl.d * wl.d_ff),
-        "expert_gemm2": dict(bytes=wbytes + n_kept * (wl.d_ff + wl.d) * sa,
-                             flops=2.0 * n_kept * wl.d_ff * wl.d),
+        "expert_gemm1": dict(bytes=wbytes + n_kept * wl.d * sa,
+                             flops=2.0 * n_kept * wl.d * wl.d_ff, h_bytes=h),
+        "expert_gemm2": dict(bytes=wbytes + n_kept * wl.d * sa,
+                             flops=2.0 * n_kept * wl.d_ff * wl.d, h_bytes=h),
     }
     if wl.pr_moe:
         T, d, F = wl.T, wl.d, wl.d_ff_dense
@@ -165,6 +181,29 @@ def kernel_work(wl, kept, cfg_C, router="topk", cos_dim=64):
     out["combine"] = dict(bytes=(n_kept + wl.T * (1 + int(wl.add_skip) + int(wl.pr_moe)))
                           * wl.d * sa, flops=2.0 * n_kept * wl.d)
     return out
+
+
+def layer_work(wl, kept):
+    """Algorithmic FLOPs and HBM bytes of one whole layer call: the router
+    reads x once and W_r; the active experts' weights are read once (int8: 1
+    byte + 2 bytes of scale per 128); the gather reads and writes the kept
+    rows; the expert GEMMs read x_disp and write y_disp; the combine reads the
+    kept expert rows and the base terms and writes y; PR-MoE adds its dense
+    weights and D; ids/gates/slots/drop mask are written once.  The hidden
+    rows of the experts and of the dense MLP are excluded."""
+    sa = 4 if wl.act == "f32" else 2
+    n_kept = int(sum(kept))
+    n_act = int(sum(1 for v in kept if v > 0))
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.d_ff
+    sw = (1 + 2 / 128) if wl.wfmt == "int8" else sa
+    flops = 2.0 * T * d * E + 4.0 * n_kept * d * F + 2.0 * n_kept * d
+    byt = (sa * T * d + sa * E * d + sw * n_act * 2 * d * F + 2 * sa * n_kept * d
+           + 2 * sa * n_kept * d + sa * (n_kept + T * (1 + int(wl.add_skip) + int(wl.pr_moe))) * d
+           + T * k * (4 + 4 + 4 + 1))
+    if wl.pr_moe:
+        flops += 4.0 * T * d * wl.d_ff_dense
+        byt += sa * 2 * d * wl.d_ff_dense + sa * T * d
+    return flops, byt
 
 
 def classify(name: str) -> str | None:
@@ -261,14 +300,16 @@ def cpu_baseline(wl, inp, target_s):
         rate = t_ffn / n
         step = (budget - t_ffn) / max(rate, 1e-9)
     t_total = t_route + t_ffn * (wl.T / n)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {
-        "value": wl.T / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    rec = {
+        "value": wl.T / t_total, "unit": "tokens/s", "cores": oracle.threads(),
+        "kind": "oracle", "cpu_model": cpu_model(),
         "sample": (f"fp64 oracle: routing, aux loss and dispatch on all {wl.T} tokens "
                    f"({t_route:.2f} s); expert FFN{' + dense MLP' if wl.pr_moe else ''} "
-                   f"on a seeded sample of {n} tokens ({t_ffn:.2f} s), extrapolated "
-                   f"linearly to {wl.T} tokens"),
+                   f"on a seeded sample of {n} tokens ({t_ffn:.2f} s)" +
+                   (f", extrapolated linearly to {wl.T} tokens" if n < wl.T else
+                    " (every token)")),
     }
+    return rec, r
 
 
 # ------------------------------------------------------------- main
@@ -323,24 +364,65 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        return pmc_summary(args)
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def routing_record(wl, out, C, ref_route=None):
+    """Expert load, drops and near-ties of the measured call.  Near-ties are
+    tokens whose k-th and (k+1)-th fp32 router logits lie within 1e-5 (the
+    oracle's fp64 logits rounded to fp32 when the oracle routed every token,
+    else the layer's own fp32 logits); with the oracle's routing the layer's
+    expert ids are also compared on every other token."""
+    import numpy as np
+    load = out.load.cpu().numpy()
+    kept = out.kept.cpu().numpy()
+    ids = out.expert_ids.cpu().numpy()
+    assigned = int((ids >= 0).sum())
+    n_kept = int(kept.sum())
+    rec = {"assignments": assigned, "kept": n_kept, "dropped": assigned - n_kept,
+           "drop_rate": round((assigned - n_kept) / max(assigned, 1), 5), "capacity": C,
+           "load_min": int(load.min()), "load_max": int(load.max()),
+           "kept_min": int(kept.min()), "kept_max": int(kept.max()),
+           "active_experts": int((kept > 0).sum())}
+    logits = None
+    if ref_route is not None:
+        logits = np.asarray(ref_route["logits"], np.float64).astype(np.float32)
+        src = "oracle fp64 logits rounded to fp32"
+    elif out.logits is not None:
+        logits = out.logits.cpu().numpy()
+        src = "layer fp32 logits"
+    if logits is not None and wl.k < wl.E:
+        srt = -np.sort(-logits.astype(np.float64), axis=1)
+        near = np.nonzero(srt[:, wl.k - 1] - srt[:, wl.k] < 1e-5)[0]
+        rec["near_ties"] = int(len(near))
+        rec["near_tie_tokens"] = near[:16].tolist()
+        rec["near_tie_source"] = src
+        if ref_route is not None:
+            bad = np.nonzero((ids != ref_route["ids"]).any(axis=1))[0]
+            rec["ids_equal_oracle_except_near_ties"] = bool(set(bad.tolist()) <= set(near.tolist()))
+            rec["ids_differing"] = int(len(bad))
+    return rec
+
+
+def run_workload(name, args, headline=True):
+    """Time one workload; returns its JSON record."""
     import torch
 
     from mixture_experts_layer_24_amd import binding, synth, workloads
 
-    name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]
     if args.k:
         wl = wl.replace(k=args.k)
     dev = "cuda:0"
-    torch.cuda.set_device(0)
+    steps = args.steps if headline else max(args.steps, args.sub_steps.get(name, args.steps))
     inp = synth.make_inputs(wl, seed=args.seed, device=dev)
     rkw = {}
     if args.router != "topk" or args.router_losses:
@@ -356,12 +438,12 @@ def main():
     bwd = args.backward or args.train
     packable = (wl.act == "bf16" and wl.wfmt == "plain" and wl.d % 128 == 0 and
                 wl.d_ff % 128 == 0)
-    packed = args.expert_weights == "packed" or (args.expert_weights == "auto" and packable
-                                                 and not bwd)
+    packed = (args.expert_weights == "packed" and packable) or (
+        args.expert_weights == "auto" and packable and not bwd)
+    if args.expert_weights == "packed" and (not packable or bwd) and headline:
+        raise SystemExit("bench.py: packed expert weights need a forward pass with bf16 "
+                         "experts and d, d_ff multiples of 128")
     if packed:
-        if not packable or bwd:
-            raise SystemExit("bench.py: packed expert weights need a forward pass with bf16 "
-                             "experts and d, d_ff multiples of 128")
         wl = wl.replace(wfmt="packed")
     cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy,
                             **rkw)
@@ -398,7 +480,7 @@ def main():
 
         step = train_step if args.train else backward
 
-    if args.copy_calibration > 0:
+    if args.copy_calibration > 0 and headline:
         n = int(args.copy_calibration * (1 << 30))
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -437,7 +519,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
@@ -446,9 +528,9 @@ def main():
     binding.profile_filter(None)
     prof = binding.profile_read()
     elapsed = t1 - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.3f})",
+    ms_per_step = 1e3 * elapsed / steps
+    ev_ms = ev0.elapsed_time(ev1) / steps
+    print(f"[bench] {name}: {steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.3f})",
           file=sys.stderr, flush=True)
 
     # cold-cache steps: the timed steps above run back to back, so inputs
@@ -475,7 +557,7 @@ def main():
         cold = {"ms_per_step_median": round(times[len(times) // 2], 4),
                 "ms_per_step_min": round(times[0], 4), "steps": args.cold_steps,
                 "evict_read_bytes": 512 << 20}
-        print(f"[bench] cold-cache steps: median {cold['ms_per_step_median']:.3f} ms",
+        print(f"[bench] {name}: cold-cache steps: median {cold['ms_per_step_median']:.3f} ms",
               file=sys.stderr, flush=True)
 
     kept = out.kept.cpu().tolist()
@@ -490,7 +572,8 @@ def main():
     wk = work.get(cls, {"bytes": 0.0, "flops": 0.0})
     avg_s = dom["avg_ms"] / 1e3
     ai = wk["flops"] / max(wk["bytes"], 1.0)
-    mfma_bound = wl.act == "bf16" and ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = wl.act == "bf16" and ai > ridge
     if mfma_bound:
         achieved = wk["flops"] / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -505,12 +588,27 @@ def main():
     roof["avg_launch_ms"] = round(dom["avg_ms"], 4)
     roof["algorithmic_bytes"] = wk["bytes"]
     roof["algorithmic_flops"] = wk["flops"]
+    if "h_bytes" in wk:
+        roof["h_bytes_excluded"] = wk["h_bytes"]
+    # the whole layer against both peaks (forward only)
+    layer = None
+    if not bwd:
+        lf, lb = layer_work(wl, kept)
+        t_s = ms_per_step / 1e3
+        layer = {"algorithmic_flops": lf, "algorithmic_bytes": lb,
+                 "tflops": round(lf / t_s / 1e12, 2), "gbs": round(lb / t_s / 1e9, 1),
+                 "mfma_frac": round(lf / t_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "hbm_frac": round(lb / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                 "floor_ms": round(1e3 * max(lb / (PEAK_HBM_GBS * 1e9),
+                                             lf / (PEAK_BF16_TFLOPS * 1e12)), 4),
+                 "bound": "hbm" if lf / lb < ridge else "mfma",
+                 "excluded": "expert and dense hidden rows (H)"}
 
     res = {
         "metric": ("MoE-layer training (forward + backward) tokens/s" if args.train else
                    "MoE-layer backward tokens/s" if args.backward else METRIC),
-        "value": round(wl.T * args.steps / elapsed, 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(wl.T * steps / elapsed, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if wl.act == "bf16" else "f32",
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02^2), bf16 RNE)",
@@ -518,7 +616,9 @@ def main():
                    "d_ff": wl.d_ff, "d_ff_dense": wl.d_ff_dense, "capacity": C,
                    "capacity_factor": wl.capacity_factor,
                    "expert_weights": ("bf16 packed (128-row x 64-k blocks, packed once "
-                                      "before timing)" if packed else wl.wfmt),
+                                      "before timing)" if packed else
+                                      "int8 + fp16 scale per 128" if wl.wfmt == "int8"
+                                      else wl.act + " row-major"),
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
                    "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
@@ -529,15 +629,61 @@ def main():
                        **{n: v for n, v in rkw.items() if n != "router"}} if rkw else {}),
                    "n_kept": int(sum(kept)), "active_experts": int(sum(v > 0 for v in kept))},
         "roofline": roof,
+        "layer": layer,
         "kernels": {n: {"avg_ms": round(k["avg_ms"], 4), "launches_per_step":
                         k["launches"] // survey_steps, "class": k["class"]}
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "cold_cache": cold,
         "cpu_baseline": None,
     }
+    ref_route = None
     if not args.no_cpu_baseline and not bwd and not rkw and not args.k:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, oracle_inp, args.cpu_seconds)
+        print(f"[bench] {name}: timing the CPU oracle on a bounded sample", file=sys.stderr,
+              flush=True)
+        budget = args.cpu_seconds if headline else args.sub_cpu_seconds
+        res["cpu_baseline"], ref_route = cpu_baseline(wl, oracle_inp, budget)
+    if not bwd:
+        if ref_route is None and not rkw:  # the layer's own logits for the near-tie count
+            out.logits = torch.empty(wl.T, wl.E, dtype=torch.float32, device=dev)
+            forward()
+            torch.cuda.synchronize()
+        res["routing"] = routing_record(wl, out, C, ref_route)
+    del inp, oracle_inp, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+SUB_WORKLOADS = ("tiny_f32", "moe128_350m", "decode_top2", "skewed_top2_int8")
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        return pmc_summary(args)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_24_amd import workloads
+
+    torch.cuda.set_device(0)
+    # launch-latency-bound workloads get more timed steps in their sub-records
+    args.sub_steps = {"tiny_f32": 200, "decode_top2": 200}
+    name = args.workload or workloads.HEADLINE
+    res = run_workload(name, args, headline=True)
+    variant = (args.backward or args.train or args.router != "topk" or args.router_losses
+               or args.k or args.serial or args.drop_policy != "token_order" or args.z_loss)
+    if args.workload is None and not variant and not args.headline_only:
+        # the other four workloads, each measured the same way, as sub-records
+        res["workloads"] = {}
+        for sub in SUB_WORKLOADS:
+            r = run_workload(sub, args, headline=False)
+            res["workloads"][sub] = {
+                n: r[n] for n in ("value", "unit", "ms_per_step", "steps", "dtype", "config",
+                                  "roofline", "layer", "routing", "kernels", "cold_cache",
+                                  "cpu_baseline")}
     print(json.dumps(res))
 
 

@@ -59,6 +59,8 @@ def _load(path: str | None = None):
             build(p)
         lib = ctypes.CDLL(p)
         i64, dbl, vp, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+        lib.oracle_threads.restype = i32
+        lib.oracle_threads.argtypes = []
         lib.oracle_capacity.restype = i64
         lib.oracle_capacity.argtypes = [i64, i64, i64, dbl, i64]
         lib.oracle_route.restype = i32
@@ -143,6 +145,11 @@ def _p(a):
 
 
 # ---------------------------------------------------------------- stages
+def threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(_load().oracle_threads())
+
+
 def capacity(T: int, E: int, k: int, cf: float, override: int = 0) -> int:
     return int(_load().oracle_capacity(T, E, k, float(cf), int(override)))
 

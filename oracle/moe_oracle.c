@@ -51,6 +51,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_F64 = 3 };
 enum { OR_DROP_TOKEN_ORDER = 0, OR_DROP_GATE_PRIORITY = 1 };
@@ -1022,4 +1025,18 @@ double oracle_cov2(int64_t n, const double *v) {
   for (int64_t i = 0; i < n; i++) var += (v[i] - mean) * (v[i] - mean);
   var /= (double)n;
   return var / (mean * mean);
+}
+
+/* Number of threads the OpenMP loops above run on (reported with timings of
+ * the oracle; not part of the layer's arithmetic). */
+int oracle_threads(void) {
+  int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+#endif
+  return n;
 }
