@@ -109,6 +109,9 @@ def parse():
                    help="extra steps, each after a 512 MiB read that evicts the 256 MB "
                         "Infinity Cache, timed one by one with HIP events (0 = skip)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--sq-summary", nargs="+", metavar="CSV",
+                   help="counter_collection.csv files of SQ/GRBM counter runs: write "
+                        "profiles/<label>__<workload>__sq_counters.txt")
     p.add_argument("--label")
     p.add_argument("--symbol")
     p.add_argument("--copy-gib", type=float, default=1.0)
@@ -656,10 +659,56 @@ def run_workload(name, args, headline=True):
 SUB_WORKLOADS = ("tiny_f32", "moe128_350m", "decode_top2", "skewed_top2_int8")
 
 
+def sq_summary(args):
+    """Mean counter values per dispatch of the kernel matching --symbol over
+    SQ/GRBM counter runs, and the derived MFMA-busy share, cycles per MFMA,
+    LDS-wait share and bank conflicts."""
+    import csv
+    vals = {}
+    for path in args.sq_summary:
+        per = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if not re.search(args.symbol, r["Kernel_Name"]):
+                    continue
+                key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, c), v in per.items():
+            vals.setdefault(c, []).append(v)
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {args.symbol!r}")
+    mean = {c: sum(v) / len(v) for c, v in vals.items()}
+    lines = [f"# rocprofv3 SQ counters -- kernel {args.label}, workload {args.workload}",
+             f"# command: {args.command}",
+             f"source_hash: {src_hash()}",
+             f"symbol_regex: {args.symbol}",
+             "# mean per dispatch, summed over the chip as rocprofv3 reports them"]
+    lines += [f"{c}: {mean[c]:.4e} (dispatches {len(vals[c])})" for c in sorted(mean)]
+    d = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs share them
+        d.append(f"mfma_busy_share: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * mean['GRBM_GUI_ACTIVE'] / 8):.3f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("SQ_INSTS_MFMA"):
+        d.append(f"cycles_per_mfma: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mean['SQ_INSTS_MFMA']:.1f}")
+    if "SQ_WAIT_INST_LDS" in mean and mean.get("SQ_BUSY_CYCLES"):
+        d.append(f"wait_inst_lds_per_busy_cycle: {mean['SQ_WAIT_INST_LDS'] / mean['SQ_BUSY_CYCLES']:.3f}")
+    if "SQ_ACTIVE_INST_VALU" in mean and mean.get("SQ_ACTIVE_INST_ANY"):
+        d.append(f"valu_share_of_active_inst: {mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_ACTIVE_INST_ANY']:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_ACTIVE_INST_LDS"):
+        d.append(f"lds_bank_conflict_per_lds_active: {mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.3f}")
+    lines += ["derived:"] + ["  " + x for x in d]
+    dst = os.path.join(ROOT, "profiles",
+                       f"{args.label.replace(':', '_')}__{args.workload}__sq_counters.txt")
+    open(dst, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         return pmc_summary(args)
+    if args.sq_summary:
+        return sq_summary(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
