@@ -84,7 +84,7 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 // ---- workspace layout
 struct Layout {
   size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
-      xsched, total;
+      xsched, rpart, total;
   // router variants
   size_t scores, cosl, embn, imp, loadp;
   // backward
@@ -136,6 +136,10 @@ Layout layout(const moe_config *c, int entry) {
   };
   const bool gp = c->drop_policy == MOE_DROP_GATE_PRIORITY;
   const size_t segB = (size_t)c->T * (size_t)c->k * 4;
+  // split-K partial products of the fused router (few token blocks)
+  const int rsplit = variant_router(c) ? 1 : moe_host::router_splits(c->T, (int)c->d,
+                                                                     c->act_dtype == MOE_BF16);
+  const size_t rpartB = rsplit > 1 ? (size_t)rsplit * nblk * 64 * ((c->E + 31) / 32 * 32) * 4 : 0;
   auto take_variant = [&]() {
     if (!variant_router(c)) return;
     L.scores = take((size_t)c->T * score_cols(c) * 4);
@@ -152,6 +156,7 @@ Layout layout(const moe_config *c, int entry) {
       L.fcount = take(blkE);
       L.term = take(termE);
       L.zpart = take((size_t)nblk * 4);
+      if (rpartB) L.rpart = take(rpartB);
       take_variant();
       break;
     case MOE_ENTRY_DISPATCH:
@@ -176,6 +181,7 @@ Layout layout(const moe_config *c, int entry) {
       L.offs = take(blkE);
       L.term = take(termE);
       L.zpart = take((size_t)nblk * 4);
+      if (rpartB) L.rpart = take(rpartB);
       take_variant();
       if (gp) L.seg = take(segB);
       if (big) {
@@ -233,8 +239,9 @@ char *at(void *ws, size_t off) { return (char *)ws + off; }
 // ---- launch sequences (arguments already validated)
 hipError_t do_router(const moe_config *c, const void *x, const void *wr, const float *br,
                      int32_t *ids, float *gates, float *logits, float *qsum, int32_t *fcount,
-                     int32_t *hist, float *zpart, float *z_loss, hipStream_t s) {
+                     int32_t *hist, float *zpart, float *z_loss, float *rpart, hipStream_t s) {
   RouterArgs a{};
+  a.part = rpart;
   a.x = x;
   a.w = wr;
   a.bias = br;
@@ -264,7 +271,7 @@ hipError_t do_router_v(const moe_config *c, const Layout &L, void *ws, const voi
                        float *imp_loss, float *load_loss, hipStream_t s) {
   if (!variant_router(c))
     return do_router(c, x, w->w_router, w->b_router, ids, gates, logits, qsum, fcount, hist,
-                     zpart, z_loss, s);
+                     zpart, z_loss, L.rpart ? (float *)at(ws, L.rpart) : nullptr, s);
   const int bf = c->act_dtype == MOE_BF16, E = (int)c->E;
   const int nblk = moe_host::router_blocks(c->T);
   float *scores = (float *)at(ws, L.scores);
@@ -511,7 +518,8 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   int32_t *fcount = (int32_t *)at(ws, L.fcount);
   double *term = (double *)at(ws, L.term);
   hipError_t e = do_router(cfg, x, w_router, b_router, expert_ids, gates, logits, qsum, fcount,
-                           nullptr, (float *)at(ws, L.zpart), z_loss, s);
+                           nullptr, (float *)at(ws, L.zpart), z_loss,
+                           L.rpart ? (float *)at(ws, L.rpart) : nullptr, s);
   if (e == hipSuccess)
     e = moe_host::launch_scan_aux(nullptr, qsum, fcount, moe_host::router_blocks(T),
                                   (int)cfg->E, T, 0, nullptr, nullptr, nullptr, term, s);

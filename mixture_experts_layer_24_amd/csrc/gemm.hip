@@ -328,8 +328,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   const int tiles_n = a.N / BN;
   const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
   const int total = a.G * tiles_m * tiles_n;
-  const int tile = (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
-                                  : xcd_remap(blockIdx.x, total);
+  // spread: each group's tiles go round-robin over the XCDs (groups with few
+  // rows share little in L2, and a group per XCD would leave the XCDs of the
+  // groups without rows idle); else a group's tiles stay on one XCD
+  const int tile = a.spread ? (int)blockIdx.x
+                   : (a.G % 8 == 0) ? xcd_remap_grouped(blockIdx.x, a.G, tiles_m * tiles_n)
+                                    : xcd_remap(blockIdx.x, total);
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
   int tm, tn;
@@ -485,8 +489,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 // one rounding), so the arithmetic is that of a bf16 GEMM on the
 // dequantised weights and half the weight bytes cross LDS.
 // Code tile rows: chunk c (16 codes) of row R sits in slot c ^ ((R >> 2) & 3),
-// which spreads 16 consecutive rows over all 64 banks for the 8-byte operand
-// reads.  Requires K % 1024 == 0 and N % BN == 0.
+// which spreads 16 consecutive rows over all 64 banks for the 16-byte code
+// reads (each lane reads one whole chunk; lanes exchange halves with
+// permlane32 swaps).  Requires K % 1024 == 0 and N % BN == 0.
 // Fragments past the group's valid rows skip their reads and MFMAs, so a
 // partly filled tile costs MFMA time at 32-row granularity.
 __device__ __forceinline__ int swz_q(int R) { return (R >> 2) & 3; }
@@ -612,32 +617,50 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
       nsc[j] = -128.f * sc[j];
     }
     // the MFMA body for LV live fragments, free of branches so that operand
-    // reads and MFMAs can be interleaved; one copy per fragment count
+    // reads and MFMAs can be interleaved; one copy per fragment count.
+    // Codes of two 16-wide sub-steps s, s + 1 arrive in one 16-byte read per
+    // fragment: lanes 0-31 read sub-step s of rows 0-31, lanes 32-63
+    // sub-step s + 1 (each 16-lane group then covers all 64 banks), and two
+    // permlane32 swaps hand every lane its own 8 codes of both sub-steps
+    // (lane l < 32: codes 0-7, lane l >= 32: codes 8-15 of the 16).
     auto body = [&](auto LV) __attribute__((always_inline)) {
       constexpr int L = decltype(LV)::value;
 #pragma unroll
-      for (int s = 0; s < BK / 16; s++) {
-        const int c = 2 * s + (lane >> 5);
-        bf16x8 af[L], bfr[TN];
-#pragma unroll
-        for (int i = 0; i < L; i++) {
-          const int R = wm * WTM + i * 32 + (lane & 31);
-          af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
-        }
+      for (int sp = 0; sp < BK / 32; sp++) {
+        uint32_t q[TN][2][2];  // [fragment][sub-step][dword]
 #pragma unroll
         for (int j = 0; j < TN; j++) {
           const int R = wn * WTN + j * 32 + (lane & 31);
-          const uint32_t *qp =
-              (const uint32_t *)(sb + R * BROWB + ((s ^ swz_q(R)) << 4) + 8 * (lane >> 5));
-          bfr[j] = dequant8(qp[0], qp[1], sc[j], nsc[j]);
+          const u32x4 v =
+              *(const u32x4 *)(sb + R * BROWB + (((2 * sp + (lane >> 5)) ^ swz_q(R)) << 4));
+          // lanes 32-63 of the first operand <-> lanes 0-31 of the second
+          const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+          q[j][0][0] = s0[0];
+          q[j][0][1] = s1[0];
+          q[j][1][0] = s0[1];
+          q[j][1][1] = s1[1];
         }
 #pragma unroll
-        for (int i = 0; i < L; i++)
+        for (int h = 0; h < 2; h++) {
+          const int s = 2 * sp + h;
+          const int c = 2 * s + (lane >> 5);
+          bf16x8 af[L], bfr[TN];
 #pragma unroll
-          for (int j = 0; j < TN; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        // keep each sub-step's operands live only for its own MFMAs
-        __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < L; i++) {
+            const int R = wm * WTM + i * 32 + (lane & 31);
+            af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
+          }
+#pragma unroll
+          for (int j = 0; j < TN; j++) bfr[j] = dequant8(q[j][h][0], q[j][h][1], sc[j], nsc[j]);
+#pragma unroll
+          for (int i = 0; i < L; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          // keep each sub-step's operands live only for its own MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     };
     body(std::integral_constant<int, TM>{});
@@ -1005,7 +1028,11 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
     return launch_cfg<256, 256, 2, 4, 32>(a, 1, gelu, s, role, "bm256_bn256_i8");
   }
   if (a.N % 128 == 0) {
-    if (a.M_cap <= 32) return launch_dma<32, 128, 1, 4, 64, 4>(a, nt, gelu, s, role, "dma32x128");
+    if (a.M_cap <= 32) {  // a few rows per group (decode): tiles spread over the XCDs
+      GemmArgs b = a;
+      b.spread = a.rows != nullptr;
+      return launch_dma<32, 128, 1, 4, 64, 4>(b, nt, gelu, s, role, "dma32x128");
+    }
     if (a.M_cap <= 64) {  // 64x256: two workgroups per CU, 64 KB of weights in flight
       if (a.N % 256 == 0) return launch_dma<64, 256, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x256");
       return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");

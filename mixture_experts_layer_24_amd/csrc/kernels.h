@@ -21,6 +21,7 @@ struct RouterArgs {
   int d, E, k, normalize;
   const void *w2;     // raw-score mode: weight rows nw1.. come from here
   int nw1;
+  float *part;        // split-K partial products [splits][blocks * 64][Ep] (workspace)
 };
 
 // router variants (router_var.hip); the values are the C ABI's MOE_ROUTER_*
@@ -41,6 +42,7 @@ struct RouteVarArgs {
   int64_t T;
   int E, k, normalize, variant;
   float top_p;
+  int ld;  // row stride of src (0 = its column count: E, or 2E for noisy)
 };
 
 // Grouped "NT" GEMM: for each group g < G and row m < rows[g] (or M_cap):
@@ -60,6 +62,9 @@ struct GemmArgs {
   const int32_t *xsched;
   // B in blocks of 128 rows x 64 K (MOE_W_BF16_PACKED) instead of row-major
   int b_packed;
+  // tiles in launch order, dealt round-robin over the XCDs (set by the
+  // launcher for groups of one row tile), instead of a group per XCD
+  int spread;
 };
 
 // general grouped GEMM of the backward (backward.hip)
@@ -85,6 +90,10 @@ struct GenArgs {
 namespace moe_host {
 
 int router_blocks(int64_t T);
+// K splits launch_router uses for this batch (1 = none); the partial
+// products need splits * router_blocks(T) * 64 * Ep floats of workspace
+// (Ep = E rounded up to a multiple of 32)
+int router_splits(int64_t T, int d, int act_bf16);
 hipError_t launch_router(const moe::RouterArgs &a, int act_bf16, hipStream_t s);
 hipError_t launch_aux_sum(const double *term, int E, float alpha, float *aux, hipStream_t s);
 hipError_t launch_router_scores(const moe::RouterArgs &a, int act_bf16, hipStream_t s);

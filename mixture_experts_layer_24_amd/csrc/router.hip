@@ -244,6 +244,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     if (kt + 1 < ksteps) load_tiles((kt + 1) * BK);
     const bf16 *sa = As + st * STAGE;
     const bf16 *sw = sa + RBM * LDA;
+    // branch-free as in router_dma_kernel: tiles past Ep are never stored
 #pragma unroll
     for (int s = 0; s < BK / 16; s++) {
       const int ch = 2 * s + (lane >> 5);
@@ -251,10 +252,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
 #pragma unroll
       for (int i = 0; i < NTW; i++) {
         const int nt = (wave >> 1) + 2 * i;
-        if (nt * 32 < Ep) {
-          bf16x8 bv = *(const bf16x8 *)(sw + (nt * 32 + (lane & 31)) * LDA + ch * 8);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
-        }
+        bf16x8 bv = *(const bf16x8 *)(sw + (nt * 32 + (lane & 31)) * LDA + ch * 8);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
       }
     }
     if (kt + 1 < ksteps) store_tiles(st ^ 1);
@@ -357,19 +356,26 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
     for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
 
   const int mt = wave & 1;  // 32-row half of the token tile
-  const int ksteps = d / 64;
+  // K range of this block: all of d, or (split K, gridDim.y > 1) its share
+  const int kall = d / 64, ns = gridDim.y;
+  const int kbeg = (int)((int64_t)blockIdx.y * kall / ns);
+  const int ksteps = (int)((int64_t)(blockIdx.y + 1) * kall / ns) - kbeg;
+  auto kidx = [&](int kt) __attribute__((always_inline)) { return kbeg + kt; };
 #pragma unroll
   for (int p = 0; p < NS - 1; p++)
-    if (p < ksteps) issue(p, p);
+    if (p < ksteps) issue(p, kidx(p));
   for (int kt = 0; kt < ksteps; kt++) {
     if (kt + NS - 2 < ksteps)
       wait_vmcnt<(NS - 2) * CPW>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // every wave's chunks of step kt; stage (kt - 1) % NS free
-    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
+    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kidx(kt + NS - 1));
     const char *sa = smem + (kt % NS) * STAGE;
     const char *sw = sa + RBM * ROWB;
+    // every wave runs all NTW expert tiles (tiles past Ep multiply the
+    // clamped weight rows and are never stored), so the loop has no branch
+    // and the accumulators stay in place across the MFMAs
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const int c = 2 * s + (lane >> 5);
@@ -377,12 +383,9 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
       const bf16x8 av = *(const bf16x8 *)(sa + Ra * ROWB + ((c ^ swz_slot<64>(Ra)) << 4));
 #pragma unroll
       for (int i = 0; i < NTW; i++) {
-        const int nt = (wave >> 1) + 2 * i;
-        if (nt * 32 < Ep) {
-          const int Rw = nt * 32 + (lane & 31);
-          const bf16x8 bv = *(const bf16x8 *)(sw + Rw * ROWB + ((c ^ swz_slot<64>(Rw)) << 4));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
-        }
+        const int Rw = ((wave >> 1) + 2 * i) * 32 + (lane & 31);
+        const bf16x8 bv = *(const bf16x8 *)(sw + Rw * ROWB + ((c ^ swz_slot<64>(Rw)) << 4));
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
       }
     }
   }
@@ -402,6 +405,17 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
   }
   __syncthreads();
   if constexpr (SCORES) {
+    // split K: partial products of K range blockIdx.y in slab blockIdx.y of
+    // a.part ([splits][blocks * 64][Ep], every row and column written; the
+    // columns past E hold products of the clamped weight row)
+    if (ns > 1) {
+      float *P = a.part + ((int64_t)blockIdx.y * gridDim.x * RBM + t0) * Ep;
+      for (int idx = tid; idx < RBM * Ep / 4; idx += 256) {
+        const int r = idx / (Ep / 4), e = 4 * (idx - r * (Ep / 4));
+        *(f32x4 *)(P + (int64_t)r * Ep + e) = *(const f32x4 *)(L + r * ldl + e);
+      }
+      return;
+    }
     for (int idx = tid; idx < RBM * E; idx += 256) {
       const int r = idx / E, e = idx - (idx / E) * E;
       const int64_t t = t0 + r;
@@ -413,6 +427,26 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
     router_epilogue<2, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
     router_epilogue<8, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
+}
+
+// Split-K router, second step: the partial products of the splits summed in
+// split order (fixed) into slab 0, 4 columns per thread with the loads of
+// every split in flight together (nsplit <= kMaxSplit); the softmax / top-k
+// epilogue then runs on the sums (route_logits_kernel, one wave per token).
+constexpr int kMaxSplit = 16;
+__global__ __launch_bounds__(256) void router_split_sum_kernel(float *part, int nsplit,
+                                                               int64_t slab, int64_t n4) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n4) return;
+  f32x4 v[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; sp++)
+    if (sp < nsplit) v[sp] = *(const f32x4 *)(part + sp * slab + 4 * q);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxSplit; sp++)
+    if (sp < nsplit) acc += v[sp];
+  *(f32x4 *)(part + 4 * q) = acc;
 }
 
 // fp32 activations: plain fp32 dot products (small shapes; correctness path)
@@ -483,6 +517,19 @@ using namespace moe;
 
 int router_blocks(int64_t T) { return (int)((T + RBM - 1) / RBM); }
 
+// K splits of the bf16 router: a batch of few 64-token blocks (decode) would
+// leave most CUs idle and one block's K sweep on the critical path, so its K
+// range is split over up to 16 blocks per token block, at least 4 K steps
+// each; 1 = no split.
+int router_splits(int64_t T, int d, int act_bf16) {
+  const int nblk = router_blocks(T), ksteps = d / 64;
+  if (!act_bf16 || nblk <= 0 || nblk > 16) return 1;
+  int s = ksteps / 4;
+  if (s > kMaxSplit) s = kMaxSplit;
+  if (s * nblk > 64) s = 64 / nblk;
+  return s < 2 ? 1 : s;
+}
+
 hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, hipStream_t s) {
   MOE_LAUNCH("zloss_sum", zloss_sum_kernel, dim3(1), dim3(256), 0, s, zpart, nblk, T, z);
   return hipGetLastError();
@@ -490,6 +537,37 @@ hipError_t launch_zloss_sum(const float *zpart, int nblk, int64_t T, float *z, h
 
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   const int nblk = router_blocks(a.T);
+  const int nsplit = a.part ? router_splits(a.T, a.d, act_bf16) : 1;
+  if (nblk > 0 && nsplit > 1) {  // split K: partial products, their sums, the epilogue
+    const int ntw = ((a.E + 31) / 32 + 1) / 2, Ep = (a.E + 31) & ~31;
+    const dim3 g(nblk, nsplit), b(256);
+    switch (ntw) {
+      case 1: MOE_LAUNCH("router_split_e64", (router_dma_kernel<1, 4, true>), g, b, 0, s, a); break;
+      case 2: MOE_LAUNCH("router_split_e128", (router_dma_kernel<2, 4, true>), g, b, 0, s, a); break;
+      case 3: MOE_LAUNCH("router_split_e192", (router_dma_kernel<3, 4, true>), g, b, 0, s, a); break;
+      default: MOE_LAUNCH("router_split_e256", (router_dma_kernel<4, 3, true>), g, b, 0, s, a); break;
+    }
+    const int64_t slab = (int64_t)nblk * RBM * Ep, n4 = slab / 4;
+    MOE_LAUNCH("router_split_sum", router_split_sum_kernel, dim3((unsigned)((n4 + 255) / 256)),
+               b, 0, s, a.part, nsplit, slab, n4);
+    RouteVarArgs va{};
+    va.src = a.part;
+    va.ld = Ep;
+    va.bias = a.bias;
+    va.ids = a.ids;
+    va.gates = a.gates;
+    va.logits = a.logits;
+    va.qsum = a.qsum;
+    va.fcount = a.fcount;
+    va.hist = a.hist;
+    va.zpart = a.zpart;
+    va.T = a.T;
+    va.E = a.E;
+    va.k = a.k;
+    va.normalize = a.normalize;
+    va.variant = RV_TOPK;
+    return launch_route_logits(va, s);
+  }
   if (nblk > 0) {
     if (act_bf16) {  // the bf16 path guarantees d % 64 == 0
       const int ntw = ((a.E + 31) / 32 + 1) / 2;

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, blk = blockIdx.x;
   const int E = a.E, k = a.k;
   const bool noisy = a.variant == RV_NOISY, topp = a.variant == RV_TOP_P;
-  const int ns = noisy ? 2 * E : E;
+  const int ns = a.ld ? a.ld : (noisy ? 2 * E : E);
   if (tid < 256) {
     fcnt[tid] = 0;
     hcnt[tid] = 0;
@@ -62,8 +62,29 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
     bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
   }
   const bool renorm = noisy ? true : (topp ? a.normalize != 0 : (k >= 2 && a.normalize));
-  for (int rr = 0; rr < VBT / VW; rr++) {
-    const int r = wave * (VBT / VW) + rr;
+  // the wave's rows of scores (and noise) are loaded before the first row is
+  // worked on, so their latencies overlap
+  constexpr int RPW = VBT / VW;
+  float src0[RPW][4], src1[RPW][4], nz[RPW][4];
+#pragma unroll
+  for (int rr = 0; rr < RPW; rr++) {
+    const int64_t t = (int64_t)blk * VBT + wave * RPW + rr;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e = lane + kWave * i;
+      src0[rr][i] = src1[rr][i] = nz[rr][i] = 0.f;
+      if (t < a.T && e < E) {
+        src0[rr][i] = a.src[t * ns + e];
+        if (noisy) {
+          src1[rr][i] = a.src[t * ns + E + e];
+          nz[rr][i] = a.noise[t * E + e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPW; rr++) {
+    const int r = wave * RPW + rr;
     const int64_t t = (int64_t)blk * VBT + r;
     if (t >= a.T) break;
     float v[4], clean[4], sig[4];
@@ -76,11 +97,11 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
       sig[i] = 0.f;
       v[i] = neg_inf();
       if (live[i]) {
-        clean[i] = a.src[t * ns + e] + bias[i];
+        clean[i] = src0[rr][i] + bias[i];
         v[i] = clean[i];
         if (noisy) {
-          sig[i] = softplus_f(a.src[t * ns + E + e]);
-          v[i] = clean[i] + a.noise[t * E + e] * sig[i];
+          sig[i] = softplus_f(src1[rr][i]);
+          v[i] = clean[i] + nz[rr][i] * sig[i];
         }
         if (a.logits) a.logits[t * E + e] = v[i];
       }
