@@ -379,7 +379,8 @@ hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t 
   const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
   hipError_t e = hipSuccess;
   if (xsched && sched_experts(c)) {
-    e = moe_host::launch_tile_sched(kept, (int)c->E, C, xsched, s);
+    e = moe_host::launch_tile_sched(kept, (int)c->E, C, c->d % 512 == 0 && c->d_ff % 512 == 0,
+                                    xsched, s);
     if (e != hipSuccess) return e;
   } else {
     xsched = nullptr;

@@ -489,12 +489,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 // one rounding), so the arithmetic is that of a bf16 GEMM on the
 // dequantised weights and half the weight bytes cross LDS.
 // Code tile rows: chunk c (16 codes) of row R sits in slot c ^ ((R >> 2) & 3),
-// which spreads 16 consecutive rows over all 64 banks for the 16-byte code
-// reads (each lane reads one whole chunk; lanes exchange halves with
-// permlane32 swaps).  Requires K % 1024 == 0 and N % BN == 0.
+// which spreads 16 consecutive rows over all 64 banks.  (One 16-byte read per
+// lane with permlane32 swaps of the halves, which avoids the two-way bank
+// conflict of the 8-byte reads, measured 1-1.5% slower.)  Requires
+// K % 1024 == 0 and N % BN == 0.
 // Fragments past the group's valid rows skip their reads and MFMAs, so a
 // partly filled tile costs MFMA time at 32-row granularity.
 __device__ __forceinline__ int swz_q(int R) { return (R >> 2) & 3; }
+
+// queue entry flag of the int8 schedule: the group runs light tiles
+constexpr int kLightGroup = 0x10000;
 
 __device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, float nsc) {
   lo ^= 0x80808080u;  // q + 128 in each byte
@@ -508,8 +512,15 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, f
   return r;
 }
 
+// LDS bytes of an int8 tile: NS stages of activations and codes, and two
+// scale blocks
+template <int BM, int BN, int NS>
+constexpr int i8_lds_bytes() {
+  return NS * (BM * 128 + BN * 64) + 2 * BN * 16;
+}
+
 template <int BM, int BN, int WM, int WN, int NS, int GELU>
-__device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn) {
+__device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn, char *smem) {
   constexpr int BK = 64;
   constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -527,7 +538,7 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
   static_assert(A_PW * W == A_CH && B_PW * W == B_CH && TM >= 1 && TN >= 1 && SC_CH <= W, "tile");
   static_assert(NS >= 2 && NS * STAGE + 2 * SCB <= 160 * 1024, "LDS budget");
   static_assert((NS - 2) * CPW < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + 2 * SCB];
+  static_assert(i8_lds_bytes<BM, BN, NS>() == NS * STAGE + 2 * SCB, "LDS size");
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -617,50 +628,32 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
       nsc[j] = -128.f * sc[j];
     }
     // the MFMA body for LV live fragments, free of branches so that operand
-    // reads and MFMAs can be interleaved; one copy per fragment count.
-    // Codes of two 16-wide sub-steps s, s + 1 arrive in one 16-byte read per
-    // fragment: lanes 0-31 read sub-step s of rows 0-31, lanes 32-63
-    // sub-step s + 1 (each 16-lane group then covers all 64 banks), and two
-    // permlane32 swaps hand every lane its own 8 codes of both sub-steps
-    // (lane l < 32: codes 0-7, lane l >= 32: codes 8-15 of the 16).
+    // reads and MFMAs can be interleaved; one copy per fragment count
     auto body = [&](auto LV) __attribute__((always_inline)) {
       constexpr int L = decltype(LV)::value;
 #pragma unroll
-      for (int sp = 0; sp < BK / 32; sp++) {
-        uint32_t q[TN][2][2];  // [fragment][sub-step][dword]
+      for (int s = 0; s < BK / 16; s++) {
+        const int c = 2 * s + (lane >> 5);
+        bf16x8 af[L], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < L; i++) {
+          const int R = wm * WTM + i * 32 + (lane & 31);
+          af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
+        }
 #pragma unroll
         for (int j = 0; j < TN; j++) {
           const int R = wn * WTN + j * 32 + (lane & 31);
-          const u32x4 v =
-              *(const u32x4 *)(sb + R * BROWB + (((2 * sp + (lane >> 5)) ^ swz_q(R)) << 4));
-          // lanes 32-63 of the first operand <-> lanes 0-31 of the second
-          const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-          q[j][0][0] = s0[0];
-          q[j][0][1] = s1[0];
-          q[j][1][0] = s0[1];
-          q[j][1][1] = s1[1];
+          const uint32_t *qp =
+              (const uint32_t *)(sb + R * BROWB + ((s ^ swz_q(R)) << 4) + 8 * (lane >> 5));
+          bfr[j] = dequant8(qp[0], qp[1], sc[j], nsc[j]);
         }
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-          const int s = 2 * sp + h;
-          const int c = 2 * s + (lane >> 5);
-          bf16x8 af[L], bfr[TN];
+        for (int i = 0; i < L; i++)
 #pragma unroll
-          for (int i = 0; i < L; i++) {
-            const int R = wm * WTM + i * 32 + (lane & 31);
-            af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
-          }
-#pragma unroll
-          for (int j = 0; j < TN; j++) bfr[j] = dequant8(q[j][h][0], q[j][h][1], sc[j], nsc[j]);
-#pragma unroll
-          for (int i = 0; i < L; i++)
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          // keep each sub-step's operands live only for its own MFMAs
-          __builtin_amdgcn_sched_barrier(0);
-        }
+          for (int j = 0; j < TN; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        // keep each sub-step's operands live only for its own MFMAs
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     body(std::integral_constant<int, TM>{});
@@ -705,6 +698,7 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
 // One tile per workgroup, tiles laid over the XCDs as in gemm_dma_kernel.
 template <int BM, int BN, int WM, int WN, int NS, int GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[i8_lds_bytes<BM, BN, NS>()];
   const int tiles_n = a.N / BN;
   const int tiles_m = (int)((a.M_cap + BM - 1) / BM);
   const int total = a.G * tiles_m * tiles_n;
@@ -714,59 +708,89 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_kernel(GemmArgs a) {
   const int rem = tile - g * tiles_m * tiles_n;
   int tm, tn;
   grouped_tile(rem, tiles_m, tiles_n, tm, tn);
-  i8_tile<BM, BN, WM, WN, NS, GELU>(a, g, tm, tn);
+  i8_tile<BM, BN, WM, WN, NS, GELU>(a, g, tm, tn, smem);
 }
 
 // Groups placed on the XCDs by a schedule (tile_sched_kernel): the
 // workgroups of XCD x (blockIdx % 8 == x) walk that XCD's queue -- its
-// groups in schedule order, each group's valid row tiles column by column --
-// so every group still runs on one XCD (operands shared in its L2) while
-// skewed row counts are spread evenly over the XCDs.
-template <int BM, int BN, int WM, int WN, int NS, int GELU>
+// groups in schedule order, each group's tiles column by column -- so every
+// group still runs on one XCD (operands shared in its L2) while skewed row
+// counts are spread evenly over the XCDs.  A group with at most 64 rows (a
+// "light" group, marked in the queue) runs BMl x BNl tiles (64 x 512): its
+// work is streaming its weights, and the 256 x 256 tile would move 256
+// activation rows and only 16 KB of codes per K step; the others run
+// BM x BN tiles.  Queue lengths are in units of half the BN-column tiles
+// of a row tile: a group of v row tiles counts 2 v, a light group 1 (the
+// schedule uses light groups only when N is a multiple of 2 BN = BNl).
+template <int BM, int BN, int WM, int WN, int NS, int BMl, int BNl, int WMl, int WNl, int NSl,
+          int GELU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_sched_kernel(GemmArgs a) {
+  static_assert(WM * WN == WMl * WNl && BNl == 2 * BN, "tile shapes");
+  constexpr int LDS = i8_lds_bytes<BM, BN, NS>() > i8_lds_bytes<BMl, BNl, NSl>()
+                          ? i8_lds_bytes<BM, BN, NS>()
+                          : i8_lds_bytes<BMl, BNl, NSl>();
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
   const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
   const int tiles_n = a.N / BN;
   const int32_t *xs = a.xsched;
   const int nx = xs[x];
   const int32_t *lst = xs + 8 + x * a.G;
   const int32_t *pre = xs + 8 + 8 * a.G + x * (a.G + 1);
-  const int ntiles = pre[nx] * tiles_n;
-  for (int i = blockIdx.x >> 3; i < ntiles; i += nbx) {
-    // the last group of the queue whose tiles start at or before i
+  const int64_t ntiles = (int64_t)pre[nx] * tiles_n / 2;
+  for (int64_t i = blockIdx.x >> 3; i < ntiles; i += nbx) {
+    // the last queue entry whose tiles start at or before i
     int lo = 0, hi = nx - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] * tiles_n <= i) lo = mid; else hi = mid - 1;
+      if ((int64_t)pre[mid] * tiles_n / 2 <= i) lo = mid; else hi = mid - 1;
     }
-    const int v = pre[lo + 1] - pre[lo], j = i - pre[lo] * tiles_n;
-    const int tn = j / v, tm = j - tn * v;
-    i8_tile<BM, BN, WM, WN, NS, GELU>(a, lst[lo], tm, tn);
+    const int ent = lst[lo], g = ent & 0xffff;
+    const int j = (int)(i - (int64_t)pre[lo] * tiles_n / 2);
+    if (ent & kLightGroup) {
+      i8_tile<BMl, BNl, WMl, WNl, NSl, GELU>(a, g, 0, j, smem);
+    } else {
+      const int v = (pre[lo + 1] - pre[lo]) / 2;
+      const int tn = j / v, tm = j - tn * v;
+      i8_tile<BM, BN, WM, WN, NS, GELU>(a, g, tm, tn, smem);
+    }
     __syncthreads();  // the next tile's DMA reuses the LDS of this epilogue
   }
 }
 
-// Schedule of the 256-row int8 tiles over the 8 XCDs: each group's cost is
-// its row tiles in 32-row fragments (at least 4 per tile: a tile with few
-// rows still streams its weight slab), groups are taken largest first and
-// each goes to the XCD with the least cost so far.  Output (int32):
-// [0, 8) groups per XCD; [8 + x * G, ...) XCD x's groups in order;
-// [8 + 8 * G + x * (G + 1), ...) prefix sums of their row tiles.  One
+// Schedule of the int8 tiles over the 8 XCDs.  A group with at most 64 rows
+// runs light tiles when `light` (both GEMMs' N multiples of 512) and costs
+// LIGHT_COST; another group's cost is its 256-row tiles in 32-row fragments
+// (at least 4 per tile: a tile with few rows still streams its weight slab)
+// -- costs per 256 output columns.  Groups are taken largest first and each
+// goes to the XCD with the least cost so far; each XCD's queue then
+// interleaves its light groups (weight streaming) evenly among its other
+// groups (mostly MFMA work) by queue length.  Output (int32): [0, 8) queue
+// entries per XCD; [8 + x * G, ...) XCD x's entries (group, | kLightGroup for
+// a light group); [8 + 8 * G + x * (G + 1), ...) prefix sums of their
+// lengths (a group of v row tiles counts 2 v, a light group 1).  One
 // workgroup of 256 threads, G <= 256.
 __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, int G, int64_t M_cap,
-                                                         int32_t *xs) {
-  constexpr int BM = 256, FLOOR = 4;
-  __shared__ int cost[256], vm[256], order[256], scost[256], svm[256];
+                                                         int light, int32_t *xs) {
+  constexpr int BM = 256, FLOOR = 4, LIGHT_ROWS = 64, LIGHT_COST = 2;
+  __shared__ int cost[256], unit[256], order[256], scost[256], sunit[256];
+  __shared__ int hl[8][256], ll[8][256], hu[8][256];
   const int tid = threadIdx.x;
   if (tid < G) {
     const int64_t r = rows[tid] < M_cap ? rows[tid] : M_cap;
-    const int v = r > 0 ? (int)((r + BM - 1) / BM) : 0;
-    int c = 0;
-    for (int t = 0; t < v; t++) {
-      const int64_t rt = r - (int64_t)t * BM < BM ? r - (int64_t)t * BM : BM;
-      const int f = (int)((rt + 31) / 32);
-      c += f > FLOOR ? f : FLOOR;
+    int c = 0, u = 0;
+    if (light && r > 0 && r <= LIGHT_ROWS) {
+      c = LIGHT_COST;
+      u = -1;  // light: one unit, flagged by the sign
+    } else if (r > 0) {
+      const int v = (int)((r + BM - 1) / BM);
+      for (int t = 0; t < v; t++) {
+        const int64_t rt = r - (int64_t)t * BM < BM ? r - (int64_t)t * BM : BM;
+        const int f = (int)((rt + 31) / 32);
+        c += f > FLOOR ? f : FLOOR;
+      }
+      u = 2 * v;
     }
-    vm[tid] = v;
+    unit[tid] = u;
     cost[tid] = c;
   }
   __syncthreads();
@@ -775,19 +799,18 @@ __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, in
     for (int h = 0; h < G; h++) rk += cost[h] > cost[tid] || (cost[h] == cost[tid] && h < tid);
     order[rk] = tid;
     scost[rk] = cost[tid];
-    svm[rk] = vm[tid];
+    sunit[rk] = unit[tid];
   }
   __syncthreads();
   if (tid < kWave) {
-    // lane x < 8 keeps XCD x's cost, group count and row tiles; each group
+    // lane x < 8 keeps XCD x's cost and its heavy and light lists; each group
     // goes to the lane with the least cost (ties: lower XCD)
     // (lanes 8..63 shuffle among themselves and never write)
     const int x = tid;
-    int load = x < 8 ? 0 : 0x7fffffff, cnt = 0, tiles = 0;
-    int32_t *lst = xs + 8 + x * G, *pre = xs + 8 + 8 * G + x * (G + 1);
+    int load = x < 8 ? 0 : 0x7fffffff, nh = 0, nl = 0, uh = 0;
     for (int i = 0; i < G; i++) {
-      const int v = svm[i];
-      if (v == 0) break;  // the rest are empty too (cost 0 ranks last)
+      const int u = sunit[i];
+      if (u == 0) break;  // the rest are empty too (cost 0 ranks last)
       int bl = load, bx = x;
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
@@ -795,16 +818,35 @@ __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, in
         if (ol < bl || (ol == bl && ox < bx)) { bl = ol; bx = ox; }
       }
       if (x < 8 && x == bx) {
-        lst[cnt] = order[i];
-        pre[cnt] = tiles;
-        cnt++;
-        tiles += v;
+        if (u < 0) {
+          ll[x][nl++] = order[i];
+        } else {
+          hl[x][nh] = order[i];
+          hu[x][nh++] = u;
+          uh += u;
+        }
         load += scost[i];
       }
     }
     if (x < 8) {
+      // merge: a light group comes next while the share of light groups
+      // placed is below the share of heavy length placed
+      int32_t *lst = xs + 8 + x * G, *pre = xs + 8 + 8 * G + x * (G + 1);
+      int ih = 0, il = 0, ch = 0, cnt = 0, len = 0;
+      while (ih < nh || il < nl) {
+        const bool take_l = il < nl && (ih == nh || (int64_t)il * uh < (int64_t)ch * nl);
+        pre[cnt] = len;
+        if (take_l) {
+          lst[cnt++] = ll[x][il++] | kLightGroup;
+          len += 1;
+        } else {
+          lst[cnt++] = hl[x][ih];
+          len += hu[x][ih];
+          ch += hu[x][ih++];
+        }
+      }
       xs[x] = cnt;
-      pre[cnt] = tiles;
+      pre[cnt] = len;
     }
   }
 }
@@ -955,16 +997,19 @@ static hipError_t launch_dma_i8(const GemmArgs &a, int gelu, hipStream_t s, cons
   if (tiles <= 0) return hipGetLastError();
   const dim3 grid(tiles), block(64 * WM * WN);
   const int epi = epi_of(a, gelu);
-  if constexpr (BM == 256) {  // the schedule counts 256-row tiles
-    if (a.xsched) {
+  if constexpr (BM == 256 && BN == 256 && WM * WN == 8) {  // the schedule counts 256-row tiles
+    if (a.xsched) {  // light groups: 64 x 512 tiles of 8 waves (64 x 64 each), 3 stages
       const dim3 sgrid((tiles + 7) / 8 * 8);
       const char *name = intern_name(role, "dma256x256_i8_sched");
       if (epi == 2)
-        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 2>), sgrid, block, 0, s, a);
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 64, 512, 1, 8, 3, 2>),
+                   sgrid, block, 0, s, a);
       else if (epi == 1)
-        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 1>), sgrid, block, 0, s, a);
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 64, 512, 1, 8, 3, 1>),
+                   sgrid, block, 0, s, a);
       else
-        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 0>), sgrid, block, 0, s, a);
+        MOE_LAUNCH(name, (gemm_dma_i8_sched_kernel<BM, BN, WM, WN, NS, 64, 512, 1, 8, 3, 0>),
+                   sgrid, block, 0, s, a);
       return hipGetLastError();
     }
   }
@@ -989,11 +1034,11 @@ hipError_t launch_pack_weights(const void *w, void *wp, int64_t G, int64_t N, in
   return hipGetLastError();
 }
 
-hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int32_t *xs,
+hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int light, int32_t *xs,
                              hipStream_t s) {
   if (G < 1 || G > 256) return hipErrorInvalidValue;
   MOE_LAUNCH(intern_name("expert_tile_sched", "lpt"), tile_sched_kernel, dim3(1), dim3(256), 0, s,
-             rows, G, M_cap, xs);
+             rows, G, M_cap, light, xs);
   return hipGetLastError();
 }
 

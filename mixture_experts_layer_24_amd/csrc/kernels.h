@@ -146,8 +146,10 @@ hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gel
 // [G][N][K] row-major bf16 -> blocks of 128 rows x 64 K (N % 128 == 0, K % 64 == 0)
 hipError_t launch_pack_weights(const void *w, void *wp, int64_t G, int64_t N, int64_t K,
                                hipStream_t s);
-// XCD schedule of G groups' 256-row int8 tiles from their row counts (G <= 256)
-hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int32_t *xs,
+// XCD schedule of G groups' int8 tiles from their row counts (G <= 256);
+// light: groups of at most 64 rows run 64 x 512 tiles (both GEMMs' N must be
+// multiples of 512)
+hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int light, int32_t *xs,
                              hipStream_t s);
 
 // a stable C string for a profiling name built at run time
