@@ -386,11 +386,16 @@ __global__ __launch_bounds__(256) void rank_gate_kernel(const int32_t *seg, cons
   }
 }
 
-// one wave per assignment; VT = the vector type moved per lane
+// one wave per assignment; VT = the vector type moved per lane.  A row is
+// copied in passes of up to GV vectors per lane, every load of a pass issued
+// before its first store (x and x_disp never overlap).
 template <typename VT>
-__global__ __launch_bounds__(256) void gather_kernel(const char *x, const int32_t *ids,
-                                                     const int32_t *slots, int64_t n_assign, int k,
-                                                     int64_t C, int64_t row_bytes, char *x_disp) {
+__global__ __launch_bounds__(256) void gather_kernel(const char *__restrict__ x,
+                                                     const int32_t *__restrict__ ids,
+                                                     const int32_t *__restrict__ slots,
+                                                     int64_t n_assign, int k, int64_t C,
+                                                     int64_t row_bytes, char *__restrict__ x_disp) {
+  constexpr int GV = 8;
   const int lane = lane_id();
   const int64_t nw = (int64_t)gridDim.x * 4;
   const int64_t nvec = row_bytes / (int64_t)sizeof(VT);
@@ -400,7 +405,15 @@ __global__ __launch_bounds__(256) void gather_kernel(const char *x, const int32_
     const int e = __builtin_amdgcn_readfirstlane(ids[a]);
     const VT *src = (const VT *)(x + (a / k) * row_bytes);
     VT *dst = (VT *)(x_disp + ((int64_t)e * C + slot) * row_bytes);
-    for (int64_t c = lane; c < nvec; c += kWave) dst[c] = src[c];
+    for (int64_t c0 = lane; c0 < nvec; c0 += GV * kWave) {
+      VT v[GV];
+#pragma unroll
+      for (int i = 0; i < GV; i++)
+        if (c0 + i * kWave < nvec) v[i] = src[c0 + i * kWave];
+#pragma unroll
+      for (int i = 0; i < GV; i++)
+        if (c0 + i * kWave < nvec) dst[c0 + i * kWave] = v[i];
+    }
   }
 }
 
