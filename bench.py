@@ -34,6 +34,10 @@ records, not part of "value").  One JSON line is printed:
              tokens (k-th and (k+1)-th fp32 logits within 1e-5) and whether
              the expert ids equal the oracle's on every other token
   kernels    per-kernel mean launch times from the survey steps
+  isolated   (PR-MoE with the dense MLP overlapped) every kernel's time in
+             two more survey steps with the dense MLP run in order, and its
+             rate against the roofline; the overlapped step's kernels share
+             the chip, so their spans in `kernels` include each other's time
   cold_cache steps timed one by one after a 512 MiB read that evicts the
              Infinity Cache (the timed steps above run back to back, so inputs
              smaller than the cache may be partly warm there)
@@ -109,6 +113,9 @@ def parse():
                    help="extra steps, each after a 512 MiB read that evicts the 256 MB "
                         "Infinity Cache, timed one by one with HIP events (0 = skip)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--stats-summary", metavar="CSV",
+                   help="kernel_stats.csv of a rocprofv3 --kernel-trace --stats run: write "
+                        "profiles/<label>__<workload>__kernel_stats.txt")
     p.add_argument("--sq-summary", nargs="+", metavar="CSV",
                    help="counter_collection.csv files of SQ/GRBM counter runs: write "
                         "profiles/<label>__<workload>__sq_counters.txt")
@@ -354,6 +361,7 @@ def pmc_summary(args):
     hbm = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][1] + out["WRITE_SIZE"][0] * out["WRITE_SIZE"][1]
     lines = [f"# rocprofv3 HBM traffic -- kernel {args.label}, workload {args.workload}",
              f"# command: {args.command}",
+             "# ($REPO is the repository root)",
              f"source_hash: {src_hash()}",
              f"symbol_regex: {args.symbol}"]
     for ctr, (raw, factor, n, ncal) in out.items():
@@ -563,6 +571,22 @@ def run_workload(name, args, headline=True):
         print(f"[bench] {name}: cold-cache steps: median {cold['ms_per_step_median']:.3f} ms",
               file=sys.stderr, flush=True)
 
+    # PR-MoE overlapped: the dense MLP's tiles share the chip with the expert
+    # path, so the kernels' spans in the survey above include each other's
+    # time; two more survey steps with the dense MLP in order give every
+    # kernel's time alone (reported as `isolated`, not part of `value`)
+    isolated = None
+    if wl.pr_moe and not args.serial and not bwd:
+        cfg_s = binding.config_of(wl, overlap_dense=False, drop_policy=args.drop_policy, **rkw)
+        binding.profile_reset()
+        binding.profile_filter(None)
+        binding.profile_enable(True)
+        for _ in range(survey_steps):
+            binding.moe_layer_forward(cfg_s, inp["x"], inp, out, ws, stream)
+        torch.cuda.synchronize()
+        binding.profile_enable(False)
+        isolated = {n: tot / cnt for n, (cnt, tot) in binding.profile_read().items()}
+
     kept = out.kept.cpu().tolist()
     work = kernel_work(wl, kept, C, args.router, args.cos_dim)
     kern = {}
@@ -607,6 +631,23 @@ def run_workload(name, args, headline=True):
                  "bound": "hbm" if lf / lb < ridge else "mfma",
                  "excluded": "expert and dense hidden rows (H)"}
 
+    iso = None
+    if isolated is not None:
+        iso = {"note": "kernels timed with the dense MLP in order (not overlapped); "
+                       "not part of value", "kernels": {}}
+        for n, ms in sorted(isolated.items(), key=lambda kv: -kv[1]):
+            c = classify(n)
+            ent = {"avg_ms": round(ms, 4), "class": c}
+            w = work.get(c)
+            if w and ms > 0:
+                if w["flops"] / max(w["bytes"], 1.0) > ridge:
+                    ent["tflops"] = round(w["flops"] / (ms / 1e3) / 1e12, 1)
+                    ent["mfma_frac"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+                else:
+                    ent["gbs"] = round(w["bytes"] / (ms / 1e3) / 1e9, 1)
+                    ent["hbm_frac"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+            iso["kernels"][n] = ent
+
     res = {
         "metric": ("MoE-layer training (forward + backward) tokens/s" if args.train else
                    "MoE-layer backward tokens/s" if args.backward else METRIC),
@@ -637,6 +678,7 @@ def run_workload(name, args, headline=True):
                         k["launches"] // survey_steps, "class": k["class"]}
                     for n, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "cold_cache": cold,
+        "isolated": iso,
         "cpu_baseline": None,
     }
     ref_route = None
@@ -657,6 +699,49 @@ def run_workload(name, args, headline=True):
 
 
 SUB_WORKLOADS = ("tiny_f32", "moe128_350m", "decode_top2", "skewed_top2_int8")
+
+
+def stats_summary(args):
+    """Per-kernel calls, average / min / max duration and share of the traced
+    GPU time from a rocprofv3 kernel_stats.csv; torch's own kernels (input
+    generation and copies) are named generically."""
+    import csv
+    rows = []
+    with open(args.stats_summary) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"]), float(r["Percentage"]), r["Name"]))
+    rows.sort(key=lambda t: -t[4])
+    # median launch duration from the per-launch trace beside the stats file
+    # (robust to the few launches of another kind in the run, e.g. the
+    # overlapped layer's isolated survey steps)
+    med = {}
+    trace = os.path.join(os.path.dirname(args.stats_summary),
+                         os.path.basename(args.stats_summary).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(trace):
+        per = {}
+        with open(trace) as fh:
+            for r in csv.DictReader(fh):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+        for n, v in per.items():
+            v.sort()
+            med[n] = v[len(v) // 2]
+    lines = [f"# rocprofv3 kernel statistics -- {args.label}, workload {args.workload}",
+             f"# command: {args.command}",
+             "# ($REPO is the repository root)",
+             f"source_hash: {src_hash()}",
+             "# columns: calls, average ns, median ns, min ns, max ns, share of traced GPU time, "
+             "kernel", ""]
+    for calls, avg, mn, mx, pct, name in rows:
+        md = med.get(name, float("nan"))
+        if name.startswith("void at::") or name.startswith("at::"):
+            name = name.split("<")[0] + "<...> (torch input generation / copies)"
+        lines.append(f"{calls:6d} {avg:12.0f} {md:12.0f} {mn:12.0f} {mx:12.0f} {pct:6.2f}%  "
+                     f"{name[:160]}")
+    dst = os.path.join(ROOT, "profiles", f"{args.label}__{args.workload}__kernel_stats.txt")
+    open(dst, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines[:12]))
 
 
 def sq_summary(args):
@@ -680,6 +765,7 @@ def sq_summary(args):
     mean = {c: sum(v) / len(v) for c, v in vals.items()}
     lines = [f"# rocprofv3 SQ counters -- kernel {args.label}, workload {args.workload}",
              f"# command: {args.command}",
+             "# ($REPO is the repository root)",
              f"source_hash: {src_hash()}",
              f"symbol_regex: {args.symbol}",
              "# mean per dispatch, summed over the chip as rocprofv3 reports them"]
@@ -709,6 +795,8 @@ def main():
         return pmc_summary(args)
     if args.sq_summary:
         return sq_summary(args)
+    if args.stats_summary:
+        return stats_summary(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the expert-parallel all-to-all across GPUs is not part of it)", file=sys.stderr)
