@@ -493,23 +493,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 // lane with permlane32 swaps of the halves, which avoids the two-way bank
 // conflict of the 8-byte reads, measured 1-1.5% slower.)  Requires
 // K % 1024 == 0 and N % BN == 0.
-// Fragments past the group's valid rows skip their reads and MFMAs, so a
-// partly filled tile costs MFMA time at 32-row granularity.
+// Waves whose row band lies past the group's valid rows skip their LDS reads,
+// dequantisation and MFMAs (they still move their share of the DMA).
 __device__ __forceinline__ int swz_q(int R) { return (R >> 2) & 3; }
 
 // queue entry flag of the int8 schedule: the group runs light tiles
 constexpr int kLightGroup = 0x10000;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two codes (bytes b and b + 1 of w, already offset by 128) -> a packed bf16 pair
+__device__ __forceinline__ uint32_t dequant2(uint32_t w, int b, float sc, float nsc) {
+  const f32x2 v = {fmaf((float)((w >> (8 * b)) & 0xffu), sc, nsc),
+                   fmaf((float)((w >> (8 * b + 8)) & 0xffu), sc, nsc)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ bf16x8 dequant8(uint32_t lo, uint32_t hi, float sc, float nsc) {
   lo ^= 0x80808080u;  // q + 128 in each byte
   hi ^= 0x80808080u;
-  bf16x8 r;
-#pragma unroll
-  for (int b = 0; b < 4; b++) {
-    r[b] = (bf16)fmaf((float)((lo >> (8 * b)) & 0xffu), sc, nsc);
-    r[4 + b] = (bf16)fmaf((float)((hi >> (8 * b)) & 0xffu), sc, nsc);
-  }
-  return r;
+  const u32x4 r = {dequant2(lo, 0, sc, nsc), dequant2(lo, 2, sc, nsc), dequant2(hi, 0, sc, nsc),
+                   dequant2(hi, 2, sc, nsc)};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // LDS bytes of an int8 tile: NS stages of activations and codes, and two
@@ -535,7 +541,9 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
   constexpr int STAGE = ASTAGE + BN * BROWB;
   constexpr int SCB = BN * 16;                  // one scale block (8 groups)
   constexpr int SC_CH = SCB / 1024;
-  static_assert(A_PW * W == A_CH && B_PW * W == B_CH && TM >= 1 && TN >= 1 && SC_CH <= W, "tile");
+  constexpr int SC_PW = (SC_CH + W - 1) / W;  // scale chunks per wave
+  static_assert(A_PW * W == A_CH && B_PW * W == B_CH && TM >= 1 && TN >= 1 &&
+                    (SC_CH <= W || SC_PW * W == SC_CH), "tile");
   static_assert(NS >= 2 && NS * STAGE + 2 * SCB <= 160 * 1024, "LDS budget");
   static_assert((NS - 2) * CPW < 64, "vmcnt range");
   static_assert(i8_lds_bytes<BM, BN, NS>() == NS * STAGE + 2 * SCB, "LDS size");
@@ -573,7 +581,9 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
     const int R = 16 * (wave * B_PW + i) + lane / 4, slot = lane % 4;
     voffb[i] = (uint32_t)((int64_t)R * K + ((slot ^ swz_q(R)) << 4));
   }
-  const uint32_t soff = (uint32_t)((64 * wave + lane) * KG * 2);  // scale chunk of wave < SC_CH
+  uint32_t soff[SC_PW];  // scale chunks wave + W * i (64 weight rows each)
+#pragma unroll
+  for (int i = 0; i < SC_PW; i++) soff[i] = (uint32_t)((64 * (wave + W * i) + lane) * KG * 2);
   const uint32_t dsta = lds0 + wave * A_PW * 1024;
   const uint32_t dstb = lds0 + ASTAGE + wave * B_PW * 1024;
   auto issue = [&](int st, int kt) __attribute__((always_inline)) {
@@ -587,9 +597,11 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
       dma16<false>(gb, voffb[i], __builtin_amdgcn_readfirstlane(dstb + st * STAGE + i * 1024));
   };
   auto issue_scales = [&](int blk) __attribute__((always_inline)) {
-    if (wave < SC_CH)
-      dma16<false>(Sbase + blk * 16, soff,
-                   __builtin_amdgcn_readfirstlane(lds_sc + (blk & 1) * SCB + wave * 1024));
+#pragma unroll
+    for (int i = 0; i < SC_PW; i++)
+      if (wave + W * i < SC_CH)
+        dma16<false>(Sbase + blk * 16, soff[i],
+                     __builtin_amdgcn_readfirstlane(lds_sc + (blk & 1) * SCB + (wave + W * i) * 1024));
   };
 
   f32x16 acc[TM][TN];
@@ -601,63 +613,123 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
   const int wm = wave / WN, wn = wave % WN;
-  const int ksteps = K / BK;
-  const int live = live_frags<TM>(rows - m0 - wm * WTM);
-  issue_scales(0);
+  const int ksteps = K / BK;  // at least 16 (K % 1024 == 0)
+  // waves of a row band past the group's valid rows skip LDS reads and MFMAs
+  const bool act = WM == 1 || live_frags<TM>(rows - m0 - wm * WTM) > 0;
+
+  // Schedule of one K step (four 16-wide sub-steps s = 0..3): the MFMAs of
+  // sub-step s run from registers while the operands of s + 1 are read from
+  // LDS and its codes dequantised (one packed pair per MFMA, interleaved), so
+  // the wave's VALU and LDS work overlaps its MFMAs.  The workgroup barrier
+  // sits between sub-steps 2 and 3: by then every wave has read all of this
+  // stage, so the DMA of stage kt + NS can go into its buffer, and sub-step 3
+  // already reads the next stage -- no exposed prologue per K step.
+  constexpr int SS = BK / 16;
+  static_assert(SS == 4, "four sub-steps per K step");
+  bf16x8 af[2][TM], bfr[2][TN];
+  uint32_t qv[2][TN][2];  // codes of sub-step c in qv[c & 1], read two sub-steps ahead
+  float sc[TN], nsc[TN];
+  auto rd_a = [&](const char *sa, int st, bf16x8 *dst) __attribute__((always_inline)) {
+    const int c = 2 * st + (lane >> 5);
 #pragma unroll
-  for (int p = 0; p < NS - 1; p++)
-    if (p < ksteps) issue(p, p);
-  for (int kt = 0; kt < ksteps; kt++) {
-    if (kt + NS - 2 < ksteps)
-      wait_vmcnt<(NS - 2) * CPW>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
-    // the next scale block's buffer was last read in the previous block
-    if ((kt & 15) == 0 && kt + 16 < ksteps) issue_scales((kt >> 4) + 1);
-    if (kt + NS - 1 < ksteps) issue((kt + NS - 1) % NS, kt + NS - 1);
-    if (live == 0) continue;
-    const char *sa = smem + (kt % NS) * STAGE;
-    const char *sb = sa + ASTAGE;
+    for (int i = 0; i < TM; i++) {
+      const int R = wm * WTM + i * 32 + (lane & 31);
+      dst[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
+    }
+  };
+  auto rd_q = [&](const char *sb, int st, uint32_t (*q)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      const int R = wn * WTN + j * 32 + (lane & 31);
+      const uint32_t *qp =
+          (const uint32_t *)(sb + R * BROWB + ((st ^ swz_q(R)) << 4) + 8 * (lane >> 5));
+      q[j][0] = qp[0];
+      q[j][1] = qp[1];
+    }
+  };
+  auto rd_sc = [&](int kt) __attribute__((always_inline)) {
     const char *ss = smem + NS * STAGE + ((kt >> 4) & 1) * SCB + ((kt >> 1) & 7) * 2;
-    float sc[TN], nsc[TN];
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int R = wn * WTN + j * 32 + (lane & 31);
       sc[j] = (float)*(const _Float16 *)(ss + R * 16);
       nsc[j] = -128.f * sc[j];
     }
-    // the MFMA body for LV live fragments, free of branches so that operand
-    // reads and MFMAs can be interleaved; one copy per fragment count
-    auto body = [&](auto LV) __attribute__((always_inline)) {
-      constexpr int L = decltype(LV)::value;
+  };
+  // the MFMAs of one sub-step, with the codes q dequantised into bn
+  auto mma = [&](const bf16x8 *af_, const bf16x8 *bf_, const uint32_t (*q)[2], bf16x8 *bn)
+      __attribute__((always_inline)) {
+    constexpr int NM = TM * TN, NP = 4 * TN;  // MFMAs, packed pairs to dequantise
+    uint32_t x[TN][2];
+    u32x4 o[TN];
 #pragma unroll
-      for (int s = 0; s < BK / 16; s++) {
-        const int c = 2 * s + (lane >> 5);
-        bf16x8 af[L], bfr[TN];
+    for (int j = 0; j < TN; j++) {
+      x[j][0] = q[j][0] ^ 0x80808080u;  // q + 128 in each byte
+      x[j][1] = q[j][1] ^ 0x80808080u;
+    }
 #pragma unroll
-        for (int i = 0; i < L; i++) {
-          const int R = wm * WTM + i * 32 + (lane & 31);
-          af[i] = *(const bf16x8 *)(sa + R * AROWB + ((c ^ swz_slot<64>(R)) << 4));
-        }
+    for (int t = 0; t < NM; t++) {
+      acc[t / TN][t % TN] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[t / TN], bf_[t % TN], acc[t / TN][t % TN], 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < TN; j++) {
-          const int R = wn * WTN + j * 32 + (lane & 31);
-          const uint32_t *qp =
-              (const uint32_t *)(sb + R * BROWB + ((s ^ swz_q(R)) << 4) + 8 * (lane >> 5));
-          bfr[j] = dequant8(qp[0], qp[1], sc[j], nsc[j]);
-        }
-#pragma unroll
-        for (int i = 0; i < L; i++)
-#pragma unroll
-          for (int j = 0; j < TN; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        // keep each sub-step's operands live only for its own MFMAs
-        __builtin_amdgcn_sched_barrier(0);
+      for (int p = t * NP / NM; p < (t + 1) * NP / NM; p++) {
+        const int j = p / 4, w = p % 4;
+        o[j][w] = dequant2(x[j][w >> 1], (w & 1) * 2, sc[j], nsc[j]);
       }
-    };
-    body(std::integral_constant<int, TM>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; j++) bn[j] = __builtin_bit_cast(bf16x8, o[j]);
+  };
+
+  issue_scales(0);
+#pragma unroll
+  for (int p = 0; p < NS; p++) issue(p, p);
+  wait_vmcnt<(NS - 1) * CPW>();
+  __syncthreads();
+  if (act) {
+    rd_sc(0);
+    rd_a(smem, 0, af[0]);
+    rd_q(smem + ASTAGE, 0, qv[0]);
+    rd_q(smem + ASTAGE, 1, qv[1]);
+#pragma unroll
+    for (int j = 0; j < TN; j++) bfr[0][j] = dequant8(qv[0][j][0], qv[0][j][1], sc[j], nsc[j]);
   }
+  for (int kt = 0; kt < ksteps; kt++) {
+    const char *sa = smem + (kt % NS) * STAGE;
+    if (act) {
+      // sub-steps 0..2: read A of s + 1 and the codes of s + 2 (this stage)
+      rd_a(sa, 1, af[1]);
+      rd_q(sa + ASTAGE, 2, qv[0]);
+      mma(af[0], bfr[0], qv[1], bfr[1]);
+      rd_a(sa, 2, af[0]);
+      rd_q(sa + ASTAGE, 3, qv[1]);
+      mma(af[1], bfr[1], qv[0], bfr[0]);
+      rd_a(sa, 3, af[1]);
+      mma(af[0], bfr[0], qv[1], bfr[1]);
+    }
+    // every LDS read of stage kt has returned (its buffer is refilled below)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters open
+    if (kt + NS - 1 < ksteps)
+      wait_vmcnt<(NS - 2) * CPW>();  // stage kt + 1 has landed
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    // the next scale block's buffer was last read in the previous block
+    if ((kt & 15) == 0 && kt + 16 < ksteps) issue_scales((kt >> 4) + 1);
+    if (kt + NS < ksteps) issue(kt % NS, kt + NS);
+    if (act) {
+      // sub-step 3, reading sub-steps 0 and 1 of stage kt + 1 (after the last
+      // K step: a stale but in-bounds buffer whose values are never used)
+      const char *na = smem + ((kt + 1) % NS) * STAGE;
+      rd_sc(kt + 1);
+      rd_a(na, 0, af[0]);
+      rd_q(na + ASTAGE, 0, qv[0]);
+      rd_q(na + ASTAGE, 1, qv[1]);
+      mma(af[1], bfr[1], qv[0], bfr[0]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // the last (unused) reads, before the epilogue's writes
 
   // epilogue as in gemm_dma_kernel
   constexpr int CROW = BN * 2 + 16;
@@ -669,9 +741,9 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
   } else {
     for (int band = 0; band < WM; band++) {
       __syncthreads();
-      if (wm == band) {
+      if (WM == 1 || wm == band) {
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++) {
 #pragma unroll
           for (int j = 0; j < TN; j++)
 #pragma unroll
@@ -682,6 +754,10 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
               if (GELU) v = gelu_f(v);
               *(bf16 *)(smem + R * CROW + Cc * 2) = (bf16)v;
             }
+          // one fragment at a time: keeps the accumulators' copies out of
+          // the VGPRs the K loop needs (no spills with 256-row wave tiles)
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __syncthreads();
       const int64_t r0 = m0 + band * WTM;
