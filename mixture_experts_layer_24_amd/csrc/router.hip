@@ -30,13 +30,15 @@ constexpr int RBM = 64;  // tokens per block
 
 
 // L: LDS logits tile [RBM][ldl] fp32 (bias not yet added).  SL = expert
-// slots per lane (E <= 64 SL): lane l holds experts l, l + 64, ...
-template <int MAXK, int SL>
+// slots per lane (E <= 64 SL): lane l holds experts l, l + 64, ...  NWV
+// waves, RBM / NWV token rows each; per-wave partials summed in wave order.
+template <int MAXK, int SL, int NWV = 4>
 __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
                                 float (*qpart)[256], int *fcnt, int *hcnt, int blk) {
+  static_assert(RBM % NWV == 0, "rows per wave");
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int E = a.E, k = a.k;
-  __shared__ float zw[4];
+  __shared__ float zw[NWV];
   float q[SL];
   float zacc = 0.f;
   float bias[SL];
@@ -46,8 +48,10 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
     const int e = lane + kWave * i;
     bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
   }
-  for (int rr = 0; rr < RBM / 4; rr++) {
-    const int r = wave * (RBM / 4) + rr;
+  for (int rr = 0; rr < RBM / NWV; rr++) {
+    // 4 waves: 16 consecutive rows each; more waves: rows dealt round-robin,
+    // so a partly filled block (decode) still keeps every wave busy
+    const int r = NWV == 4 ? wave * (RBM / 4) + rr : rr * NWV + wave;
     const int64_t t = (int64_t)blk * RBM + r;
     if (t >= a.T) break;
     float v[SL];
@@ -153,11 +157,19 @@ __device__ void router_epilogue(const RouterArgs &a, const float *L, int ldl,
   }
   if (lane == 0) zw[wave] = zacc;
   __syncthreads();
-  if (a.zpart && threadIdx.x == 0) a.zpart[blk] = ((zw[0] + zw[1]) + zw[2]) + zw[3];
+  if (a.zpart && threadIdx.x == 0) {
+    float z = zw[0];
+#pragma unroll
+    for (int w = 1; w < NWV; w++) z += zw[w];
+    a.zpart[blk] = z;
+  }
   const int e = threadIdx.x;
   if (e < E) {
     const int64_t o = (int64_t)e * gridDim.x + blk;  // expert-major [E][nblk]
-    a.qsum[o] = ((qpart[0][e] + qpart[1][e]) + qpart[2][e]) + qpart[3][e];
+    float q = qpart[0][e];
+#pragma unroll
+    for (int w = 1; w < NWV; w++) q += qpart[w][e];
+    a.qsum[o] = q;
     a.fcount[o] = fcnt[e];
     if (a.hist) a.hist[o] = hcnt[e];
   }
@@ -429,24 +441,42 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
     router_epilogue<8, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
 }
 
-// Split-K router, second step: the partial products of the splits summed in
-// split order (fixed) into slab 0, 4 columns per thread with the loads of
-// every split in flight together (nsplit <= kMaxSplit); the softmax / top-k
-// epilogue then runs on the sums (route_logits_kernel, one wave per token).
+// Split-K router, second step (one block of 16 waves per 64-token block):
+// the partial products of the splits summed in split order (fixed) into an
+// LDS logits tile, 4 columns per thread with the loads of every split in
+// flight together (nsplit <= kMaxSplit), then the softmax / top-k epilogue
+// of the fused router on it, 4 token rows per wave.
 constexpr int kMaxSplit = 16;
-__global__ __launch_bounds__(256) void router_split_sum_kernel(float *part, int nsplit,
-                                                               int64_t slab, int64_t n4) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q >= n4) return;
-  f32x4 v[kMaxSplit];
+template <int MAXK, int SL>
+__global__ __launch_bounds__(1024) void router_split_epi_kernel(RouterArgs a, int nsplit) {
+  constexpr int NWV = 16, LDL = 64 * SL + 4;
+  __shared__ __attribute__((aligned(16))) float L[RBM * LDL];
+  __shared__ float qpart[NWV][256];
+  __shared__ int fcnt[256], hcnt[256];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int Ep = (a.E + 31) & ~31;
+  if (tid < 256) {
+    fcnt[tid] = 0;
+    hcnt[tid] = 0;
+  }
+  const int64_t slab = (int64_t)gridDim.x * RBM * Ep;
+  const float *P = a.part + (int64_t)blk * RBM * Ep;
+  const int64_t left = a.T - (int64_t)blk * RBM;  // rows past T are never read
+  const int nrow = left < RBM ? (int)left : RBM;
+  for (int idx = tid; idx < nrow * Ep / 4; idx += 64 * NWV) {
+    const int r = idx / (Ep / 4), e = 4 * (idx - r * (Ep / 4));
+    f32x4 v[kMaxSplit];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; sp++)
-    if (sp < nsplit) v[sp] = *(const f32x4 *)(part + sp * slab + 4 * q);
-  f32x4 acc = v[0];
+    for (int sp = 0; sp < kMaxSplit; sp++)
+      if (sp < nsplit) v[sp] = *(const f32x4 *)(P + sp * slab + (int64_t)r * Ep + e);
+    f32x4 acc = v[0];
 #pragma unroll
-  for (int sp = 1; sp < kMaxSplit; sp++)
-    if (sp < nsplit) acc += v[sp];
-  *(f32x4 *)(part + 4 * q) = acc;
+    for (int sp = 1; sp < kMaxSplit; sp++)
+      if (sp < nsplit) acc += v[sp];
+    *(f32x4 *)(L + r * LDL + e) = acc;
+  }
+  __syncthreads();
+  router_epilogue<MAXK, SL, NWV>(a, L, LDL, qpart, fcnt, hcnt, blk);
 }
 
 // fp32 activations: plain fp32 dot products (small shapes; correctness path)
@@ -547,26 +577,21 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
       case 3: MOE_LAUNCH("router_split_e192", (router_dma_kernel<3, 4, true>), g, b, 0, s, a); break;
       default: MOE_LAUNCH("router_split_e256", (router_dma_kernel<4, 3, true>), g, b, 0, s, a); break;
     }
-    const int64_t slab = (int64_t)nblk * RBM * Ep, n4 = slab / 4;
-    MOE_LAUNCH("router_split_sum", router_split_sum_kernel, dim3((unsigned)((n4 + 255) / 256)),
-               b, 0, s, a.part, nsplit, slab, n4);
-    RouteVarArgs va{};
-    va.src = a.part;
-    va.ld = Ep;
-    va.bias = a.bias;
-    va.ids = a.ids;
-    va.gates = a.gates;
-    va.logits = a.logits;
-    va.qsum = a.qsum;
-    va.fcount = a.fcount;
-    va.hist = a.hist;
-    va.zpart = a.zpart;
-    va.T = a.T;
-    va.E = a.E;
-    va.k = a.k;
-    va.normalize = a.normalize;
-    va.variant = RV_TOPK;
-    return launch_route_logits(va, s);
+    (void)Ep;
+    const dim3 ge(nblk), be(1024);
+#define MOE_SPLIT_EPI(SL)                                                                  \
+  if (a.k <= 2)                                                                            \
+    MOE_LAUNCH("router_split_epi", (router_split_epi_kernel<2, SL>), ge, be, 0, s, a, nsplit); \
+  else                                                                                     \
+    MOE_LAUNCH("router_split_epi", (router_split_epi_kernel<8, SL>), ge, be, 0, s, a, nsplit);
+    switch (ntw) {
+      case 1: MOE_SPLIT_EPI(1) break;
+      case 2: MOE_SPLIT_EPI(2) break;
+      case 3: MOE_SPLIT_EPI(3) break;
+      default: MOE_SPLIT_EPI(4) break;
+    }
+#undef MOE_SPLIT_EPI
+    return hipGetLastError();
   }
   if (nblk > 0) {
     if (act_bf16) {  // the bf16 path guarantees d % 64 == 0
