@@ -878,33 +878,48 @@ __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, in
     sunit[rk] = unit[tid];
   }
   __syncthreads();
-  if (tid < kWave) {
-    // lane x < 8 keeps XCD x's cost and its heavy and light lists; each group
-    // goes to the lane with the least cost (ties: lower XCD)
-    // (lanes 8..63 shuffle among themselves and never write)
-    const int x = tid;
-    int load = x < 8 ? 0 : 0x7fffffff, nh = 0, nl = 0, uh = 0;
-    for (int i = 0; i < G; i++) {
-      const int u = sunit[i];
-      if (u == 0) break;  // the rest are empty too (cost 0 ranks last)
-      int bl = load, bx = x;
+  // the deal: one thread, the XCD loads in registers; each group goes to the
+  // XCD with the least cost so far (ties: lower XCD)
+  __shared__ int xof[256];
+  if (tid == 0) {
+    int ld[8];
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const int ol = __shfl_xor(bl, o), ox = __shfl_xor(bx, o);
-        if (ol < bl || (ol == bl && ox < bx)) { bl = ol; bx = ox; }
+    for (int x = 0; x < 8; x++) ld[x] = 0;
+    for (int i = 0; i < G; i++) {
+      if (sunit[i] == 0) {  // the rest are empty too (cost 0 ranks last)
+        xof[i] = -1;
+        continue;
       }
-      if (x < 8 && x == bx) {
-        if (u < 0) {
-          ll[x][nl++] = order[i];
-        } else {
-          hl[x][nh] = order[i];
-          hu[x][nh++] = u;
-          uh += u;
+      int bx = 0, bl = ld[0];
+#pragma unroll
+      for (int x = 1; x < 8; x++)
+        if (ld[x] < bl) {
+          bl = ld[x];
+          bx = x;
         }
-        load += scost[i];
+      xof[i] = bx;
+#pragma unroll
+      for (int x = 0; x < 8; x++)
+        if (x == bx) ld[x] += scost[i];
+    }
+  }
+  __syncthreads();
+  if (tid < 8) {
+    // thread x collects XCD x's heavy and light lists in deal order
+    const int x = tid;
+    int nh = 0, nl = 0, uh = 0;
+    for (int i = 0; i < G; i++) {
+      if (xof[i] != x) continue;
+      const int u = sunit[i];
+      if (u < 0) {
+        ll[x][nl++] = order[i];
+      } else {
+        hl[x][nh] = order[i];
+        hu[x][nh++] = u;
+        uh += u;
       }
     }
-    if (x < 8) {
+    {
       // merge: a light group comes next while the share of light groups
       // placed is below the share of heavy length placed
       int32_t *lst = xs + 8 + x * G, *pre = xs + 8 + 8 * G + x * (G + 1);
