@@ -307,27 +307,33 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
 // bytes with the 16-byte chunks XOR-swizzled as in the GEMMs.  The K order
 // of the MFMAs is that of router_bf16_kernel: identical logits.  One weight
 // matrix (SCORES with two matrices uses router_bf16_kernel).
-template <int NTW, int NS, bool SCORES = false>
-__global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
+template <int NTW, int NS, bool SCORES = false, int NWR = 4>
+__global__ __launch_bounds__(64 * NWR) void router_dma_kernel(RouterArgs a) {
+  static_assert(NWR == 4 || NWR == 8, "waves");
   constexpr int EPMAX = 64 * NTW;
+  constexpr int NT = 2 * NTW;                       // 32-wide expert tiles
+  constexpr int TPW = (NT + NWR / 2 - 1) / (NWR / 2);  // expert tiles per wave
   constexpr int ROWB = 128;                         // bytes per tile row (64 bf16)
   constexpr int STAGE = (RBM + EPMAX) * ROWB;
-  constexpr int A_PW = RBM * ROWB / 1024 / 4;       // 1 KB chunks per wave per stage
-  constexpr int W_PW = EPMAX * ROWB / 1024 / 4;
+  constexpr int A_PW = RBM * ROWB / 1024 / NWR;     // 1 KB chunks per wave per stage
+  constexpr int W_PW = EPMAX * ROWB / 1024 / NWR;
   constexpr int CPW = A_PW + W_PW;
+  static_assert(A_PW * NWR * 1024 == RBM * ROWB && W_PW * NWR * 1024 == EPMAX * ROWB, "chunks");
   constexpr int LOGIT_BYTES = RBM * (EPMAX + 4) * 4;
   constexpr int SMEM = NS * STAGE > LOGIT_BYTES ? NS * STAGE : LOGIT_BYTES;
   static_assert(NS >= 2 && (NS - 2) * CPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  __shared__ float qpart[4][256];
+  __shared__ float qpart[NWR][256];
   __shared__ int fcnt[256], hcnt[256];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int blk = blockIdx.x;
   const int E = a.E, Ep = (E + 31) & ~31, d = a.d;
-  fcnt[tid] = 0;
-  hcnt[tid] = 0;
+  if (tid < 256) {
+    fcnt[tid] = 0;
+    hcnt[tid] = 0;
+  }
   const int64_t t0 = (int64_t)blk * RBM;
   const char *Xb = (const char *)a.x + t0 * d * 2;
   const char *Wb = (const char *)a.w;
@@ -361,11 +367,17 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
       dma16<false>(gw, voffw[i], __builtin_amdgcn_readfirstlane(dstw + st * STAGE + i * 1024));
   };
 
-  f32x16 acc[NTW];
+  f32x16 acc[TPW];
 #pragma unroll
-  for (int i = 0; i < NTW; i++)
+  for (int i = 0; i < TPW; i++)
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
+  // expert tile i of this wave (clamped to the last tile: a wave with fewer
+  // tiles than TPW multiplies a copy and never stores it)
+  auto tile_of = [&](int i) __attribute__((always_inline)) {
+    const int nt = (wave >> 1) + (NWR / 2) * i;
+    return nt < NT ? nt : NT - 1;
+  };
 
   const int mt = wave & 1;  // 32-row half of the token tile
   // K range of this block: all of d, or (split K, gridDim.y > 1) its share
@@ -394,8 +406,8 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
       const int Ra = mt * 32 + (lane & 31);
       const bf16x8 av = *(const bf16x8 *)(sa + Ra * ROWB + ((c ^ swz_slot<64>(Ra)) << 4));
 #pragma unroll
-      for (int i = 0; i < NTW; i++) {
-        const int Rw = ((wave >> 1) + 2 * i) * 32 + (lane & 31);
+      for (int i = 0; i < TPW; i++) {
+        const int Rw = tile_of(i) * 32 + (lane & 31);
         const bf16x8 bv = *(const bf16x8 *)(sw + Rw * ROWB + ((c ^ swz_slot<64>(Rw)) << 4));
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
       }
@@ -405,9 +417,9 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
   float *L = (float *)smem;
   const int ldl = EPMAX + 4;
 #pragma unroll
-  for (int i = 0; i < NTW; i++) {
-    const int nt = (wave >> 1) + 2 * i;
-    if (nt * 32 < Ep) {
+  for (int i = 0; i < TPW; i++) {
+    const int nt = (wave >> 1) + (NWR / 2) * i;
+    if (nt < NT && nt * 32 < Ep) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int m = mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -422,13 +434,13 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
     // columns past E hold products of the clamped weight row)
     if (ns > 1) {
       float *P = a.part + ((int64_t)blockIdx.y * gridDim.x * RBM + t0) * Ep;
-      for (int idx = tid; idx < RBM * Ep / 4; idx += 256) {
+      for (int idx = tid; idx < RBM * Ep / 4; idx += 64 * NWR) {
         const int r = idx / (Ep / 4), e = 4 * (idx - r * (Ep / 4));
         *(f32x4 *)(P + (int64_t)r * Ep + e) = *(const f32x4 *)(L + r * ldl + e);
       }
       return;
     }
-    for (int idx = tid; idx < RBM * E; idx += 256) {
+    for (int idx = tid; idx < RBM * E; idx += 64 * NWR) {
       const int r = idx / E, e = idx - (idx / E) * E;
       const int64_t t = t0 + r;
       if (t < a.T) a.logits[t * E + e] = L[r * ldl + e];
@@ -436,9 +448,9 @@ __global__ __launch_bounds__(256) void router_dma_kernel(RouterArgs a) {
     return;
   }
   if (a.k <= 2)
-    router_epilogue<2, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<2, NTW, NWR>(a, L, ldl, qpart, fcnt, hcnt, blk);
   else
-    router_epilogue<8, NTW>(a, L, ldl, qpart, fcnt, hcnt, blk);
+    router_epilogue<8, NTW, NWR>(a, L, ldl, qpart, fcnt, hcnt, blk);
 }
 
 // Split-K router, second step (one block of 16 waves per 64-token block):
@@ -596,12 +608,14 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (nblk > 0) {
     if (act_bf16) {  // the bf16 path guarantees d % 64 == 0
       const int ntw = ((a.E + 31) / 32 + 1) / 2;
-      const dim3 g(nblk), b(256);
+      const dim3 g(nblk), b(512);
       switch (ntw) {
-        case 1: MOE_LAUNCH("router_bf16_e64", (router_dma_kernel<1, 4>), g, b, 0, s, a); break;
-        case 2: MOE_LAUNCH("router_bf16_e128", (router_dma_kernel<2, 4>), g, b, 0, s, a); break;
-        case 3: MOE_LAUNCH("router_bf16_e192", (router_dma_kernel<3, 4>), g, b, 0, s, a); break;
-        default: MOE_LAUNCH("router_bf16_e256", (router_dma_kernel<4, 3>), g, b, 0, s, a); break;
+        case 1:  // E <= 64: four waves (half of eight would only repeat tiles)
+          MOE_LAUNCH("router_bf16_e64", (router_dma_kernel<1, 4>), g, dim3(256), 0, s, a);
+          break;
+        case 2: MOE_LAUNCH("router_bf16_e128", (router_dma_kernel<2, 4, false, 8>), g, b, 0, s, a); break;
+        case 3: MOE_LAUNCH("router_bf16_e192", (router_dma_kernel<3, 4, false, 8>), g, b, 0, s, a); break;
+        default: MOE_LAUNCH("router_bf16_e256", (router_dma_kernel<4, 3, false, 8>), g, b, 0, s, a); break;
       }
     } else {
       MOE_LAUNCH("router_f32", router_f32_kernel<false>, dim3(nblk), dim3(256), 0, s, a);
