@@ -40,37 +40,42 @@ __device__ __forceinline__ float phi_cdf(float z) { return 0.5f * erfcf(-z * 0.7
 // other experts (the (k+1)-th overall when e is kept, the k-th otherwise);
 // otherwise 1 for a taken expert, 0 else.  No float atomics: every per-expert
 // sum is owned by one lane and summed over the waves in a fixed order.
-template <int MAXK>
+// SL expert slots per lane (E <= 64 SL); VAR: RV_TOPK (also the cosine
+// router, whose logits come precomputed), RV_TOP_P or RV_NOISY.  Rows are
+// dealt round-robin over the waves, so a partly filled block keeps every
+// wave busy.
+template <int MAXK, int SL, int VAR>
 __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
   __shared__ float qpart[VW][256], ipart[VW][256], lpart[VW][256];
   __shared__ int fcnt[256], hcnt[256];
   __shared__ float zw[VW];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, blk = blockIdx.x;
   const int E = a.E, k = a.k;
-  const bool noisy = a.variant == RV_NOISY, topp = a.variant == RV_TOP_P;
+  constexpr bool noisy = VAR == RV_NOISY, topp = VAR == RV_TOP_P;
   const int ns = a.ld ? a.ld : (noisy ? 2 * E : E);
   if (tid < 256) {
     fcnt[tid] = 0;
     hcnt[tid] = 0;
   }
   __syncthreads();
-  float q[4] = {0.f, 0.f, 0.f, 0.f}, imp[4] = {0.f, 0.f, 0.f, 0.f}, ld[4] = {0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f, bias[4];
+  float q[SL], imp[SL], ld[SL];
+  float zacc = 0.f, bias[SL];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < SL; i++) {
     const int e = lane + kWave * i;
+    q[i] = imp[i] = ld[i] = 0.f;
     bias[i] = (a.bias && e < E) ? a.bias[e] : 0.f;
   }
   const bool renorm = noisy ? true : (topp ? a.normalize != 0 : (k >= 2 && a.normalize));
   // the wave's rows of scores (and noise) are loaded before the first row is
   // worked on, so their latencies overlap
   constexpr int RPW = VBT / VW;
-  float src0[RPW][4], src1[RPW][4], nz[RPW][4];
+  float src0[RPW][SL], src1[RPW][SL], nz[RPW][SL];
 #pragma unroll
   for (int rr = 0; rr < RPW; rr++) {
-    const int64_t t = (int64_t)blk * VBT + wave * RPW + rr;
+    const int64_t t = (int64_t)blk * VBT + rr * VW + wave;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < SL; i++) {
       const int e = lane + kWave * i;
       src0[rr][i] = src1[rr][i] = nz[rr][i] = 0.f;
       if (t < a.T && e < E) {
@@ -84,13 +89,13 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
   }
 #pragma unroll
   for (int rr = 0; rr < RPW; rr++) {
-    const int r = wave * RPW + rr;
+    const int r = rr * VW + wave;
     const int64_t t = (int64_t)blk * VBT + r;
     if (t >= a.T) break;
-    float v[4], clean[4], sig[4];
-    bool live[4];
+    float v[SL], clean[SL], sig[SL];
+    bool live[SL];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < SL; i++) {
       const int e = lane + kWave * i;
       live[i] = e < E;
       clean[i] = 0.f;
@@ -106,10 +111,13 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
         if (a.logits) a.logits[t * E + e] = v[i];
       }
     }
-    float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    float p[4], s = 0.f;
+    float m = v[0];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 1; i < SL; i++) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    float p[SL], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < SL; i++) {
       p[i] = live[i] ? expf(v[i] - m) : 0.f;
       s += p[i];
     }
@@ -119,11 +127,13 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
       zacc += lz * lz;
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < SL; i++) {
       p[i] = p[i] / s;
       q[i] += p[i];
     }
-    bool taken[4] = {false, false, false, false};
+    bool taken[SL];
+#pragma unroll
+    for (int i = 0; i < SL; i++) taken[i] = false;
     int sel[MAXK];
     float selp[MAXK], thr_out = neg_inf();
     int n = 0;
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
         float bv = neg_inf();
         int be = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < SL; i++) {
           const int e = lane + kWave * i;
           if (live[i] && !taken[i] && (be == 0x7fffffff || v[i] > bv)) {
             bv = v[i];
@@ -156,9 +166,9 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
         } else {
           const int oi = be / kWave;
           float pi = p[0];
-          if (oi == 1) pi = p[1];
-          if (oi == 2) pi = p[2];
-          if (oi == 3) pi = p[3];
+#pragma unroll
+          for (int i = 1; i < SL; i++)
+            if (oi == i) pi = p[i];
           pi = lane_f(pi, be % kWave);  // be is wave-uniform
           sel[j] = be;
           selp[j] = pi;
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
           n = j + 1;
           cum += pi;
 #pragma unroll
-          for (int i = 0; i < 4; i++)
+          for (int i = 0; i < SL; i++)
             if (lane + kWave * i == be) taken[i] = true;
           if (topp && cum > a.top_p) stop = true;
         }
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
         if ((e & (kWave - 1)) == lane) {
           const int oi = e / kWave;
 #pragma unroll
-          for (int i = 0; i < 4; i++)
+          for (int i = 0; i < SL; i++)
             if (i == oi) imp[i] += gj;
         }
       }
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
     }
     if (a.loadp) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < SL; i++) {
         if (!live[i]) continue;
         float P;
         if (noisy) {
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < SL; i++) {
     const int e = lane + kWave * i;
     if (e < E) {
       qpart[wave][e] = q[i];
@@ -397,13 +407,33 @@ __global__ __launch_bounds__(1024) void cov_loss_kernel(const float *imp, const 
 namespace moe_host {
 using namespace moe;
 
+template <int MAXK, int SL>
+static void launch_route_logits_sl(const RouteVarArgs &a, int nblk, hipStream_t s) {
+  const dim3 g(nblk), b(64 * VW);
+  if (a.variant == RV_NOISY)
+    MOE_LAUNCH("route_logits", (route_logits_kernel<MAXK, SL, RV_NOISY>), g, b, 0, s, a);
+  else if (a.variant == RV_TOP_P)
+    MOE_LAUNCH("route_logits", (route_logits_kernel<MAXK, SL, RV_TOP_P>), g, b, 0, s, a);
+  else
+    MOE_LAUNCH("route_logits", (route_logits_kernel<MAXK, SL, RV_TOPK>), g, b, 0, s, a);
+}
+
+template <int MAXK>
+static void launch_route_logits_k(const RouteVarArgs &a, int nblk, hipStream_t s) {
+  const int sl = (a.E + kWave - 1) / kWave;
+  if (sl <= 1) launch_route_logits_sl<MAXK, 1>(a, nblk, s);
+  else if (sl == 2) launch_route_logits_sl<MAXK, 2>(a, nblk, s);
+  else if (sl == 3) launch_route_logits_sl<MAXK, 3>(a, nblk, s);
+  else launch_route_logits_sl<MAXK, 4>(a, nblk, s);
+}
+
 hipError_t launch_route_logits(const RouteVarArgs &a, hipStream_t s) {
   const int nblk = router_blocks(a.T);
   if (nblk <= 0) return hipGetLastError();
   if (a.k <= 2)
-    MOE_LAUNCH("route_logits", route_logits_kernel<2>, dim3(nblk), dim3(64 * VW), 0, s, a);
+    launch_route_logits_k<2>(a, nblk, s);
   else
-    MOE_LAUNCH("route_logits", route_logits_kernel<8>, dim3(nblk), dim3(64 * VW), 0, s, a);
+    launch_route_logits_k<8>(a, nblk, s);
   return hipGetLastError();
 }
 
