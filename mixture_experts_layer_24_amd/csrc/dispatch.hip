@@ -127,6 +127,17 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
                                                             float aux_alpha, float *aux,
                                                             const int32_t *load, int32_t *seg) {
   const int lane = lane_id(), blk = blockIdx.x, nblk = gridDim.x;
+  // this block's offsets and its first 64 assignments are loaded before
+  // anything else, so their latencies overlap the aux sum and the scan below
+  int run0 = 0, run1 = 0, run2 = 0, run3 = 0;
+  if (lane < E) run0 = offs[(int64_t)lane * nblk + blk];
+  if (lane + 64 < E) run1 = offs[(int64_t)(lane + 64) * nblk + blk];
+  if (lane + 128 < E) run2 = offs[(int64_t)(lane + 128) * nblk + blk];
+  if (lane + 192 < E) run3 = offs[(int64_t)(lane + 192) * nblk + blk];
+  const int64_t a0 = (int64_t)blk * DBT * k;
+  int64_t a1 = a0 + (int64_t)DBT * k;
+  if (a1 > T * k) a1 = T * k;
+  int e_next = (a0 + lane < a1) ? ids[a0 + lane] : -1;
   // the layer's aux loss is finished here, by block 0, when asked
   if (aux && blk == 0) aux_sum_wave(aux_term, E, aux_alpha, aux);
   // segment base of expert lane + 64 i (gate priority)
@@ -151,21 +162,12 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
       carry += __shfl(inc, kWave - 1, kWave);
     }
   }
-  // running slot of expert e = lane + 64 i, starting at this block's offset
-  int run0 = 0, run1 = 0, run2 = 0, run3 = 0;
-  {
-    if (lane < E) run0 = offs[(int64_t)lane * nblk + blk];
-    if (lane + 64 < E) run1 = offs[(int64_t)(lane + 64) * nblk + blk];
-    if (lane + 128 < E) run2 = offs[(int64_t)(lane + 128) * nblk + blk];
-    if (lane + 192 < E) run3 = offs[(int64_t)(lane + 192) * nblk + blk];
-  }
-  const int64_t a0 = (int64_t)blk * DBT * k;
-  int64_t a1 = a0 + (int64_t)DBT * k;
-  if (a1 > T * k) a1 = T * k;
+  // run0..run3: running slot of expert e = lane + 64 i, from this block's offset
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = a0; base < a1; base += 64) {
     const int64_t a = base + lane;
-    int e = (a < a1) ? ids[a] : -1;
+    int e = e_next;
+    if (base + 64 < a1) e_next = (a + 64 < a1) ? ids[a + 64] : -1;  // next chunk's ids
     const bool valid = e >= 0 && e < E;
     if (!valid) e = -1;
     int slot = -1, ebase = 0;

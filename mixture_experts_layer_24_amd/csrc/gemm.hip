@@ -480,18 +480,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
 // DMA-pipelined GEMM with int8 weights (symmetric codes q, one fp16 scale s
 // per 128 consecutive K elements of a weight row; weight = s * q).
 // The activations (bf16, 128-byte tile rows) and the int8 codes (64-byte
-// tile rows: one 64-wide K step) both travel global -> LDS by DMA, NS - 1 K
-// steps ahead, exactly like gemm_dma_kernel; the scales of the tile's BN
-// weight rows arrive by DMA in blocks of 8 groups (1024 K elements, 16 bytes
-// per row), double-buffered.  Each wave turns its own B fragments into bf16
-// in registers just before the MFMAs: bf16(s * q) with s * q rounded once
+// tile rows: one 64-wide K step) both travel global -> LDS by DMA into NS
+// stage buffers, as in gemm_dma_kernel; the scales of the tile's BN weight
+// rows arrive by DMA in blocks of 8 groups (1024 K elements, 16 bytes per
+// row), double-buffered.  Each wave turns its own B fragments into bf16 in
+// registers, one sub-step ahead of the MFMAs that use them (the schedule of
+// a K step is described at the loop): bf16(s * q) with s * q rounded once
 // to fp32 (computed as fma(q + 128, s, -128 s), which is exact up to that
 // one rounding), so the arithmetic is that of a bf16 GEMM on the
 // dequantised weights and half the weight bytes cross LDS.
 // Code tile rows: chunk c (16 codes) of row R sits in slot c ^ ((R >> 2) & 3),
 // which spreads 16 consecutive rows over all 64 banks.  (One 16-byte read per
 // lane with permlane32 swaps of the halves, which avoids the two-way bank
-// conflict of the 8-byte reads, measured 1-1.5% slower.)  Requires
+// conflict of the 8-byte reads, measured 1-3% slower.)  Requires
 // K % 1024 == 0 and N % BN == 0.
 // Waves whose row band lies past the group's valid rows skip their LDS reads,
 // dequantisation and MFMAs (they still move their share of the DMA).
