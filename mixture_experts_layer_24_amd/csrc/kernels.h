@@ -42,7 +42,6 @@ struct RouteVarArgs {
   int64_t T;
   int E, k, normalize, variant;
   float top_p;
-  int ld;  // row stride of src (0 = its column count: E, or 2E for noisy)
 };
 
 // Grouped "NT" GEMM: for each group g < G and row m < rows[g] (or M_cap):

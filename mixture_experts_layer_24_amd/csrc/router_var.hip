@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * VW) void route_logits_kernel(RouteVarArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, blk = blockIdx.x;
   const int E = a.E, k = a.k;
   constexpr bool noisy = VAR == RV_NOISY, topp = VAR == RV_TOP_P;
-  const int ns = a.ld ? a.ld : (noisy ? 2 * E : E);
+  const int ns = noisy ? 2 * E : E;  // row stride of the scores
   if (tid < 256) {
     fcnt[tid] = 0;
     hcnt[tid] = 0;
