@@ -836,9 +836,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_sched_kernel(GemmArg
 
 // Schedule of the int8 tiles over the 8 XCDs.  A group with at most 64 rows
 // runs light tiles when `light` (both GEMMs' N multiples of 512) and costs
-// LIGHT_COST; another group's cost is its 256-row tiles in 32-row fragments
-// (at least 4 per tile: a tile with few rows still streams its weight slab)
-// -- costs per 256 output columns.  Groups are taken largest first and each
+// LIGHT_COST; another group's cost is the sum over its 256-row tiles of 8
+// for a tile with more than 128 rows (both row bands of waves busy) and 5
+// for one with at most 128 (one band does the tile's MFMAs and
+// dequantisation, the other only its share of the DMA) -- costs per 256
+// output columns, after the tile times measured on the skewed int8 workload
+// relative to a full tile: 0.71 (layer 1) and 0.58 (layer 2) for a one-band
+// tile, 0.42 per 256 columns for a light 64 x 512 tile.  Groups are taken largest first and each
 // goes to the XCD with the least cost so far; each XCD's queue then
 // interleaves its light groups (weight streaming) evenly among its other
 // groups (mostly MFMA work) by queue length.  Output (int32): [0, 8) queue
@@ -848,7 +852,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_i8_sched_kernel(GemmArg
 // workgroup of 256 threads, G <= 256.
 __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, int G, int64_t M_cap,
                                                          int light, int32_t *xs) {
-  constexpr int BM = 256, FLOOR = 4, LIGHT_ROWS = 64, LIGHT_COST = 2;
+  constexpr int BM = 256, LIGHT_ROWS = 64, LIGHT_COST = 3, COST_TWO_BANDS = 8, COST_ONE_BAND = 5;
   __shared__ int cost[256], unit[256], order[256], scost[256], sunit[256];
   __shared__ int hl[8][256], ll[8][256], hu[8][256];
   const int tid = threadIdx.x;
@@ -862,8 +866,7 @@ __global__ __launch_bounds__(256) void tile_sched_kernel(const int32_t *rows, in
       const int v = (int)((r + BM - 1) / BM);
       for (int t = 0; t < v; t++) {
         const int64_t rt = r - (int64_t)t * BM < BM ? r - (int64_t)t * BM : BM;
-        const int f = (int)((rt + 31) / 32);
-        c += f > FLOOR ? f : FLOOR;
+        c += rt > BM / 2 ? COST_TWO_BANDS : COST_ONE_BAND;
       }
       u = 2 * v;
     }
