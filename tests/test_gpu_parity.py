@@ -131,7 +131,14 @@ def test_layer_small_all_outputs(wl):
     ("f32", 64, 32, 4, 1, False), ("f32", 100, 40, 7, 2, True),
     ("bf16", 100, 128, 5, 1, False), ("bf16", 300, 256, 64, 2, False),
     ("bf16", 257, 128, 128, 1, True), ("bf16", 130, 64, 200, 3, False),
-    ("bf16", 65, 64, 256, 2, True), ("bf16", 1, 64, 32, 1, False)])
+    ("bf16", 65, 64, 256, 2, True), ("bf16", 1, 64, 32, 1, False),
+    # eight-wave fused router with three 64-expert slots per lane
+    ("bf16", 257, 128, 160, 2, True),
+    # split K (at most 16 token blocks, d >= 512): partial products, then the
+    # split sums and the epilogue in one kernel; one to four expert slots per
+    # lane, k up to 8, partly filled token blocks, a single token
+    ("bf16", 32, 1024, 64, 2, True), ("bf16", 65, 512, 160, 3, False),
+    ("bf16", 300, 1024, 256, 8, True), ("bf16", 1, 512, 128, 1, False)])
 def test_route_alone(act, T, d, E, k, bias):
     wl = W("r", T=T, d=d, E=E, k=k, d_ff=64, capacity_factor=1.0, act=act,
            zipf_s=1.2 if bias else 0.0, w_std=0.1)
