@@ -44,6 +44,15 @@ CASES = [
      "topk", {}),
     ("topp_f32", W("j", T=77, d=24, E=5, k=3, d_ff=40, capacity_factor=1.0, act="f32",
                    w_std=0.2), "top_p", dict(top_p=0.6)),
+    # three and four 64-expert slots per lane in the variant epilogue
+    ("topp_e256_k2", W("k", T=200, d=128, E=256, k=2, d_ff=128, capacity_factor=2.0,
+                       w_std=0.6), "top_p", dict(top_p=0.5)),
+    ("topp_e160_k3", W("l", T=150, d=128, E=160, k=3, d_ff=128, capacity_factor=2.0,
+                       w_std=0.6), "top_p", dict(top_p=0.6)),
+    ("cosine_e192_k2", W("m", T=100, d=128, E=192, k=2, d_ff=128, capacity_factor=2.0),
+     "cosine", dict(cos_tau=0.1, cos_dim=64)),
+    ("topk_losses_e200_k3", W("n", T=130, d=128, E=200, k=3, d_ff=128, capacity_factor=2.0),
+     "topk", {}),
 ]
 
 
