@@ -269,18 +269,21 @@ def test_expert_ffn_alone(C, d, F, wfmt):
     assert np.all(np.isnan(ydn[3, kept[3]:]))
 
 
-def test_int8_expert_schedule_matches_unscheduled_tiles():
-    # 40 int8 experts with C > 128 run on the XCD schedule (skewed loads,
-    # empty and single-row experts, one and two 256-row tiles); the same
+@pytest.mark.parametrize("E,C,F", [(40, 300, 1024), (32, 200, 768), (256, 136, 512)])
+def test_int8_expert_schedule_matches_unscheduled_tiles(E, C, F):
+    # int8 experts with C > 128 run on the XCD schedule (skewed loads, empty
+    # and single-row experts, light experts (<= 64 rows; not when d_ff is not
+    # a multiple of 512), tiles with one or two busy row bands, one and two
+    # 256-row tiles; E at both ends of the schedule's range); the same
     # experts eight at a time take the unscheduled tile order.  Same tiles,
     # same arithmetic: bit-identical rows.  Sampled rows against the oracle.
-    E, C, d, F = 40, 300, 1024, 1024
+    d = 1024
     wl = W("s", T=C, d=d, E=E, k=1, d_ff=F, capacity_factor=float(E), wfmt="int8")
     cfg = binding.config_of(wl)
     assert binding.capacity(cfg) == C
     inp = synth.make_inputs(wl, seed=5)
-    kept = np.array([C, C, 0, 1, 256, 257, 255, 3] + [int(C * 0.8 ** i) for i in range(32)],
-                    np.int32)
+    head = [C, C, 0, 1, min(256, C), min(257, C), min(255, C), 3, 128, 129, 64, 65]
+    kept = np.array((head + [int(C * 0.8 ** i) for i in range(E)])[:E], np.int32)
     xd = synth.normal((E, C, d), 1.0, 9, "xd", "cpu", torch.bfloat16)
     w1, s1, w2, s2 = (inp[n].to(DEV) for n in ("w1", "w1_scale", "w2", "w2_scale"))
     ys = torch.full((E, C, d), float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -300,7 +303,7 @@ def test_int8_expert_schedule_matches_unscheduled_tiles():
         assert torch.equal(ys[e, :n], yu[e, :n]), f"expert {e}"
         assert torch.isnan(ys[e, n:].float()).all(), f"expert {e}: rows past kept written"
     rng = np.random.default_rng(3)
-    for e in (0, 3, 5, 12):
+    for e in (0, 3, 5, 9, 12):
         n = int(kept[e])
         rows = sorted({0, n - 1, *rng.integers(0, n, size=3).tolist()})
         ref = oracle.ffn_rows(xd[e, rows], inp["w1"][e], inp["w2"][e], inp["w1_scale"][e],
