@@ -1174,6 +1174,10 @@ hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, co
       return launch_dma<32, 128, 1, 4, 64, 4>(b, nt, gelu, s, role, "dma32x128");
     }
     if (a.M_cap <= 64) {  // 64x256: two workgroups per CU, 64 KB of weights in flight
+      // (three stages, one workgroup per CU, for a long K: 0.197 -> 0.189 ms for
+      // the 350M shape's expert layer 2; a short K sweep loses on the longer fill)
+      if (a.N % 256 == 0 && a.K >= 4096)
+        return launch_dma<64, 256, 1, 4, 64, 3>(a, nt, gelu, s, role, "dma64x256");
       if (a.N % 256 == 0) return launch_dma<64, 256, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x256");
       return launch_dma<64, 128, 1, 4, 64, 2>(a, nt, gelu, s, role, "dma64x128");
     }
