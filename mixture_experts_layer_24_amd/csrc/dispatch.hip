@@ -18,9 +18,11 @@
 //           per-block counts are stored expert-major so this read is contiguous)
 //   place : one wave per block walks its 64*k assignments in order in chunks
 //           of 64; within a chunk, lanes with equal expert ids are grouped
-//           with ballots, ranked by lane order (popcount of the lower lanes),
-//           and the running per-expert count lives in registers spread over
-//           the lanes (expert e in lane e % 64, register e / 64)
+//           with one ballot per bit of the id (eight for E <= 256, however
+//           many experts the chunk holds), ranked by lane order (popcount of
+//           the lower lanes), and the running per-expert count lives in
+//           registers spread over the lanes (expert e in lane e % 64,
+//           register e / 64)
 //   gather: one wave per assignment copies the token's row to its slot with
 //           16-byte vector loads/stores (each row is contiguous on both sides,
 //           so the copy is fully coalesced without staging)
@@ -109,10 +111,6 @@ __global__ __launch_bounds__(256) void scan_aux_kernel(const int32_t *hist, cons
   }
 }
 
-__device__ __forceinline__ int sel4(int v0, int v1, int v2, int v3, int i) {
-  return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
-}
-
 // Token-order position of every assignment within its expert (the n-th
 // assignment of expert e in token order has position n), from the per-block
 // offsets; a wave ranks 64 assignments at a time with ballots.
@@ -169,28 +167,50 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
     int e = e_next;
     if (base + 64 < a1) e_next = (a + 64 < a1) ? ids[a + 64] : -1;  // next chunk's ids
     const bool valid = e >= 0 && e < E;
-    if (!valid) e = -1;
-    int slot = -1, ebase = 0;
-    uint64_t rem = __ballot(valid);
-    while (rem) {
-      const int leader = __ffsll((long long)rem) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t mask = __ballot(e == el);
-      const int ri = el >> 6, rl = el & 63;
-      const int start = __builtin_amdgcn_readlane(sel4(run0, run1, run2, run3, ri), rl);
-      const int eb = __builtin_amdgcn_readlane(sel4(eb0, eb1, eb2, eb3, ri), rl);
-      if (e == el) {
-        slot = start + __popcll(mask & lower);
-        ebase = eb;
+    if (!valid) e = 0;
+    // one ballot per bit of the expert id (E <= 256): the lanes holding
+    // expert x in this chunk are the valid lanes that agree with x on all
+    // eight bits, so every lane finds its group without a loop over experts
+    const uint64_t vm = __ballot(valid);
+    uint64_t bal[8];
+#pragma unroll
+    for (int b = 0; b < 8; b++) bal[b] = __ballot(valid && ((e >> b) & 1));
+    uint64_t same = vm, mine = vm;  // lanes of this lane's expert e; of expert lane (+ 64 i)
+#pragma unroll
+    for (int b = 0; b < 8; b++) same &= ((e >> b) & 1) ? bal[b] : ~bal[b];
+#pragma unroll
+    for (int b = 0; b < 6; b++) mine &= ((lane >> b) & 1) ? bal[b] : ~bal[b];
+    const uint64_t hi0 = ~bal[6] & ~bal[7], hi1 = bal[6] & ~bal[7];  // bits 6, 7 of 64 i
+    const uint64_t hi2 = ~bal[6] & bal[7], hi3 = bal[6] & bal[7];
+    // start of e's run: register e / 64 of lane e % 64 (before this chunk)
+    const int rl = e & 63, ri = e >> 6;
+    int start = __shfl(run0, rl, kWave);
+    int ebase = 0;
+    if (seg) ebase = __shfl(eb0, rl, kWave);
+    if (E > 64) {
+      const int s1 = __shfl(run1, rl, kWave);
+      if (ri == 1) start = s1;
+      if (seg) {
+        const int b1 = __shfl(eb1, rl, kWave);
+        if (ri == 1) ebase = b1;
       }
-      if (lane == rl) {
-        const int add = __popcll(mask);
-        if (ri == 0) run0 += add;
-        else if (ri == 1) run1 += add;
-        else if (ri == 2) run2 += add;
-        else run3 += add;
+    }
+    if (E > 128) {
+      const int s2 = __shfl(run2, rl, kWave), s3 = __shfl(run3, rl, kWave);
+      if (ri == 2) start = s2;
+      if (ri == 3) start = s3;
+      if (seg) {
+        const int b2 = __shfl(eb2, rl, kWave), b3 = __shfl(eb3, rl, kWave);
+        if (ri == 2) ebase = b2;
+        if (ri == 3) ebase = b3;
       }
-      rem &= ~mask;
+    }
+    const int slot = start + __popcll(same & lower);
+    run0 += __popcll(mine & hi0);
+    if (E > 64) run1 += __popcll(mine & hi1);
+    if (E > 128) {
+      run2 += __popcll(mine & hi2);
+      run3 += __popcll(mine & hi3);
     }
     if (a < a1) {
       // an id that is not an expert (an unused TopP slot) is no assignment

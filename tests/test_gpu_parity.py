@@ -194,15 +194,24 @@ def test_route_exact_ties_break_to_lower_index(k):
     assert np.array_equal(to_np(ids2), ref["ids"])
 
 
-@pytest.mark.parametrize("T,E,k,C", [(1000, 7, 2, 150), (64 * 5 + 3, 128, 1, 3),
-                                     (50, 3, 3, 50), (200, 16, 2, 1), (129, 256, 1, 2)])
-def test_dispatch_alone(T, E, k, C):
+# holes: share of the ids set outside [0, E) (-1, as a TopP router leaves an
+# unused slot, or E): no assignment, counted nowhere
+@pytest.mark.parametrize("T,E,k,C,holes", [(1000, 7, 2, 150, 0), (64 * 5 + 3, 128, 1, 3, 0),
+                                           (50, 3, 3, 50, 0), (200, 16, 2, 1, 0),
+                                           (129, 256, 1, 2, 0), (300, 200, 8, 20, 0),
+                                           (777, 192, 3, 16, 0.1), (500, 65, 2, 40, 0.05),
+                                           (70, 256, 4, 3, 0.2), (64, 1, 1, 64, 0.3)])
+def test_dispatch_alone(T, E, k, C, holes):
     d = 128
     rng = np.random.default_rng(T + E)
     # skewed synthetic choices: distinct experts per token
     p = 1.0 / np.arange(1, E + 1) ** 1.1
     p /= p.sum()
     ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    if holes:
+        hole = rng.random(ids.shape) < holes
+        ids[hole] = np.where(rng.random(ids.shape) < 0.5, -1, E)[hole]
+        assert hole.any()
     ref = oracle.dispatch(ids, E, C)
     cfg = binding.make_config(T=T, d=d, E=E, k=k, d_ff=64, capacity=C)
     assert binding.capacity(cfg) == C
