@@ -184,7 +184,11 @@ typedef struct moe_outputs {
   float *aux_loss;     /* [1]                                   required */
   uint8_t *drop_mask;  /* [T, k] 1 = dropped                    optional */
   float *logits;       /* [T, E] router logits (+ bias)         optional */
-  void *x_disp;        /* [E, C, d] act; NULL = in the workspace */
+  void *x_disp;        /* [E, C, d] act; NULL = not kept: with token-order
+                          dispatch, bf16 activations and expert shapes on the
+                          DMA tiles the first expert GEMM then reads the token
+                          rows of x through a slot -> token table and no
+                          gathered copy is made, else it is in the workspace */
   void *y_disp;        /* [E, C, d] act; NULL = in the workspace */
   void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
   float *z_loss;       /* [1] router z-loss                     optional */

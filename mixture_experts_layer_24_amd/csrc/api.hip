@@ -84,7 +84,7 @@ bool opt(const void *p, size_t align) { return p == nullptr || aligned(p, align)
 // ---- workspace layout
 struct Layout {
   size_t qsum, fcount, hist, offs, term, zpart, seg, x_disp, y_disp, hidden, hidden_dense, dense,
-      xsched, rpart, total;
+      xsched, rpart, src, total;  // src: 0 = not in this layout
   // router variants
   size_t scores, cosl, embn, imp, loadp;
   // backward
@@ -185,6 +185,7 @@ Layout layout(const moe_config *c, int entry) {
       take_variant();
       if (gp) L.seg = take(segB);
       if (big) {
+        L.src = take((size_t)c->E * C * 4);
         L.x_disp = take((size_t)c->E * C * c->d * as);
         L.y_disp = take((size_t)c->E * C * c->d * as);
         L.hidden = take((size_t)c->E * C * c->d_ff * as);
@@ -351,29 +352,31 @@ bool loss_outputs_ok(const moe_config *c, const moe_outputs *o) {
 // place slots (token order, or gate priority through the segment array
 // `seg`, which needs gates and load) and gather the kept rows; hist/offs are
 // the per-block counts and offsets ([E][blocks]); aux_term non-null -> the
-// place kernel also finishes the aux loss
+// place kernel also finishes the aux loss.  src non-null (token order): the
+// slot -> token table is written instead of the gathered rows.
 hipError_t do_place_gather(const moe_config *c, const void *x, const int32_t *ids,
                            const float *gates, const int32_t *offs, const int32_t *load,
                            int32_t *seg, int32_t *slots, uint8_t *drop, const double *aux_term,
-                           float *aux, void *x_disp, hipStream_t s) {
+                           float *aux, void *x_disp, hipStream_t s, int32_t *src = nullptr) {
   const int64_t C = capacity_of(c);
   const bool gp = c->drop_policy == MOE_DROP_GATE_PRIORITY;
+  if (gp && src) return hipErrorInvalidValue;
   hipError_t e = moe_host::launch_dispatch_place(ids, offs, c->T, (int)c->E, (int)c->k, C, slots,
                                                  drop, aux_term, c->aux_alpha, aux, s,
                                                  gp ? gates : nullptr, gp ? load : nullptr,
-                                                 gp ? seg : nullptr);
-  if (e != hipSuccess) return e;
+                                                 gp ? seg : nullptr, src);
+  if (e != hipSuccess || src) return e;
   return moe_host::launch_gather(x, ids, slots, c->T, (int)c->k, C,
                                  c->d * (int64_t)act_size(c), x_disp, s);
 }
 
 // hidden: GELU(W1 x) of the kept rows; zpre: W1 x itself, or null (not kept);
 // xsched: workspace for the XCD schedule of the int8 tiles (sched_experts),
-// or null
+// or null; asrc: the slot -> token table, with x_disp then the token rows x
 hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t *kept,
                          const void *w1, const void *s1, const void *w2, const void *s2,
                          void *y_disp, void *hidden, hipStream_t s, void *zpre = nullptr,
-                         int32_t *xsched = nullptr) {
+                         int32_t *xsched = nullptr, const int32_t *asrc = nullptr) {
   const int64_t C = capacity_of(c);
   if (C == 0) return hipSuccess;
   const int bf = c->act_dtype == MOE_BF16, q8 = c->expert_wfmt == MOE_W_INT8_G128;
@@ -388,6 +391,7 @@ hipError_t do_expert_ffn(const moe_config *c, const void *x_disp, const int32_t 
   const int pk = c->expert_wfmt == MOE_W_BF16_PACKED;
   GemmArgs g1{x_disp, w1, s1, hidden, kept, C, (int)c->d_ff, (int)c->d, (int)c->E, zpre, xsched,
               pk};
+  g1.asrc = asrc;
   e = moe_host::launch_gemm(g1, bf, q8, 1, "expert_ffn1", s);
   if (e != hipSuccess) return e;
   GemmArgs g2{hidden, w2, s2, y_disp, kept, C, (int)c->d, (int)c->d_ff, (int)c->E, nullptr, xsched,
@@ -720,6 +724,18 @@ static hipError_t layer_forward_launch(const moe_config *cfg, const void *x, con
   } else if (cfg->pr_moe) {
     e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden_dense, s, zd);
   }
+  // x_disp not asked for: the first expert GEMM reads the token rows of x
+  // through the slot -> token table that placement writes, and no gathered
+  // copy is made (token-order dispatch, shapes on the DMA tiles)
+  int32_t *asrc = nullptr;
+  if (!out->x_disp && L.src && cfg->drop_policy != MOE_DROP_GATE_PRIORITY &&
+      capacity_of(cfg) > 0) {
+    GemmArgs g1{x, nullptr, nullptr, nullptr, nullptr, capacity_of(cfg), (int)cfg->d_ff,
+                (int)cfg->d, (int)cfg->E};
+    if (moe_host::gemm_reads_row_table(g1, cfg->act_dtype == MOE_BF16,
+                                       cfg->expert_wfmt == MOE_W_INT8_G128, T))
+      asrc = (int32_t *)at(ws, L.src);
+  }
   double *term = (double *)at(ws, L.term);
   if (e == hipSuccess)
     e = do_router_v(cfg, L, ws, x, w, out->expert_ids, out->gates, out->logits, qsum, fcount,
@@ -732,11 +748,11 @@ static hipError_t layer_forward_launch(const moe_config *cfg, const void *x, con
     e = do_place_gather(cfg, x, out->expert_ids, out->gates, offs, out->load,
                         cfg->drop_policy == MOE_DROP_GATE_PRIORITY ? (int32_t *)at(ws, L.seg)
                                                                    : nullptr,
-                        out->slots, out->drop_mask, term, out->aux_loss, x_disp, s);
+                        out->slots, out->drop_mask, term, out->aux_loss, x_disp, s, asrc);
   if (e == hipSuccess)
-    e = do_expert_ffn(cfg, x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale, y_disp,
-                      hidden, s, out->z_disp,
-                      sched_experts(cfg) ? (int32_t *)at(ws, L.xsched) : nullptr);
+    e = do_expert_ffn(cfg, asrc ? x : x_disp, out->kept, w->w1, w->w1_scale, w->w2, w->w2_scale,
+                      y_disp, hidden, s, out->z_disp,
+                      sched_experts(cfg) ? (int32_t *)at(ws, L.xsched) : nullptr, asrc);
   // join: the combine reads D(x)
   if (e == hipSuccess && side) e = hipStreamWaitEvent(s, side->join, 0);
   if (e == hipSuccess)

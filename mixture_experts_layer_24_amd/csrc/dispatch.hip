@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void scan_aux_kernel(const int32_t *hist, cons
 // Token-order position of every assignment within its expert (the n-th
 // assignment of expert e in token order has position n), from the per-block
 // offsets; a wave ranks 64 assignments at a time with ballots.
-// Token order (seg == null): slot = position if < C, else dropped.
+// Token order (seg == null): slot = position if < C, else dropped; with src,
+// src[e * C + slot] = the token of each kept assignment.
 // Gate priority (seg != null): no capacity here; the position goes to
 // slots[] and the assignment index to seg[ebase[e] + position], where ebase
 // is the exclusive prefix of load[] over experts, for rank_gate_kernel.
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
                                                             int32_t *slots, uint8_t *drop,
                                                             const double *aux_term,
                                                             float aux_alpha, float *aux,
-                                                            const int32_t *load, int32_t *seg) {
+                                                            const int32_t *load, int32_t *seg,
+                                                            int32_t *src) {
   const int lane = lane_id(), blk = blockIdx.x, nblk = gridDim.x;
   // this block's offsets and its first 64 assignments are loaded before
   // anything else, so their latencies overlap the aux sum and the scan below
@@ -222,6 +224,7 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *ids, 
         const bool keep = valid && (int64_t)slot < C;
         slots[a] = keep ? slot : -1;
         if (drop) drop[a] = (valid && !keep) ? 1 : 0;
+        if (src && keep) src[(int64_t)e * C + slot] = (int32_t)(a / k);
       }
     }
   }
@@ -464,11 +467,11 @@ hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
                                  int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
                                  float aux_alpha, float *aux, hipStream_t s, const float *gates,
-                                 const int32_t *load, int32_t *seg) {
+                                 const int32_t *load, int32_t *seg, int32_t *src) {
   const int nblk = (int)((T + DBT - 1) / DBT);
   if (nblk > 0)
     MOE_LAUNCH("dispatch_place", dispatch_place_kernel, dim3(nblk), dim3(64), 0, s, ids, offs, T,
-               E, k, C, slots, drop, aux_term, aux_alpha, aux, load, seg);
+               E, k, C, slots, drop, aux_term, aux_alpha, aux, load, seg, seg ? nullptr : src);
   else if (aux)
     return launch_aux_sum(aux_term, E, aux_alpha, aux, s);
   if (seg && T > 0) {

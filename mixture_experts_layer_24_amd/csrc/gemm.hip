@@ -348,7 +348,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   const int n0 = tn * BN;
   const int K = a.K, N = a.N;
   // per-tile operand bases: every per-lane offset below is < 2^32 bytes
-  const char *Abase = (const char *)a.A + ((int64_t)g * a.M_cap + m0) * K * 2;
+  // (with a row table, A's base is its first row)
+  const char *Abase =
+      (const char *)a.A + (a.asrc ? 0 : ((int64_t)g * a.M_cap + m0) * K * 2);
   const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K * 2;
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
   bf16 *Zg = GELU == 2 ? (bf16 *)a.Zpre + (int64_t)g * a.M_cap * N : nullptr;
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
     const int R = RPC * (wave * A_PW + i) + lr;
     int64_t m = R;
     if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
+    if (a.asrc) m = a.asrc[(int64_t)g * a.M_cap + m0 + m];
     voffa[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<BK>(R)) << 4));
   }
 #pragma unroll
@@ -560,7 +563,8 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
   if (m0 >= rows) return;
   const int n0 = tn * BN;
   const int K = a.K, N = a.N, KG = K / 128;
-  const char *Abase = (const char *)a.A + ((int64_t)g * a.M_cap + m0) * K * 2;
+  const char *Abase =
+      (const char *)a.A + (a.asrc ? 0 : ((int64_t)g * a.M_cap + m0) * K * 2);
   const char *Bbase = (const char *)a.B + ((int64_t)g * N + n0) * (int64_t)K;
   const char *Sbase = (const char *)a.Bscale + ((int64_t)g * N + n0) * (int64_t)KG * 2;
   bf16 *Cg = (bf16 *)a.C + (int64_t)g * a.M_cap * N;
@@ -575,6 +579,7 @@ __device__ __forceinline__ void i8_tile(const GemmArgs &a, int g, int tm, int tn
     const int R = 8 * (wave * A_PW + i) + lane / 8, slot = lane % 8;
     int64_t m = R;
     if (m0 + m >= rows) m = rows - 1 - m0;  // clamp to the last valid row
+    if (a.asrc) m = a.asrc[(int64_t)g * a.M_cap + m0 + m];
     voffa[i] = (uint32_t)(m * K * 2 + ((slot ^ swz_slot<64>(R)) << 4));
   }
 #pragma unroll
@@ -1137,12 +1142,23 @@ hipError_t launch_tile_sched(const int32_t *rows, int G, int64_t M_cap, int ligh
   return hipGetLastError();
 }
 
+// Whether launch_gemm takes a DMA kernel for these shapes (the kernels that
+// can read A's rows through a table, GemmArgs::asrc); a_rows: rows of A
+// behind the table.  Follows the tile choice below.
+bool gemm_reads_row_table(const GemmArgs &a, int act_bf16, int b_int8, int64_t a_rows) {
+  if (!act_bf16 || a_rows * a.K * 2 > (int64_t)UINT32_MAX) return false;
+  if (b_int8) return a.K % 1024 == 0 && a.N % 256 == 0;
+  return a.N % 128 == 0;
+}
+
 // Tile choice (measured on MI355X at the workload shapes) by rows per group
 // (the capacity, or T for the dense MLP), N, and whether the weights are
 // streamed once (expert GEMMs: non-temporal weight loads).
 hipError_t launch_gemm(const GemmArgs &a, int act_bf16, int b_int8, int gelu, const char *role,
                        hipStream_t s) {
   if (a.G <= 0 || a.M_cap <= 0 || a.N <= 0) return hipGetLastError();
+  // a row table needs a DMA kernel (the caller also checks the row count)
+  if (a.asrc && !gemm_reads_row_table(a, act_bf16, b_int8, 0)) return hipErrorInvalidValue;
   if (!act_bf16) {
     const int tiles = a.G * (int)((a.M_cap + 63) / 64) * ((a.N + 63) / 64);
     const char *name = intern_name(role, "f32");

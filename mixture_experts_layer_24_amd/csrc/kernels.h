@@ -64,6 +64,10 @@ struct GemmArgs {
   // tiles in launch order, dealt round-robin over the XCDs (set by the
   // launcher for groups of one row tile), instead of a group per XCD
   int spread;
+  // rows of A through a table: row m of group g is row asrc[g * M_cap + m]
+  // of A ([rows][K], e.g. the token rows; rows * K * 2 < 2^32), or null = A
+  // is [G][M_cap][K]; only the DMA kernels take it (gemm_reads_row_table)
+  const int32_t *asrc;
 };
 
 // general grouped GEMM of the backward (backward.hip)
@@ -129,12 +133,14 @@ hipError_t launch_scan_aux(const int32_t *hist, const float *qsum, const int32_t
                            int32_t *kept, double *term, hipStream_t s);
 // slots in token order; block 0 also finishes the aux loss when aux != null
 // seg == null: token-order capacity.  seg != null: gate priority (gates and
-// load required; seg is workspace of T*k int32).
+// load required; seg is workspace of T*k int32).  src != null (token order
+// only): src[e * C + slot] = token of every kept assignment, the row table
+// through which the first expert GEMM reads x instead of a gathered x_disp.
 hipError_t launch_dispatch_place(const int32_t *ids, const int32_t *offs, int64_t T, int E, int k,
                                  int64_t C, int32_t *slots, uint8_t *drop, const double *aux_term,
                                  float aux_alpha, float *aux, hipStream_t s,
                                  const float *gates = nullptr, const int32_t *load = nullptr,
-                                 int32_t *seg = nullptr);
+                                 int32_t *seg = nullptr, int32_t *src = nullptr);
 hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots, int64_t T, int k,
                          int64_t C, int64_t row_bytes, void *x_disp, hipStream_t s);
 
@@ -142,6 +148,9 @@ hipError_t launch_gather(const void *x, const int32_t *ids, const int32_t *slots
 // in the per-kernel timing ("expert_ffn1", "expert_ffn2", "dense_mlp1", ...)
 hipError_t launch_gemm(const moe::GemmArgs &a, int act_bf16, int b_int8, int gelu,
                        const char *role, hipStream_t s);
+// whether launch_gemm can read A's rows through a.asrc for these shapes, with
+// a_rows rows behind the table
+bool gemm_reads_row_table(const moe::GemmArgs &a, int act_bf16, int b_int8, int64_t a_rows);
 // [G][N][K] row-major bf16 -> blocks of 128 rows x 64 K (N % 128 == 0, K % 64 == 0)
 hipError_t launch_pack_weights(const void *w, void *wp, int64_t G, int64_t N, int64_t K,
                                hipStream_t s);

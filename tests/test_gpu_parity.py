@@ -439,6 +439,70 @@ def test_empty_batch():
 
 
 # ------------------------------------------------------------ full-size workloads
+# ------------------------------------------------------------ x_disp not kept
+# Without x_disp among the outputs, the first expert GEMM reads the token rows
+# of x through the slot -> token table that placement writes (token-order
+# dispatch, bf16 activations, shapes on the DMA tiles) and no gathered copy
+# is made.  Every output must equal, bit for bit, the run that keeps x_disp
+# (checked against the oracle in the tests above), and the expert rows are
+# checked against the oracle as well.
+ROW_TABLE = [w for w in SMALL if w.act == "bf16"] + [
+    # int8 experts on the scheduled 256-row DMA tiles (E >= 32, C > 128, d
+    # and d_ff multiples of 1024) and on the 128-row ones (C <= 128)
+    W("int8_sched_rows", T=2400, d=1024, E=32, k=2, d_ff=1024, capacity_factor=1.25,
+      wfmt="int8", zipf_s=1.2),
+    W("int8_rows_c128", T=1000, d=1024, E=16, k=2, d_ff=2048, capacity_factor=1.0,
+      wfmt="int8"),
+]
+
+
+def _layer_outputs(wl, inp, keep_x_disp, wfmt=None):
+    cfg = binding.config_of(wl, wfmt=wfmt) if wfmt else binding.config_of(wl)
+    out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=keep_x_disp, y_disp=True,
+                                dense_out=True)
+    check_guards = guard_outputs(out)
+    binding.moe_layer_forward(cfg, inp["x"], inp, out, binding.alloc_workspace(cfg))
+    torch.cuda.synchronize()
+    check_guards()
+    return out
+
+
+def _same_layer_outputs(a, b, E):
+    for name in ("y", "expert_ids", "gates", "slots", "drop_mask", "load", "kept", "aux_loss",
+                 "logits", "dense_out"):
+        u, v = getattr(a, name), getattr(b, name)
+        assert (u is None) == (v is None), name
+        if u is not None:
+            assert torch.equal(u, v), name
+    kept = a.kept.cpu().tolist()
+    for e in range(E):  # rows past kept[e] are not written
+        assert torch.equal(a.y_disp[e, :kept[e]], b.y_disp[e, :kept[e]]), f"y_disp[{e}]"
+
+
+@pytest.mark.parametrize("wl", ROW_TABLE, ids=[w.name for w in ROW_TABLE])
+def test_layer_without_x_disp_reads_token_rows(wl):
+    print(f"[row_table] {wl.name}", flush=True)
+    inp = synth.make_inputs(wl, seed=0, device=DEV)
+    a = _layer_outputs(wl, inp, True)
+    b = _layer_outputs(wl, inp, False)
+    assert b.x_disp is None
+    _same_layer_outputs(a, b, wl.E)
+    # the first and last kept row of every active expert against the oracle
+    inv = _inverse(to_np(b.expert_ids), to_np(b.slots), wl.E)
+    want, where = {}, []
+    for e in range(wl.E):
+        for i in sorted({0, len(inv[e]) - 1}) if inv[e] else ():
+            s_, t_, _ = inv[e][i]
+            want.setdefault(e, []).append(t_)
+            where.append((e, s_))
+    rows = oracle_rows_by_expert(inp["x"].cpu(), inp, want)
+    ref_rows = np.concatenate([rows[e] for e in sorted(rows)])
+    es = torch.as_tensor([w[0] for w in where], device=DEV)
+    ss = torch.as_tensor([w[1] for w in where], device=DEV)
+    check_close("y_disp (first/last kept row of every expert)", b.y_disp[es, ss], ref_rows,
+                TAU["bf16"])
+
+
 def _inverse(ids, slots, E):
     """per expert: list of (slot, token, j) of its kept assignments, by slot"""
     rows = [[] for _ in range(E)]
@@ -494,5 +558,20 @@ def test_full_size_layer_sampled(name):
                                        out.y_disp, m, out.y, toks, dense=dref)
     print(f"  {len(toks)} tokens, {n_rows} of their rows kept; M rel err {err_m:.2e}",
           flush=True)
+    if wl.act == "bf16":
+        # as the benchmark runs it: x_disp not kept (the first expert GEMM
+        # reads the token rows through the slot -> token table) and bf16
+        # expert weights packed: every output equal to this run's
+        wts = inp
+        wfmt = "packed" if wl.wfmt == "plain" and wl.d % 128 == 0 and wl.d_ff % 128 == 0 else None
+        if wfmt:
+            cfgp = binding.config_of(wl, wfmt=wfmt)
+            wts = dict(inp, w1=binding.pack_expert_weights(cfgp, 1, inp["w1"]),
+                       w2=binding.pack_expert_weights(cfgp, 2, inp["w2"]))
+        b = _layer_outputs(wl, wts, False, wfmt=wfmt)
+        _same_layer_outputs(out, b, wl.E)
+        print(f"  without x_disp{' (packed weights)' if wfmt else ''}: outputs identical",
+              flush=True)
+        del wts, b
     del inp, out, m
     torch.cuda.empty_cache()
