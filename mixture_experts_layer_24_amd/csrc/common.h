@@ -95,8 +95,8 @@ __device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }  // RNE
 // erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 // t = 1 / (1 + p x) for x >= 0 (odd extension), |error| <= 1.5e-7 -- far
-// below the bf16 rounding of the GELU output; about a third of the
-// instructions of the device library's erff on the GEMM epilogue.
+// below the bf16 rounding of the values it feeds (the backward's GELU
+// derivative, Phi(z) + z phi(z)).
 __device__ __forceinline__ float erf_as(float x) {
   const float ax = fabsf(x);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
@@ -110,9 +110,26 @@ __device__ __forceinline__ float erf_as(float x) {
   return copysignf(fmaf(-poly, e, 1.0f), x);
 }
 
-// GELU with the exact (erf) form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2))
+// GELU with the exact (erf) form, z * Phi(z), written as
+//   max(z, 0) - |z| Q(|z|),  Q(x) = Phi(-x) = 2^g(u),  u = min(x, 6) / 3 - 1,
+// g a degree-9 polynomial fitted to log2 Q on [0, 6] (gelu_fit.py, which
+// prints these coefficients): one exp2 and no reciprocal per element, |error|
+// <= 3.1e-7 in fp32 (the erf_as form above needs a reciprocal and an exp2 and
+// is as accurate; the GEMM epilogues' GELU took ~10% of the first layers'
+// time with it).  Past |z| = 6, Q stays at Q(6) ~ 1e-9.
 __device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752440f));
+  const float u = fmaf(fminf(fabsf(z), 6.0f), 1.0f / 3.0f, -1.0f);
+  float g = 9.821072454e-04f;
+  g = fmaf(g, u, -4.859279215e-05f);
+  g = fmaf(g, u, -6.342675537e-03f);
+  g = fmaf(g, u, 1.686366647e-02f);
+  g = fmaf(g, u, -3.910345584e-02f);
+  g = fmaf(g, u, 9.169072658e-02f);
+  g = fmaf(g, u, -2.044294178e-01f);
+  g = fmaf(g, u, -6.033986092e+00f);
+  g = fmaf(g, u, -1.420952320e+01f);
+  g = fmaf(g, u, -9.532935143e+00f);
+  return fmaf(-fabsf(z), __builtin_amdgcn_exp2f(g), fmaxf(z, 0.0f));
 }
 
 template <typename T>

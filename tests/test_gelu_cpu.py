@@ -1,0 +1,59 @@
+"""The kernels' GELU approximation (csrc/common.h gelu_f) against the exact
+erf form of GELU, z * Phi(z) (survey notes sec. 1.1.2.1: the expert FFN's
+activation).  CPU only: the coefficients are read from the kernel source and
+evaluated in fp32 in the kernel's order; the reference is scipy's erf in
+fp64, a library routine independent of both the kernels and the fit."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+from scipy.special import erf
+
+from mixture_experts_layer_24_amd import gelu_fit
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COMMON_H = os.path.join(HERE, "..", "mixture_experts_layer_24_amd", "csrc", "common.h")
+
+
+def kernel_coeffs():
+    src = open(COMMON_H).read()
+    body = src[src.index("float gelu_f(float z)"):]
+    body = body[:body.index("}")]
+    first = float(re.search(r"float g = ([-+0-9.e]+)f;", body).group(1))
+    rest = [float(v) for v in re.findall(r"g = fmaf\(g, u, ([-+0-9.e]+)f\);", body)]
+    hi_to_lo = [first] + rest
+    return np.array(hi_to_lo[::-1], dtype=np.float32)  # u^0 first
+
+
+def exact_gelu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z * 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def test_kernel_coefficients_are_the_fit():
+    c = kernel_coeffs()
+    assert c.shape == (gelu_fit.DEGREE + 1,)
+    np.testing.assert_array_equal(c, gelu_fit.fit())
+
+
+@pytest.mark.parametrize("lo,hi,n", [(-12.0, 12.0, 2_400_001), (-1e-3, 1e-3, 20_001),
+                                     (-60.0, 60.0, 600_001)])
+def test_fp32_gelu_error_bound(lo, hi, n):
+    z = np.linspace(lo, hi, n).astype(np.float32)
+    got = gelu_fit.gelu_fp32(z, kernel_coeffs()).astype(np.float64)
+    want = exact_gelu(z)
+    err = np.abs(got - want)
+    # absolute bound, plus the fp32 rounding of max(z, 0) for large positive z
+    assert (err <= 3.5e-7 + 2 ** -23 * np.abs(want)).all(), float(err.max())
+
+
+def test_special_values():
+    c = kernel_coeffs()
+    z = np.array([0.0, -0.0, 1.0, -1.0, 6.0, -6.0, 30.0, -30.0, 1e4, -1e4], dtype=np.float32)
+    got = gelu_fit.gelu_fp32(z, c)
+    assert got[0] == 0.0 and got[1] == 0.0
+    np.testing.assert_allclose(got[2:6], exact_gelu(z[2:6]), atol=3.5e-7)
+    assert got[6] == np.float32(30.0) and abs(got[7]) < 1e-7   # saturated tails
+    assert got[8] == np.float32(1e4) and abs(got[9]) < 2e-5
