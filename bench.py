@@ -104,6 +104,9 @@ def parse():
                         "the backward recomputes them")
     p.add_argument("--serial", action="store_true",
                    help="PR-MoE: dense MLP in order on the launch stream (no side-stream overlap)")
+    p.add_argument("--read-x-rows", action="store_true",
+                   help="the first expert GEMM reads the token rows of x through the slot -> "
+                        "token table instead of the gathered [E, C, d] buffer (default: gather)")
     p.add_argument("--expert-weights", default="auto", choices=["auto", "plain", "packed"],
                    help="bf16 expert weights row-major (plain) or in 128-row x 64-k blocks "
                         "(packed once before timing); auto = packed for a forward pass "
@@ -457,7 +460,7 @@ def run_workload(name, args, headline=True):
     if packed:
         wl = wl.replace(wfmt="packed")
     cfg = binding.config_of(wl, overlap_dense=not args.serial, drop_policy=args.drop_policy,
-                            **rkw)
+                            read_x_rows=args.read_x_rows, **rkw)
     oracle_inp = inp  # the CPU oracle reads the row-major weights
     if packed:  # once, where a model's weights are loaded: outside the timed steps
         inp = dict(inp, w1=binding.pack_expert_weights(cfg, 1, inp["w1"]),
@@ -577,7 +580,8 @@ def run_workload(name, args, headline=True):
     # kernel's time alone (reported as `isolated`, not part of `value`)
     isolated = None
     if wl.pr_moe and not args.serial and not bwd:
-        cfg_s = binding.config_of(wl, overlap_dense=False, drop_policy=args.drop_policy, **rkw)
+        cfg_s = binding.config_of(wl, overlap_dense=False, drop_policy=args.drop_policy,
+                                  read_x_rows=args.read_x_rows, **rkw)
         binding.profile_reset()
         binding.profile_filter(None)
         binding.profile_enable(True)
@@ -665,6 +669,8 @@ def run_workload(name, args, headline=True):
                                       else wl.act + " row-major"),
                    "pr_moe": wl.pr_moe, "add_skip": wl.add_skip,
                    "dense_mlp_overlapped": bool(wl.pr_moe and not args.serial),
+                   "x_rows": ("read through the slot -> token table" if args.read_x_rows
+                              else "gathered into [E, C, d]"),
                    "drop_policy": args.drop_policy, "z_loss": bool(args.z_loss),
                    "pass": "train" if args.train else "backward" if args.backward else "forward",
                    **({"ffn_activations": "recomputed" if args.recompute else "saved"}
@@ -811,7 +817,8 @@ def main():
     name = args.workload or workloads.HEADLINE
     res = run_workload(name, args, headline=True)
     variant = (args.backward or args.train or args.router != "topk" or args.router_losses
-               or args.k or args.serial or args.drop_policy != "token_order" or args.z_loss)
+               or args.k or args.serial or args.drop_policy != "token_order" or args.z_loss
+               or args.read_x_rows)
     if args.workload is None and not variant and not args.headline_only:
         # the other four workloads, each measured the same way, as sub-records
         res["workloads"] = {}

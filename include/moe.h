@@ -155,6 +155,14 @@ typedef struct moe_config {
   int32_t cos_dim;        /* COSINE: projection width 1..256 */
   float w_importance;     /* Importance-loss weight (0 = not computed) */
   float w_load;           /* Load-loss weight (0 = not computed) */
+  int32_t read_x_rows;    /* moe_layer_forward: 0 (default) = the gather builds
+                             the explicit [E, C, d] buffer x_disp that the first
+                             expert GEMM reads; 1 = when x_disp is not among the
+                             outputs (and with token-order dispatch, bf16
+                             activations and expert shapes on the DMA tiles),
+                             the first expert GEMM reads the token rows of x
+                             through the slot -> token table instead and no
+                             gathered copy is made (same results, bit for bit) */
 } moe_config;
 
 typedef struct moe_weights {
@@ -184,11 +192,8 @@ typedef struct moe_outputs {
   float *aux_loss;     /* [1]                                   required */
   uint8_t *drop_mask;  /* [T, k] 1 = dropped                    optional */
   float *logits;       /* [T, E] router logits (+ bias)         optional */
-  void *x_disp;        /* [E, C, d] act; NULL = not kept: with token-order
-                          dispatch, bf16 activations and expert shapes on the
-                          DMA tiles the first expert GEMM then reads the token
-                          rows of x through a slot -> token table and no
-                          gathered copy is made, else it is in the workspace */
+  void *x_disp;        /* [E, C, d] act; NULL = in the workspace (or, with
+                          cfg->read_x_rows, not built: see moe_config) */
   void *y_disp;        /* [E, C, d] act; NULL = in the workspace */
   void *dense_out;     /* [T, d] act D(x) (pr_moe); NULL = workspace */
   float *z_loss;       /* [1] router z-loss                     optional */

@@ -55,7 +55,7 @@ class Config(ctypes.Structure):
                 ("aux_alpha", ctypes.c_float), ("overlap_dense", ctypes.c_int32),
                 ("router", ctypes.c_int32), ("top_p", ctypes.c_float), ("cos_tau", ctypes.c_float),
                 ("cos_dim", ctypes.c_int32), ("w_importance", ctypes.c_float),
-                ("w_load", ctypes.c_float)]
+                ("w_load", ctypes.c_float), ("read_x_rows", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -155,7 +155,7 @@ def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16"
                 wfmt="plain", d_ff_dense=0, pr_moe=False, add_skip=True,
                 normalize_topk=True, aux_alpha=1.0, overlap_dense=True,
                 drop_policy="token_order", router="topk", top_p=0.0, cos_tau=0.0,
-                cos_dim=0, w_importance=0.0, w_load=0.0) -> Config:
+                cos_dim=0, w_importance=0.0, w_load=0.0, read_x_rows=False) -> Config:
     if drop_policy not in ("token_order", "gate_priority"):
         raise ValueError(f"drop_policy {drop_policy!r}")
     if router not in ROUTERS:
@@ -172,7 +172,7 @@ def make_config(*, T, d, E, k, d_ff, capacity_factor=1.0, capacity=0, act="bf16"
                                else MOE_DROP_TOKEN_ORDER),
                   aux_alpha=aux_alpha, overlap_dense=int(overlap_dense),
                   router=ROUTERS[router], top_p=top_p, cos_tau=cos_tau, cos_dim=cos_dim,
-                  w_importance=w_importance, w_load=w_load)
+                  w_importance=w_importance, w_load=w_load, read_x_rows=int(read_x_rows))
 
 
 def config_of(wl: Workload, **override) -> Config:

@@ -31,7 +31,7 @@ int check_config(const moe_config *c) {
   if (c->expert_wfmt != MOE_W_PLAIN && c->expert_wfmt != MOE_W_INT8_G128 &&
       c->expert_wfmt != MOE_W_BF16_PACKED)
     return MOE_ERR_INVALID_ARG;
-  if ((c->normalize_topk | c->pr_moe | c->add_skip) & ~1) return MOE_ERR_INVALID_ARG;
+  if ((c->normalize_topk | c->pr_moe | c->add_skip | c->read_x_rows) & ~1) return MOE_ERR_INVALID_ARG;
   if (c->capacity < 0) return MOE_ERR_INVALID_ARG;
   if (c->capacity == 0 && !(c->capacity_factor > 0.0 && isfinite(c->capacity_factor)))
     return MOE_ERR_INVALID_ARG;
@@ -724,11 +724,12 @@ static hipError_t layer_forward_launch(const moe_config *cfg, const void *x, con
   } else if (cfg->pr_moe) {
     e = do_dense(cfg, x, w->wm1, w->wm2, dense, hidden_dense, s, zd);
   }
-  // x_disp not asked for: the first expert GEMM reads the token rows of x
-  // through the slot -> token table that placement writes, and no gathered
-  // copy is made (token-order dispatch, shapes on the DMA tiles)
+  // read_x_rows and x_disp not asked for: the first expert GEMM reads the
+  // token rows of x through the slot -> token table that placement writes,
+  // and no gathered copy is made (token-order dispatch, shapes on the DMA
+  // tiles); otherwise the gather builds x_disp
   int32_t *asrc = nullptr;
-  if (!out->x_disp && L.src && cfg->drop_policy != MOE_DROP_GATE_PRIORITY &&
+  if (cfg->read_x_rows && !out->x_disp && L.src && cfg->drop_policy != MOE_DROP_GATE_PRIORITY &&
       capacity_of(cfg) > 0) {
     GemmArgs g1{x, nullptr, nullptr, nullptr, nullptr, capacity_of(cfg), (int)cfg->d_ff,
                 (int)cfg->d, (int)cfg->E};

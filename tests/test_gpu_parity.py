@@ -440,12 +440,13 @@ def test_empty_batch():
 
 # ------------------------------------------------------------ full-size workloads
 # ------------------------------------------------------------ x_disp not kept
-# Without x_disp among the outputs, the first expert GEMM reads the token rows
-# of x through the slot -> token table that placement writes (token-order
-# dispatch, bf16 activations, shapes on the DMA tiles) and no gathered copy
-# is made.  Every output must equal, bit for bit, the run that keeps x_disp
-# (checked against the oracle in the tests above), and the expert rows are
-# checked against the oracle as well.
+# With read_x_rows and without x_disp among the outputs, the first expert
+# GEMM reads the token rows of x through the slot -> token table that
+# placement writes (token-order dispatch, bf16 activations, shapes on the DMA
+# tiles) and no gathered copy is made.  Every output must equal, bit for bit,
+# the run that keeps x_disp (checked against the oracle in the tests above),
+# and the expert rows are checked against the oracle as well.  Without
+# read_x_rows (the default) the gathered buffer goes to the workspace.
 ROW_TABLE = [w for w in SMALL if w.act == "bf16"] + [
     # int8 experts on the scheduled 256-row DMA tiles (E >= 32, C > 128, d
     # and d_ff multiples of 1024) and on the 128-row ones (C <= 128)
@@ -456,8 +457,9 @@ ROW_TABLE = [w for w in SMALL if w.act == "bf16"] + [
 ]
 
 
-def _layer_outputs(wl, inp, keep_x_disp, wfmt=None):
-    cfg = binding.config_of(wl, wfmt=wfmt) if wfmt else binding.config_of(wl)
+def _layer_outputs(wl, inp, keep_x_disp, wfmt=None, read_x_rows=False):
+    kw = {"wfmt": wfmt} if wfmt else {}
+    cfg = binding.config_of(wl, read_x_rows=read_x_rows, **kw)
     out = binding.alloc_outputs(cfg, DEV, logits=True, x_disp=keep_x_disp, y_disp=True,
                                 dense_out=True)
     check_guards = guard_outputs(out)
@@ -484,9 +486,11 @@ def test_layer_without_x_disp_reads_token_rows(wl):
     print(f"[row_table] {wl.name}", flush=True)
     inp = synth.make_inputs(wl, seed=0, device=DEV)
     a = _layer_outputs(wl, inp, True)
-    b = _layer_outputs(wl, inp, False)
-    assert b.x_disp is None
+    b = _layer_outputs(wl, inp, False, read_x_rows=True)
+    c = _layer_outputs(wl, inp, False)  # gathered into the workspace
+    assert b.x_disp is None and c.x_disp is None
     _same_layer_outputs(a, b, wl.E)
+    _same_layer_outputs(a, c, wl.E)
     # the first and last kept row of every active expert against the oracle
     inv = _inverse(to_np(b.expert_ids), to_np(b.slots), wl.E)
     want, where = {}, []
@@ -559,19 +563,22 @@ def test_full_size_layer_sampled(name):
     print(f"  {len(toks)} tokens, {n_rows} of their rows kept; M rel err {err_m:.2e}",
           flush=True)
     if wl.act == "bf16":
-        # as the benchmark runs it: x_disp not kept (the first expert GEMM
-        # reads the token rows through the slot -> token table) and bf16
-        # expert weights packed: every output equal to this run's
+        # as the benchmark runs it: x_disp not kept (gathered into the
+        # workspace) and bf16 expert weights packed, and the same with the
+        # first expert GEMM reading the token rows through the slot -> token
+        # table (read_x_rows): every output equal to this run's
         wts = inp
         wfmt = "packed" if wl.wfmt == "plain" and wl.d % 128 == 0 and wl.d_ff % 128 == 0 else None
         if wfmt:
             cfgp = binding.config_of(wl, wfmt=wfmt)
             wts = dict(inp, w1=binding.pack_expert_weights(cfgp, 1, inp["w1"]),
                        w2=binding.pack_expert_weights(cfgp, 2, inp["w2"]))
-        b = _layer_outputs(wl, wts, False, wfmt=wfmt)
-        _same_layer_outputs(out, b, wl.E)
-        print(f"  without x_disp{' (packed weights)' if wfmt else ''}: outputs identical",
-              flush=True)
-        del wts, b
+        for rows_direct in (False, True):
+            b = _layer_outputs(wl, wts, False, wfmt=wfmt, read_x_rows=rows_direct)
+            _same_layer_outputs(out, b, wl.E)
+            del b
+            print(f"  without x_disp{' (packed weights)' if wfmt else ''}"
+                  f"{', read_x_rows' if rows_direct else ''}: outputs identical", flush=True)
+        del wts
     del inp, out, m
     torch.cuda.empty_cache()
