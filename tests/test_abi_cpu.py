@@ -112,6 +112,14 @@ def test_bad_config_rejected_before_launch(L, over, status):
     assert rc == status
 
 
+def test_read_x_rows_flag_is_validated(L):
+    cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, read_x_rows=True)
+    assert cfg.read_x_rows == 1 and L.moe_capacity(ctypes.byref(cfg)) > 0
+    cfg.read_x_rows = 2  # a flag: 0 or 1
+    assert L.moe_capacity(ctypes.byref(cfg)) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_bytes(ctypes.byref(cfg), binding.ENTRY_LAYER) == 0
+
+
 def test_drop_policies(L):
     cfg = binding.make_config(T=16, d=128, E=4, k=1, d_ff=128, drop_policy="gate_priority")
     assert cfg.drop_policy == binding.MOE_DROP_GATE_PRIORITY
