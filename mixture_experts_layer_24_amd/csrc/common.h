@@ -170,8 +170,8 @@ __device__ __forceinline__ int xcd_remap_grouped(int b, int G, int per_group) {
 // row-tiles are swept column by column (r -> (tm, tn)), so the tiles that
 // run at the same time share both operand slabs in L2 instead of each reading
 // its own weight slab.  Bijective on [0, tiles_m * tiles_n).
+template <int GM = 8>
 __device__ __forceinline__ void grouped_tile(int r, int tiles_m, int tiles_n, int &tm, int &tn) {
-  constexpr int GM = 8;
   const int q = r / (GM * tiles_n);
   const int tm0 = q * GM;
   const int gm = tiles_m - tm0 < GM ? tiles_m - tm0 : GM;

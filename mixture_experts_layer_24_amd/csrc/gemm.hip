@@ -336,8 +336,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
                                     : xcd_remap(blockIdx.x, total);
   const int g = tile / (tiles_m * tiles_n);
   const int rem = tile - g * tiles_m * tiles_n;
+  // row groups: 8 for the expert GEMMs (their weight slabs are streamed
+  // once, shared by an expert's row tiles); 2 for the dense MLP, whose 32
+  // concurrent tiles per XCD then cover 2 row x 16 column tiles and read
+  // each activation panel fewer times -- beside the expert weight stream,
+  // which evicts the dense operands from the caches, the overlapped 1.3B
+  // layer runs 2.527 -> 2.484 ms (row groups of 1, 4 and 16: 2.51, 2.51,
+  // 2.53 ms; the serial layer is unchanged)
   int tm, tn;
-  grouped_tile(rem, tiles_m, tiles_n, tm, tn);
+  if constexpr (NTB)
+    grouped_tile<8>(rem, tiles_m, tiles_n, tm, tn);
+  else
+    grouped_tile<2>(rem, tiles_m, tiles_n, tm, tn);
   int64_t rows = a.M_cap;
   if (a.rows) {
     const int64_t r = a.rows[g];
