@@ -457,8 +457,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
   // each once, and as ordinary stores their dirty lines (256 MB at the 1.3B
   // shape) were written back from the caches in the middle of the next
   // weight stream -- 350M-shape layer 0.447 -> 0.418 ms, serial 1.3B layer
-  // 2.82 -> 2.72 ms (expert GEMMs 0.866 / 0.755 -> 0.81 / 0.69 ms).  32x32 MFMA layout:
-  // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // 2.82 -> 2.72 ms (expert GEMMs 0.866 / 0.755 -> 0.81 / 0.69 ms).
+  // 32x32 MFMA layout: register r of lane l holds row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32.
   constexpr int CROW = BN * 2 + 16;  // bytes per LDS row of the C band
   static_assert(WTM * CROW <= NS * STAGE, "C band fits the stage buffers");
   constexpr int OCPR = BN / 8;       // 16-byte chunks per output row
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a) {
           const u32x4 cv = *(const u32x4 *)(smem + R * CROW + ch * 16);
           u32x4 *dst = (u32x4 *)(Cg + (r0 + R) * N + n0 + ch * 8);
           if constexpr (GELU == 1)
-            __builtin_nontemporal_store(cv, dst);  // hidden rows: see below
+            __builtin_nontemporal_store(cv, dst);  // hidden rows (see above)
           else
             *dst = cv;
         }
