@@ -33,9 +33,12 @@ def exact_gelu(z):
 
 
 def test_kernel_coefficients_are_the_fit():
+    # the fit is a least-squares solve: another LAPACK may round its last
+    # bits differently, so the coefficients are compared to 1e-5 relative
+    # (the error bound below is checked on the kernel's own values)
     c = kernel_coeffs()
     assert c.shape == (gelu_fit.DEGREE + 1,)
-    np.testing.assert_array_equal(c, gelu_fit.fit())
+    np.testing.assert_allclose(c, gelu_fit.fit(), rtol=1e-5, atol=1e-9)
 
 
 @pytest.mark.parametrize("lo,hi,n", [(-12.0, 12.0, 2_400_001), (-1e-3, 1e-3, 20_001),
