@@ -321,7 +321,10 @@ def test_int8_expert_schedule_matches_unscheduled_tiles(E, C, F):
         check_close(f"y_disp[{e}]", ys[e, rows], ref, TAU["bf16"])
 
 
-@pytest.mark.parametrize("T,d,Fd", [(300, 256, 512), (1000, 256, 512), (17, 64, 128)])
+# (700, 512, 4096): three row tiles (the last ragged) by 16 column tiles,
+# the dense MLP's row groups of 2 with a partial last group
+@pytest.mark.parametrize("T,d,Fd", [(300, 256, 512), (1000, 256, 512), (17, 64, 128),
+                                    (700, 512, 4096)])
 def test_dense_mlp_alone(T, d, Fd):
     wl = W("dm", T=T, d=d, E=2, k=1, d_ff=64, capacity_factor=1.0, d_ff_dense=Fd, pr_moe=True)
     cfg = binding.config_of(wl)
