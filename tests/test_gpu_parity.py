@@ -510,6 +510,22 @@ def test_layer_without_x_disp_reads_token_rows(wl):
                 TAU["bf16"])
 
 
+@pytest.mark.parametrize("wl", ROW_TABLE[:2], ids=[w.name for w in ROW_TABLE[:2]])
+def test_read_x_rows_falls_back_to_the_gather(wl):
+    # gate-priority dispatch has no slot -> token table: read_x_rows then
+    # gathers as usual, bit for bit the same outputs
+    print(f"[read_x_rows gate priority] {wl.name}", flush=True)
+    inp = synth.make_inputs(wl, seed=1, device=DEV)
+    outs = []
+    for rows_direct in (False, True):
+        cfg = binding.config_of(wl, drop_policy="gate_priority", read_x_rows=rows_direct)
+        out = binding.alloc_outputs(cfg, DEV, logits=True, y_disp=True, dense_out=True)
+        binding.moe_layer_forward(cfg, inp["x"], inp, out, binding.alloc_workspace(cfg))
+        torch.cuda.synchronize()
+        outs.append(out)
+    _same_layer_outputs(outs[0], outs[1], wl.E)
+
+
 def _inverse(ids, slots, E):
     """per expert: list of (slot, token, j) of its kept assignments, by slot"""
     rows = [[] for _ in range(E)]
